@@ -1,0 +1,419 @@
+/*
+ * llsa_oracle.c -- plain, slow CPU reference of Log-linear Sparse Attention (LLSA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The product path (the HIP library) never calls it, shares no
+ * code, header, table or helper with it, and must fail loudly when its own extension is missing.
+ *
+ * Source of the method.  "LLSA review" below means the pith.science review page of arXiv 2512.16615,
+ * "Trainable Log-linear Sparse Attention for Efficient Diffusion Transformers" (Zhou, Xiao, Wei, Yang,
+ * Pan).  That page relays the paper's Sec. 4.1 (hierarchical compression, hierarchical Top-K selection,
+ * KV enrichment and reweighting), Sec. 4.2 (Eq. 6 complexity) and Sec. 4.3 (sparse-index backward with
+ * a CSR-to-CSC transpose).  Each function cites the section of that page it follows.
+ *
+ * Arithmetic: IEEE double throughout.  Inputs are the exact values of the caller's fp32/bf16 tensors
+ * widened to double.  Loops are written in the order of the definition; no blocking, no fusion.
+ *
+ * Layouts (all contiguous, row-major, one slice per (batch*head) "bh"):
+ *   raw tensors        [bh][n][d]
+ *   pyramid            [bh][R][d],  R = sum_{l=1..L} n_l,  n_l = n / B^l,  level l starts at row
+ *                      off_l = sum_{l'<l} n_l'
+ *   selection indices  [bh][R][K]   row (off_l + u) holds the blocks kept for level-l unit u, ascending;
+ *                      slots past k_l = min(K, n_l) hold -1
+ *   CSC                per level l = 1..T (T = max(1, Le)): col_ptr has n_l + 1 entries, perm n_l*K
+ *                      entries; levels are concatenated, per bh, in level order.
+ *
+ * Readings of points the page leaves open (the design notes list them with reasons):
+ *   - pooled levels are l = 1..L with n_l = n / B^l; the coarsest level scores every one of its n_L
+ *     blocks; finer levels score the B children of each block the parent unit kept;
+ *   - parent of unit u is u / B, children of block c are c*B .. c*B+B-1 (contiguous pooling);
+ *   - selection score is the plain dot product of pooled query and pooled key (no scale, no bias);
+ *   - ties go to the lower block index;
+ *   - enrichment appends, for every level l = 1..Le, the level-l pooled K/V tokens that the query's
+ *     level-l ancestor unit kept, each with logit bias l*ln(B) (weight B^l on the exponentiated score);
+ *   - softmax scale sigma on every entry, no causal mask;
+ *   - gradient reaches K and V through the pooled tokens (each pooled token is the mean of B^l raw
+ *     tokens) and none flows through the Top-K choice or into the pooled queries.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------------------ */
+/* small helpers                                                                                     */
+/* ------------------------------------------------------------------------------------------------ */
+
+/* Number of pooled levels L = floor(log_B n - 1): the largest m with B^m <= n, minus one.
+ * [LLSA review, "What carries the argument" and the parameter ledger entry for L]                   */
+int llsa_ref_default_levels(int64_t n, int B) {
+  if (B < 2 || n < 1) return -1;
+  int m = 0;
+  int64_t p = 1;
+  while (p <= n / B) { p *= B; ++m; }
+  return m - 1;
+}
+
+static int64_t ipow(int64_t b, int e) {
+  int64_t r = 1;
+  for (int i = 0; i < e; ++i) r *= b;
+  return r;
+}
+
+/* rows of level l (1-based) and its row offset inside the pyramid */
+static int64_t level_rows(int64_t n, int B, int l) { return n / ipow(B, l); }
+static int64_t level_off(int64_t n, int B, int l) {
+  int64_t off = 0;
+  for (int j = 1; j < l; ++j) off += level_rows(n, B, j);
+  return off;
+}
+
+int64_t llsa_ref_pyramid_rows(int64_t n, int B, int L) { return level_off(n, B, L + 1); }
+
+/* number of slots actually filled at level l: k_l = min(K, n_l) */
+static int level_k(int64_t n, int B, int l, int K) {
+  int64_t nl = level_rows(n, B, l);
+  return (int)(K < nl ? K : nl);
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* O1 -- hierarchical compression: mean pooling of B consecutive tokens, level by level.              */
+/* [LLSA review, "Core claim": Q, K, V are mean-pooled over the levels; "What carries the argument"] */
+/* ------------------------------------------------------------------------------------------------ */
+void llsa_ref_pool(int64_t bh, int64_t n, int d, int B, int L, const double* x, double* pyr) {
+  const int64_t R = llsa_ref_pyramid_rows(n, B, L);
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < bh; ++s) {
+    const double* src = x + s * n * d;
+    double* dst_base = pyr + s * R * d;
+    int64_t src_rows = n;
+    for (int l = 1; l <= L; ++l) {
+      double* dst = dst_base + level_off(n, B, l) * d;
+      int64_t rows = level_rows(n, B, l);
+      for (int64_t j = 0; j < rows; ++j) {
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int t = 0; t < B; ++t) acc += src[(j * B + t) * d + c];
+          dst[j * d + c] = acc / (double)B;
+        }
+      }
+      (void)src_rows;
+      src_rows = rows;
+      src = dst; /* the next level pools this one */
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Top-K with the tie rule: order by (score descending, block index ascending), keep the first k,    */
+/* store them ascending by block index.                                                              */
+/* ------------------------------------------------------------------------------------------------ */
+static void topk_select(const double* score, const int64_t* cand, int ncand, int k, int32_t* out,
+                        unsigned char* taken) {
+  memset(taken, 0, (size_t)ncand);
+  for (int r = 0; r < k; ++r) {
+    int best = -1;
+    for (int c = 0; c < ncand; ++c) {
+      if (taken[c]) continue;
+      if (best < 0 || score[c] > score[best] || (score[c] == score[best] && cand[c] < cand[best]))
+        best = c;
+    }
+    taken[best] = 1;
+    out[r] = (int32_t)cand[best];
+  }
+  /* ascending by block index (insertion sort, k is small) */
+  for (int a = 1; a < k; ++a) {
+    int32_t v = out[a];
+    int b = a - 1;
+    while (b >= 0 && out[b] > v) { out[b + 1] = out[b]; --b; }
+    out[b + 1] = v;
+  }
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* O2 + O3 -- hierarchical Top-K selection.                                                          */
+/* Coarsest level: every level-L unit scores all n_L pooled key blocks and keeps the best K.         */
+/* Finer levels l = L-1..1: unit u inherits the picks of its parent u/B at level l+1, scores only    */
+/* their B children each (k_{l+1}*B candidates) and keeps the best K.                                */
+/* [LLSA review, "Core claim"; "What carries the argument"; referee major comment 1 on Alg. 1]      */
+/* Returns the number of (query unit, key block) pairs scored, summed over bh -- the Eq. (6) count.  */
+/* ------------------------------------------------------------------------------------------------ */
+int64_t llsa_ref_select(int64_t bh, int64_t n, int d, int B, int L, int K, const double* pq,
+                        const double* pk, int32_t* idx) {
+  const int64_t R = llsa_ref_pyramid_rows(n, B, L);
+  int64_t pairs = 0;
+  for (int64_t i = 0; i < bh * R * K; ++i) idx[i] = -1;
+#pragma omp parallel for schedule(static) reduction(+ : pairs)
+  for (int64_t s = 0; s < bh; ++s) {
+    const double* Q = pq + s * R * d;
+    const double* Kp = pk + s * R * d;
+    int32_t* I = idx + s * R * K;
+    int64_t maxc = level_rows(n, B, L);
+    if ((int64_t)K * B > maxc) maxc = (int64_t)K * B;
+    double* score = (double*)malloc(sizeof(double) * (size_t)maxc);
+    int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)maxc);
+    unsigned char* taken = (unsigned char*)malloc((size_t)maxc);
+
+    /* coarsest level: candidates are all n_L blocks */
+    {
+      const int64_t nL = level_rows(n, B, L), off = level_off(n, B, L);
+      const int kL = level_k(n, B, L, K);
+      for (int64_t u = 0; u < nL; ++u) {
+        for (int64_t j = 0; j < nL; ++j) {
+          double acc = 0.0;
+          for (int c = 0; c < d; ++c) acc += Q[(off + u) * d + c] * Kp[(off + j) * d + c];
+          score[j] = acc;
+          cand[j] = j;
+        }
+        pairs += nL;
+        topk_select(score, cand, (int)nL, kL, I + (off + u) * K, taken);
+      }
+    }
+    /* descent */
+    for (int l = L - 1; l >= 1; --l) {
+      const int64_t nl = level_rows(n, B, l), off = level_off(n, B, l), offp = level_off(n, B, l + 1);
+      const int kp = level_k(n, B, l + 1, K), kl = level_k(n, B, l, K);
+      for (int64_t u = 0; u < nl; ++u) {
+        const int64_t p = u / B;
+        int nc = 0;
+        for (int k = 0; k < kp; ++k) {
+          const int64_t c = I[(offp + p) * K + k];
+          for (int t = 0; t < B; ++t) cand[nc++] = c * B + t;
+        }
+        for (int c = 0; c < nc; ++c) {
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e) acc += Q[(off + u) * d + e] * Kp[(off + cand[c]) * d + e];
+          score[c] = acc;
+        }
+        pairs += nc;
+        topk_select(score, cand, nc, kl, I + (off + u) * K, taken);
+      }
+    }
+    free(score);
+    free(cand);
+    free(taken);
+  }
+  return pairs;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* The entry set E(n) of one raw query, written out: fine tokens of the level-1 blocks its fine      */
+/* block kept (bias 0), then for l = 1..Le the level-l pooled tokens its level-l ancestor kept        */
+/* (bias l*ln B, i.e. weight B^l).                                                                    */
+/* [LLSA review, "Core claim" (enrichment, weights B^l); "What carries the argument" (O(K log N) set)] */
+/* ------------------------------------------------------------------------------------------------ */
+typedef struct {
+  int level;     /* 0 = raw token, l >= 1 = pooled level-l token */
+  int64_t row;   /* raw token index (level 0) or pooled row index within its level */
+  double bias;   /* additive logit bias */
+} entry_t;
+
+static int build_entries(int64_t n, int B, int L, int K, int Le, const int32_t* I, int64_t query,
+                         entry_t* E) {
+  int ne = 0;
+  const int64_t i = query / B; /* fine query block = level-1 unit */
+  const int k1 = level_k(n, B, 1, K);
+  const int64_t off1 = level_off(n, B, 1);
+  for (int k = 0; k < k1; ++k) {
+    const int64_t c = I[(off1 + i) * K + k];
+    for (int t = 0; t < B; ++t) {
+      E[ne].level = 0;
+      E[ne].row = c * B + t;
+      E[ne].bias = 0.0;
+      ++ne;
+    }
+  }
+  for (int l = 1; l <= Le && l <= L; ++l) {
+    const int64_t a = i / ipow(B, l - 1); /* level-l unit containing fine block i */
+    const int64_t offl = level_off(n, B, l);
+    const int kl = level_k(n, B, l, K);
+    for (int k = 0; k < kl; ++k) {
+      E[ne].level = l;
+      E[ne].row = I[(offl + a) * K + k];
+      E[ne].bias = (double)l * log((double)B);
+      ++ne;
+    }
+  }
+  return ne;
+}
+
+static int max_entries(int B, int L, int K, int Le) { return K * B + K * (Le > L ? L : Le); }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* O4 -- enriched sparse attention forward: z_e = sigma * q.k_e + bias_e; lse = ln sum exp z;        */
+/* O = sum_e exp(z_e - lse) v_e.                                                                     */
+/* [LLSA review, "Core claim"; "What carries the argument"; abstract (sparse indices, no dense mask)] */
+/* ------------------------------------------------------------------------------------------------ */
+void llsa_ref_attn_fwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                       const double* q, const double* k, const double* v, const double* pk,
+                       const double* pv, const int32_t* idx, double* o, double* lse) {
+  const int64_t R = llsa_ref_pyramid_rows(n, B, L);
+  const int me = max_entries(B, L, K, Le);
+#pragma omp parallel
+  {
+    entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
+    double* z = (double*)malloc(sizeof(double) * (size_t)me);
+#pragma omp for schedule(static)
+    for (int64_t sq = 0; sq < bh * n; ++sq) {
+      const int64_t s = sq / n, qi = sq % n;
+      const double* qv = q + (s * n + qi) * d;
+      const int32_t* I = idx + s * R * K;
+      const int ne = build_entries(n, B, L, K, Le, I, qi, E);
+      double zmax = -INFINITY;
+      for (int e = 0; e < ne; ++e) {
+        const double* kv = E[e].level == 0 ? k + (s * n + E[e].row) * d
+                                           : pk + (s * R + level_off(n, B, E[e].level) + E[e].row) * d;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += qv[c] * kv[c];
+        z[e] = sigma * acc + E[e].bias;
+        if (z[e] > zmax) zmax = z[e];
+      }
+      double sum = 0.0;
+      for (int e = 0; e < ne; ++e) sum += exp(z[e] - zmax);
+      const double l = zmax + log(sum);
+      lse[s * n + qi] = l;
+      double* out = o + (s * n + qi) * d;
+      for (int c = 0; c < d; ++c) out[c] = 0.0;
+      for (int e = 0; e < ne; ++e) {
+        const double p = exp(z[e] - l);
+        const double* vv = E[e].level == 0 ? v + (s * n + E[e].row) * d
+                                           : pv + (s * R + level_off(n, B, E[e].level) + E[e].row) * d;
+        for (int c = 0; c < d; ++c) out[c] += p * vv[c];
+      }
+    }
+    free(E);
+    free(z);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* O5 -- CSR -> CSC transpose of the per-level selection (Gustavson's permuted transposition:        */
+/* count, exclusive prefix sum, then a stable pass over the CSR positions in ascending order).       */
+/* perm lists CSR positions p = u*K + k; levels 1..T with T = max(1, Le).                             */
+/* [LLSA review, "What carries the argument" (CSR-to-CSC scan for the backward pass)]               */
+/* ------------------------------------------------------------------------------------------------ */
+void llsa_ref_index_transpose(int64_t bh, int64_t n, int B, int L, int K, int Le, const int32_t* idx,
+                              int32_t* col_ptr, int32_t* perm) {
+  const int64_t R = llsa_ref_pyramid_rows(n, B, L);
+  const int T = Le < 1 ? 1 : (Le > L ? L : Le);
+  int64_t cp_len = 0, pm_len = 0;
+  for (int l = 1; l <= T; ++l) {
+    cp_len += level_rows(n, B, l) + 1;
+    pm_len += level_rows(n, B, l) * K;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < bh; ++s) {
+    int64_t cp_off = 0, pm_off = 0;
+    for (int l = 1; l <= T; ++l) {
+      const int64_t nl = level_rows(n, B, l), off = level_off(n, B, l);
+      const int32_t* I = idx + s * R * K + off * K;
+      int32_t* cp = col_ptr + s * cp_len + cp_off;
+      int32_t* pm = perm + s * pm_len + pm_off;
+      for (int64_t j = 0; j <= nl; ++j) cp[j] = 0;
+      for (int64_t p = 0; p < nl * K; ++p)
+        if (I[p] >= 0) cp[I[p] + 1] += 1;
+      for (int64_t j = 0; j < nl; ++j) cp[j + 1] += cp[j];
+      int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)nl);
+      for (int64_t j = 0; j < nl; ++j) cursor[j] = cp[j];
+      for (int64_t p = 0; p < nl * K; ++p)
+        if (I[p] >= 0) pm[cursor[I[p]]++] = (int32_t)p;
+      for (int64_t p = cp[nl]; p < nl * K; ++p) pm[p] = -1; /* unused tail when k_l < K */
+      free(cursor);
+      cp_off += nl + 1;
+      pm_off += nl * K;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* O6 -- backward through the same entry sets.                                                        */
+/* Delta_n = dO_n . O_n; for every entry e of query n with P = exp(z_e - lse_n):                       */
+/*   dV_e += P dO_n;  dS = P (dO_n . v_e - Delta_n);  dQ_n += sigma dS k_e;  dK_e += sigma dS q_n.    */
+/* Raw entries accumulate into dK, dV; level-l entries into the pooled gradients dK^(l), dV^(l),     */
+/* which flow back to the raw tokens with the pooling Jacobian: dK[m] += B^-l dK^(l)[m / B^l].        */
+/* No gradient through the Top-K choice or into pooled queries.                                       */
+/* [LLSA review, "If this is right" (backward uses only sparse indices); abstract; "Core claim"]     */
+/* Optional dpk/dpv (may be NULL) receive the pooled-token gradients [bh][R][d].                       */
+/* ------------------------------------------------------------------------------------------------ */
+void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                       const double* q, const double* k, const double* v, const double* o,
+                       const double* lse, const double* dout, const double* pk, const double* pv,
+                       const int32_t* idx, double* dq, double* dk, double* dv, double* dpk,
+                       double* dpv) {
+  const int64_t R = llsa_ref_pyramid_rows(n, B, L);
+  const int me = max_entries(B, L, K, Le);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < bh; ++s) {
+    entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
+    double* gk = (double*)calloc((size_t)(R * d), sizeof(double)); /* pooled-token gradients */
+    double* gv = (double*)calloc((size_t)(R * d), sizeof(double));
+    const int32_t* I = idx + s * R * K;
+    double* DQ = dq + s * n * d;
+    double* DK = dk + s * n * d;
+    double* DV = dv + s * n * d;
+    for (int64_t t = 0; t < n * d; ++t) { DQ[t] = 0.0; DK[t] = 0.0; DV[t] = 0.0; }
+    for (int64_t qi = 0; qi < n; ++qi) {
+      const double* qv = q + (s * n + qi) * d;
+      const double* ov = o + (s * n + qi) * d;
+      const double* gov = dout + (s * n + qi) * d;
+      double delta = 0.0;
+      for (int c = 0; c < d; ++c) delta += gov[c] * ov[c];
+      const int ne = build_entries(n, B, L, K, Le, I, qi, E);
+      for (int e = 0; e < ne; ++e) {
+        const double *kv, *vv;
+        double *gkd, *gvd;
+        if (E[e].level == 0) {
+          kv = k + (s * n + E[e].row) * d;
+          vv = v + (s * n + E[e].row) * d;
+          gkd = DK + E[e].row * d;
+          gvd = DV + E[e].row * d;
+        } else {
+          const int64_t r = level_off(n, B, E[e].level) + E[e].row;
+          kv = pk + (s * R + r) * d;
+          vv = pv + (s * R + r) * d;
+          gkd = gk + r * d;
+          gvd = gv + r * d;
+        }
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += qv[c] * kv[c];
+        const double P = exp(sigma * dot + E[e].bias - lse[s * n + qi]);
+        double dP = 0.0;
+        for (int c = 0; c < d; ++c) dP += gov[c] * vv[c];
+        const double dS = P * (dP - delta);
+        for (int c = 0; c < d; ++c) {
+          gvd[c] += P * gov[c];
+          DQ[qi * d + c] += sigma * dS * kv[c];
+          gkd[c] += sigma * dS * qv[c];
+        }
+      }
+    }
+    /* pooling Jacobian: each pooled level-l token is the mean of B^l raw tokens */
+    for (int l = 1; l <= L; ++l) {
+      const int64_t span = ipow(B, l), off = level_off(n, B, l);
+      for (int64_t m = 0; m < n; ++m) {
+        const int64_t r = off + m / span;
+        for (int c = 0; c < d; ++c) {
+          DK[m * d + c] += gk[r * d + c] / (double)span;
+          DV[m * d + c] += gv[r * d + c] / (double)span;
+        }
+      }
+    }
+    if (dpk) memcpy(dpk + s * R * d, gk, sizeof(double) * (size_t)(R * d));
+    if (dpv) memcpy(dpv + s * R * d, gv, sizeof(double) * (size_t)(R * d));
+    free(gk);
+    free(gv);
+    free(E);
+  }
+}
+
+int llsa_ref_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,50 @@
+"""The seeded input generators: determinism, slice independence, bf16 rounding, field statistics."""
+import math
+
+import numpy as np
+import torch
+
+from hierarchical_sparse_attention_mean_amd import inputs
+
+
+def test_deterministic_and_slice_independent():
+    w = inputs.custom(1, 3, 1024, 64, "bf16", seed=7)
+    a = inputs.make_inputs(w)
+    b = inputs.make_inputs(w)
+    c = inputs.make_inputs(w, heads=[2])
+    for name in ("q", "k", "v"):
+        assert np.array_equal(a[name].store, b[name].store)
+        assert np.array_equal(a[name].store[0, 2], c[name].store[0, 0])
+        assert not np.array_equal(a[name].store[0, 0], a[name].store[0, 1])
+
+
+def test_bf16_rounding_is_round_to_nearest_even():
+    x = np.random.default_rng(0).standard_normal(100000) * 10.0 ** np.random.default_rng(1).integers(-8, 8, 100000)
+    bits = inputs.round_to_bf16_bits(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    np.testing.assert_array_equal(inputs.bf16_bits_to_f64(bits), torch.from_numpy(ref.view(np.int16)).view(
+        torch.bfloat16).double().numpy())
+
+
+def test_field_statistics():
+    """Standardised channels; the lag-l autocorrelation of a squared-exponential field with length
+    scale l is exp(-1/2)."""
+    grid, ell = (256, 256), 16.0
+    F = inputs.smooth_field(5, 0, grid, ell, 8)
+    assert F.shape == (65536, 8)
+    np.testing.assert_allclose(F.mean(0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(F.std(0), 1.0, atol=1e-12)
+    img = F.reshape(256, 256, 8)
+    lag = int(ell)
+    rho = (img * np.roll(img, -lag, axis=1)).mean()
+    assert abs(rho - math.exp(-0.5)) < 0.08, rho
+
+
+def test_workloads_shapes():
+    w = inputs.WORKLOADS["fwdbwd_bf16_n65536"]
+    assert (w.heads, w.n, w.d, w.block, w.topk, w.levels, w.kind) == (16, 65536, 64, 16, 8, 3, "field")
+    w5 = inputs.WORKLOADS["fwdbwd_bf16_n262144"]
+    assert (w5.heads, w5.n, w5.topk, w5.levels) == (8, 262144, 16, 3)
+    s = inputs.make_inputs(inputs.WORKLOADS["fwd_bf16_n65536"], heads=[0])
+    assert s["q"].store.shape == (1, 1, 65536, 64) and s["q"].store.dtype == np.uint16
