@@ -1,0 +1,502 @@
+// attn_bwd.hip -- backward of the enriched sparse block attention (bf16, MFMA).
+//
+// Method [LLSA review (pith.science, arXiv 2512.16615), "If this is right" (the backward pass uses only
+// the sparse indices), "What carries the argument" (CSR-to-CSC transpose gives each key block its
+// query blocks), "Core claim" (enrichment tokens are mean-pooled, weight B^l)]:
+//   Delta_t = dO_t . O_t;  for every entry e of query t with P = exp(z_e - lse_t):
+//   dV_e += P dO_t,  dS = P (dO_t . v_e - Delta_t),  dQ_t += sigma dS k_e,  dK_e += sigma dS q_t.
+//   Pooled level-l tokens pass their gradient to the B^l raw tokens they average with factor B^-l.
+//
+// Kernels, in stream order:
+//   1. bwd_dq (Q-major, one wavefront per fine query block, four waves per workgroup, the workgroup
+//      owning the 16 fine blocks of one level-2 unit): recomputes P over fine and enrichment entries,
+//      writes dQ and Delta, and -- because all 256 queries of a level-2 unit share the enrichment tokens
+//      of levels >= 2 -- accumulates their dK^(l), dV^(l) contributions for the unit in registers and
+//      reduces the four waves in LDS in a fixed order (partials per level-2 unit and slot).
+//   2. coarse_reduce: for each pooled token of levels >= 2, sums the partials of the (unit, slot) pairs
+//      that kept it, found through that level's CSC column (no atomics).
+//   3. bwd_dkdv (K-major, one wavefront per fine key block): walks the key block's CSC column of level 1
+//      -- the query blocks that kept it -- and accumulates dK, dV for its 16 keys.  The same query
+//      blocks are exactly those that attend the block's level-1 pooled token, so that token's gradient
+//      (scaled by B^-1) is folded into the same products, and the B^-l share of the level >= 2 tokens is
+//      added before the bf16 store.
+// Every gradient element is owned by one wavefront: no floating-point atomics, bitwise reproducible.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace llsa {
+
+namespace {
+
+constexpr int kLd = kD + 8;   // bf16 row stride of K / Q / dO tiles in LDS
+constexpr int kSt = 16 + 8;   // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
+constexpr int kMaxHigh = 32;  // enrichment entries of levels >= 2 per query (K * (Le - 1))
+
+__device__ __forceinline__ void coarse_entry(const Geom& g, int e, int* level, int* slot) {
+  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
+  if (e < nhigh) {
+    *level = 2 + e / g.K;
+    *slot = e % g.K;
+  } else {
+    *level = 1;
+    *slot = e - nhigh;
+  }
+}
+
+__device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e, int* level) {
+  int l, s;
+  coarse_entry(g, e, &l, &s);
+  *level = l;
+  const int unit = i >> (4 * (l - 1));
+  return g.off[l] + I[(size_t)(g.off[l] + unit) * g.K + s];
+}
+
+__device__ __forceinline__ float dot16_bf16(uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
+  const uint32_t x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const uint32_t y[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
+    s += __uint_as_float(x[e] & 0xFFFF0000u) * __uint_as_float(y[e] & 0xFFFF0000u);
+  }
+  return s;
+}
+
+__device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (short)f32_to_bf16(a);
+  r[1] = (short)f32_to_bf16(b);
+  r[2] = (short)f32_to_bf16(c);
+  r[3] = (short)f32_to_bf16(d);
+  return r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 1. dQ, Delta and the level >= 2 pooled-token partials.
+// grid.x = bh * ceil(n_1 / 16) (remapped), 256 threads; wave w takes blocks 16u + w + 4jj, jj = 0..3.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dq_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
+                                                   const float* __restrict__ lse, const bf16_t* __restrict__ dout,
+                                                   const float* __restrict__ pk, const float* __restrict__ pv,
+                                                   const int32_t* __restrict__ idx, bf16_t* __restrict__ dq,
+                                                   float* __restrict__ delta, float* __restrict__ part_k,
+                                                   float* __restrict__ part_v, Geom g) {
+  __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t sts[4][32 * kSt];
+  __shared__ __attribute__((aligned(16))) bf16_t pts[4][32 * kSt];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int n1 = g.rows[1];
+  const int gps = (n1 + 15) / 16;
+  const int grp = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = grp / gps, u2 = grp - slice * gps;
+  const size_t base = (size_t)slice * g.n * kD;
+  const float* PK = pk + (size_t)slice * g.R * kD;
+  const float* PV = pv + (size_t)slice * g.R * kD;
+  const int32_t* I = idx + (size_t)slice * g.R * g.K;
+  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
+  const int ncoarse = g.K * g.Le;
+  bf16_t* kt = ks[w];
+  const int kr = lane >> 1, half = lane & 1;
+
+  f32x4 gk_acc[2][4], gv_acc[2][4];
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) gk_acc[T][t] = gv_acc[T][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int jj = 0; jj < 4; ++jj) {
+    const int i = 16 * u2 + w + 4 * jj;
+    if (i >= n1) continue;
+    const int row = 16 * i + c;
+    const uint4* qp = reinterpret_cast<const uint4*>(q + base + (size_t)row * kD + 16 * gq);
+    const uint4* dp = reinterpret_cast<const uint4*>(dout + base + (size_t)row * kD + 16 * gq);
+    const uint4* op = reinterpret_cast<const uint4*>(o + base + (size_t)row * kD + 16 * gq);
+    const uint4 q0 = qp[0], q1 = qp[1], d0 = dp[0], d1 = dp[1];
+    const bf16x8 qa0 = as_bf16x8(q0), qa1 = as_bf16x8(q1), da0 = as_bf16x8(d0), da1 = as_bf16x8(d1);
+    const float dlt = group_sum(dot16_bf16(d0, d1, op[0], op[1]));
+    const float lse2 = lse[(size_t)slice * g.n + row] * kLog2e;
+    if (gq == 0) delta[(size_t)slice * g.n + row] = dlt;
+    if (nhigh > 0) {
+      uint4* qd = reinterpret_cast<uint4*>(qs[w] + c * kLd + 16 * gq);
+      uint4* dd = reinterpret_cast<uint4*>(dos[w] + c * kLd + 16 * gq);
+      qd[0] = q0; qd[1] = q1; dd[0] = d0; dd[1] = d1;
+    }
+    f32x4 dq_acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dq_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // dS^T for 2 key tiles -> dQ^T += K^T dS^T (K^T read transposed from the LDS tile kt)
+    auto accumulate_dq = [&](const float ds[8]) {
+      uint4 u;
+      u.x = pack_bf16x2(ds[0], ds[1]);
+      u.y = pack_bf16x2(ds[2], ds[3]);
+      u.z = pack_bf16x2(ds[4], ds[5]);
+      u.w = pack_bf16x2(ds[6], ds[7]);
+      const bf16x8 db = as_bf16x8(u);
+      const bf16_t* r0 = kt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+      const bf16_t* r1 = r0 + 16 * kLd;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 ka = cat4(lds_read_tr16(r0 + 16 * t), lds_read_tr16(r1 + 16 * t));
+        dq_acc[t] = mfma_bf16_k32(ka, db, dq_acc[t]);
+      }
+    };
+
+    // fine key blocks, two per step
+    const int32_t* I1 = I + (size_t)(g.off[1] + i) * g.K;
+    for (int kk = 0; kk < g.K; kk += 2) {
+      const int b0 = I1[kk];
+      const bool has1 = kk + 1 < g.K;
+      const int b1 = has1 ? I1[kk + 1] : b0;
+      bf16x8 ka[2][2], va[2][2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const size_t r = base + (size_t)(16 * (t2 ? b1 : b0) + c) * kD + 16 * gq;
+        const uint4* kp = reinterpret_cast<const uint4*>(k + r);
+        const uint4* vp = reinterpret_cast<const uint4*>(v + r);
+        const uint4 k0 = kp[0], k1 = kp[1];
+        ka[t2][0] = as_bf16x8(k0); ka[t2][1] = as_bf16x8(k1);
+        va[t2][0] = as_bf16x8(vp[0]); va[t2][1] = as_bf16x8(vp[1]);
+        uint4* kd = reinterpret_cast<uint4*>(kt + (16 * t2 + c) * kLd + 16 * gq);
+        kd[0] = k0; kd[1] = k1;
+      }
+      float ds[8];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
+        s = mfma_bf16_k32(ka[t2][0], qa0, s);
+        s = mfma_bf16_k32(ka[t2][1], qa1, s);
+        dpv = mfma_bf16_k32(va[t2][0], da0, dpv);
+        dpv = mfma_bf16_k32(va[t2][1], da1, dpv);
+        const bool ok = t2 == 0 || has1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = ok ? exp2f(s[r] * g.scale_log2 - lse2) : 0.f;
+          ds[4 * t2 + r] = p * (dpv[r] - dlt);
+        }
+      }
+      accumulate_dq(ds);
+    }
+
+    // enrichment tokens, 32 per step (levels >= 2 first, then level 1)
+    for (int e0 = 0; e0 < ncoarse; e0 += 32) {
+      bf16x8 ka[2][2], va[2][2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int e = e0 + 16 * t2 + c;
+        int lvl;
+        const int prow = e < ncoarse ? coarse_row(g, I, i, e, &lvl) : g.off[1];
+        const float4* kp = reinterpret_cast<const float4*>(PK + (size_t)prow * kD + 16 * gq);
+        const float4* vp = reinterpret_cast<const float4*>(PV + (size_t)prow * kD + 16 * gq);
+        ka[t2][0] = f32x8_to_bf16x8(kp[0], kp[1]);
+        ka[t2][1] = f32x8_to_bf16x8(kp[2], kp[3]);
+        va[t2][0] = f32x8_to_bf16x8(vp[0], vp[1]);
+        va[t2][1] = f32x8_to_bf16x8(vp[2], vp[3]);
+        bf16x8* kd = reinterpret_cast<bf16x8*>(kt + (16 * t2 + c) * kLd + 16 * gq);
+        kd[0] = ka[t2][0];
+        kd[1] = ka[t2][1];
+      }
+      float ds[8], pr[8];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
+        s = mfma_bf16_k32(ka[t2][0], qa0, s);
+        s = mfma_bf16_k32(ka[t2][1], qa1, s);
+        dpv = mfma_bf16_k32(va[t2][0], da0, dpv);
+        dpv = mfma_bf16_k32(va[t2][1], da1, dpv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = e0 + 16 * t2 + 4 * gq + r;
+          int lvl, slot;
+          coarse_entry(g, e, &lvl, &slot);
+          const float p = e < ncoarse ? exp2f(s[r] * g.scale_log2 + 4.0f * (float)lvl - lse2) : 0.f;
+          pr[4 * t2 + r] = p;
+          ds[4 * t2 + r] = p * (dpv[r] - dlt);
+        }
+      }
+      accumulate_dq(ds);
+      if (e0 == 0 && nhigh > 0) {
+        // entries of levels >= 2 all sit in this first step: dK^(l)[e] += sum_q dS^T[e][q] q,
+        // dV^(l)[e] += sum_q P^T[e][q] dO over this block's 16 queries (16x16x16 MFMA, k = query)
+        bf16_t* st = sts[w];
+        bf16_t* pt = pts[w];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            st[(16 * t2 + 4 * gq + r) * kSt + c] = f32_to_bf16(ds[4 * t2 + r]);
+            pt[(16 * t2 + 4 * gq + r) * kSt + c] = f32_to_bf16(pr[4 * t2 + r]);
+          }
+        const bf16_t* qr = qs[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+        const bf16_t* dr = dos[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+          if (16 * T < nhigh) {
+            const bf16x4 as = *reinterpret_cast<const bf16x4*>(st + (16 * T + c) * kSt + 4 * gq);
+            const bf16x4 ap = *reinterpret_cast<const bf16x4*>(pt + (16 * T + c) * kSt + 4 * gq);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              gk_acc[T][t] = mfma_bf16_k16(as, lds_read_tr16(qr + 16 * t), gk_acc[T][t]);
+              gv_acc[T][t] = mfma_bf16_k16(ap, lds_read_tr16(dr + 16 * t), gv_acc[T][t]);
+            }
+          }
+        }
+      }
+    }
+    // dQ = sigma * dQ^T (lane holds d = 16t + 4g + r of query c)
+    bf16_t* qrow = dq + base + (size_t)row * kD + 4 * gq;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint2 u;
+      u.x = pack_bf16x2(dq_acc[t][0] * g.scale, dq_acc[t][1] * g.scale);
+      u.y = pack_bf16x2(dq_acc[t][2] * g.scale, dq_acc[t][3] * g.scale);
+      *reinterpret_cast<uint2*>(qrow + 16 * t) = u;
+    }
+  }
+
+  if (nhigh == 0) return;  // uniform over the workgroup
+  // Fixed-order reduction of the four waves' partials through LDS, then one store per element.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&ks[0][0]);  // [2][kMaxHigh][kD] fp32 = 16 KB
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 16 * T + 4 * gq + r, d = 16 * t + c;
+            float* rk = red + e * kD + d;
+            float* rv = red + (kMaxHigh + e) * kD + d;
+            if (ww == 0) {
+              *rk = gk_acc[T][t][r];
+              *rv = gv_acc[T][t][r];
+            } else {
+              *rk += gk_acc[T][t][r];
+              *rv += gv_acc[T][t][r];
+            }
+          }
+    }
+    __syncthreads();
+  }
+  float* outk = part_k + ((size_t)slice * gps + u2) * nhigh * kD;
+  float* outv = part_v + ((size_t)slice * gps + u2) * nhigh * kD;
+  for (int x = threadIdx.x; x < nhigh * kD; x += 256) {
+    outk[x] = red[x] * g.scale;
+    outv[x] = red[kMaxHigh * kD + x];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 2. Pooled-token gradients of levels 2..Le from the per-(level-2 unit, slot) partials via the CSC.
+// grid.x = sum_{l=2..Le} n_l, grid.y = slice; 64 threads (one per dim).
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void coarse_reduce(const int32_t* __restrict__ col_ptr,
+                                                    const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ part_k,
+                                                    const float* __restrict__ part_v, float* __restrict__ gk,
+                                                    float* __restrict__ gv, Geom g, CscGeom cg) {
+  const int slice = blockIdx.y, d = threadIdx.x;
+  int x = blockIdx.x, l = 2;
+  while (x >= g.rows[l]) {
+    x -= g.rows[l];
+    ++l;
+  }
+  const int j = x;
+  const int nhigh = g.K * (g.Le - 1);
+  const int n2 = g.rows[2];
+  const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[l];
+  const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[l];
+  const int span = 1 << (4 * (l - 2));  // level-2 units per level-l unit
+  float ak = 0.f, av = 0.f;
+  for (int y = cp[j]; y < cp[j + 1]; ++y) {
+    const int p = pm[y];
+    const int u = p / g.K, slot = p - u * g.K;
+    const int e = (l - 2) * g.K + slot;
+    for (int u2 = u * span; u2 < (u + 1) * span; ++u2) {
+      const size_t off = (((size_t)slice * n2 + u2) * nhigh + e) * kD + d;
+      ak += part_k[off];
+      av += part_v[off];
+    }
+  }
+  const size_t o = ((size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + j) * kD + d;
+  gk[o] = ak;
+  gv[o] = av;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 3. dK, dV per fine key block over its level-1 CSC column.
+// grid.x = ceil(bh * n_1 / 4) (remapped), 256 threads; wave w handles key block 4 * id + w.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                     const float* __restrict__ lse, const float* __restrict__ delta,
+                                                     const float* __restrict__ pk, const float* __restrict__ pv,
+                                                     const int32_t* __restrict__ col_ptr,
+                                                     const int32_t* __restrict__ perm, const float* __restrict__ gk,
+                                                     const float* __restrict__ gv, bf16_t* __restrict__ dk,
+                                                     bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kLd];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int n1 = g.rows[1];
+  const int gb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
+  if (gb >= g.bh * n1) return;  // no workgroup barrier below
+  const int slice = gb / n1, j = gb - slice * n1;
+  const size_t base = (size_t)slice * g.n * kD;
+  const size_t krow = base + (size_t)(16 * j + c) * kD + 16 * gq;
+  const bf16x8 kb0 = as_bf16x8(ld16(k + krow)), kb1 = as_bf16x8(ld16(k + krow + 8));
+  const bf16x8 vb0 = as_bf16x8(ld16(v + krow)), vb1 = as_bf16x8(ld16(v + krow + 8));
+  // level-1 pooled token of this block, rounded to bf16 as in the forward products
+  uint4 pk1[2], pv1[2];
+  const bool enrich1 = g.Le >= 1;
+  if (enrich1) {
+    const float4* kp = reinterpret_cast<const float4*>(pk + ((size_t)slice * g.R + g.off[1] + j) * kD + 16 * gq);
+    const float4* vp = reinterpret_cast<const float4*>(pv + ((size_t)slice * g.R + g.off[1] + j) * kD + 16 * gq);
+    bf16x8 a = f32x8_to_bf16x8(kp[0], kp[1]), b = f32x8_to_bf16x8(kp[2], kp[3]);
+    __builtin_memcpy(&pk1[0], &a, 16);
+    __builtin_memcpy(&pk1[1], &b, 16);
+    a = f32x8_to_bf16x8(vp[0], vp[1]);
+    b = f32x8_to_bf16x8(vp[2], vp[3]);
+    __builtin_memcpy(&pv1[0], &a, 16);
+    __builtin_memcpy(&pv1[1], &b, 16);
+  }
+  f32x4 dk_acc[4], dv_acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
+  const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[1];
+  const float* LS = lse + (size_t)slice * g.n;
+  const float* DL = delta + (size_t)slice * g.n;
+  const bf16_t* qr = qs[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+  const bf16_t* dr = dos[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+  const int y1 = cp[j + 1];
+  for (int y = cp[j]; y < y1; ++y) {
+    const int i = pm[y] / g.K;  // query block that kept this key block
+    const size_t qrow = base + (size_t)(16 * i + c) * kD + 16 * gq;
+    const uint4 q0 = ld16(q + qrow), q1 = ld16(q + qrow + 8);
+    const uint4 d0 = ld16(dout + qrow), d1 = ld16(dout + qrow + 8);
+    const float4 ls4 = *reinterpret_cast<const float4*>(LS + 16 * i + 4 * gq);
+    const float4 dl4 = *reinterpret_cast<const float4*>(DL + 16 * i + 4 * gq);
+    {
+      uint4* qd = reinterpret_cast<uint4*>(qs[w] + c * kLd + 16 * gq);
+      uint4* dd = reinterpret_cast<uint4*>(dos[w] + c * kLd + 16 * gq);
+      qd[0] = q0; qd[1] = q1; dd[0] = d0; dd[1] = d1;
+    }
+    f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
+    s = mfma_bf16_k32(as_bf16x8(q0), kb0, s);
+    s = mfma_bf16_k32(as_bf16x8(q1), kb1, s);
+    dpv = mfma_bf16_k32(as_bf16x8(d0), vb0, dpv);
+    dpv = mfma_bf16_k32(as_bf16x8(d1), vb1, dpv);
+    // s[r] = S[query 4g + r][key c]
+    const float ls[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+    const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+    float p[4], ds[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = exp2f(s[r] * g.scale_log2 - ls[r] * kLog2e);
+      ds[r] = p[r] * (dpv[r] - dl[r]);
+    }
+    if (enrich1) {
+      // level-1 pooled token of this block for query c: logit sigma q.k1 + ln B
+      const float zq = group_sum(dot16_bf16(q0, q1, pk1[0], pk1[1]));
+      const float dq1 = group_sum(dot16_bf16(d0, d1, pv1[0], pv1[1]));
+      const float lc = LS[16 * i + c] * kLog2e, dc = DL[16 * i + c];
+      const float pc = exp2f(zq * g.scale_log2 + 4.0f - lc);
+      const float dsc = pc * (dq1 - dc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // each raw key of the block receives B^-1 of the pooled token's gradient
+        p[r] += __shfl(pc, 4 * gq + r, 64) * (1.0f / (float)kB);
+        ds[r] += __shfl(dsc, 4 * gq + r, 64) * (1.0f / (float)kB);
+      }
+    }
+    const bf16x4 pb = pack4(p[0], p[1], p[2], p[3]);
+    const bf16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dv_acc[t] = mfma_bf16_k16(lds_read_tr16(dr + 16 * t), pb, dv_acc[t]);
+      dk_acc[t] = mfma_bf16_k16(lds_read_tr16(qr + 16 * t), db, dk_acc[t]);
+    }
+  }
+  // lane holds d = 16t + 4g + r of key c; add the B^-l share of the level >= 2 pooled tokens
+  const size_t orow = base + (size_t)(16 * j + c) * kD + 4 * gq;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float kx[4], vx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kx[r] = dk_acc[t][r] * g.scale;
+      vx[r] = dv_acc[t][r];
+    }
+    for (int l = 2; l <= g.Le; ++l) {
+      const int a = j >> (4 * (l - 1));
+      const float wgt = 1.0f / (float)(1 << (4 * l));
+      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 16 * t + 4 * gq;
+      const float4 gk4 = *reinterpret_cast<const float4*>(gk + gr);
+      const float4 gv4 = *reinterpret_cast<const float4*>(gv + gr);
+      kx[0] += gk4.x * wgt; kx[1] += gk4.y * wgt; kx[2] += gk4.z * wgt; kx[3] += gk4.w * wgt;
+      vx[0] += gv4.x * wgt; vx[1] += gv4.y * wgt; vx[2] += gv4.z * wgt; vx[3] += gv4.w * wgt;
+    }
+    uint2 uk, uv;
+    uk.x = pack_bf16x2(kx[0], kx[1]);
+    uk.y = pack_bf16x2(kx[2], kx[3]);
+    uv.x = pack_bf16x2(vx[0], vx[1]);
+    uv.y = pack_bf16x2(vx[2], vx[3]);
+    *reinterpret_cast<uint2*>(dk + orow + 16 * t) = uk;
+    *reinterpret_cast<uint2*>(dv + orow + 16 * t) = uv;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
+  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
+  const size_t n_delta = align256((size_t)g.bh * g.n * sizeof(float));
+  const size_t n_part = nhigh ? align256((size_t)g.bh * g.rows[2] * nhigh * kD * sizeof(float)) : 0;
+  const size_t n_g = nhigh ? align256((size_t)g.bh * (g.R - g.rows[1]) * kD * sizeof(float)) : 0;
+  if (out) {
+    char* p = static_cast<char*>(base);
+    out->delta = reinterpret_cast<float*>(p);
+    p += n_delta;
+    out->part_k = nhigh ? reinterpret_cast<float*>(p) : nullptr;
+    p += n_part;
+    out->part_v = nhigh ? reinterpret_cast<float*>(p) : nullptr;
+    p += n_part;
+    out->gk = nhigh ? reinterpret_cast<float*>(p) : nullptr;
+    p += n_g;
+    out->gv = nhigh ? reinterpret_cast<float*>(p) : nullptr;
+  }
+  return n_delta + 2 * n_part + 2 * n_g;
+}
+
+hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, const float* pk, const float* pv,
+                           const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk,
+                           void* dv, const BwdWs& ws, hipStream_t stream) {
+  const int n1 = g.rows[1];
+  const int groups = g.bh * ((n1 + 15) / 16);
+  bwd_dq_bf16<<<groups, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
+                                          lse, (const bf16_t*)dout, pk, pv, idx, (bf16_t*)dq, ws.delta, ws.part_k,
+                                          ws.part_v, g);
+  if (g.Le >= 2) {
+    int tokens = 0;
+    for (int l = 2; l <= g.Le; ++l) tokens += g.rows[l];
+    coarse_reduce<<<dim3(tokens, g.bh), 64, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, g,
+                                                          cg);
+  }
+  bwd_dkdv_bf16<<<(g.bh * n1 + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                                         (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm,
+                                                         ws.gk, ws.gv, (bf16_t*)dk, (bf16_t*)dv, g, cg);
+  return hipGetLastError();
+}
+
+}  // namespace llsa

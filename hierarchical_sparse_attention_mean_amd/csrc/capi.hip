@@ -1,0 +1,252 @@
+// capi.hip -- the C ABI of libllsa.so: host-side validation, workspace carving and kernel launches.
+//
+// Every entry point validates the problem and its pointers before launching anything, enqueues its
+// kernels on the caller's stream and returns without synchronising (contract in include/llsa.h).
+#include <math.h>
+#include <string.h>
+
+#include "launch.hpp"
+#include "llsa.h"
+
+namespace {
+
+using llsa::CscGeom;
+using llsa::Geom;
+
+struct Resolved {
+  llsa_problem p;
+  Geom g;
+  CscGeom cg;
+  int64_t bh;
+};
+
+// largest m with B^m <= n
+int floor_log(int64_t n, int B) {
+  int m = 0;
+  int64_t p = 1;
+  while (p <= n / B) {
+    p *= B;
+    ++m;
+  }
+  return m;
+}
+
+int resolve(const llsa_problem* in, Resolved* r) {
+  if (!in) return LLSA_ERR_NULL;
+  llsa_problem p = *in;
+  if (p.dtype != LLSA_F32 && p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
+  if (p.batch < 0 || p.heads < 0 || p.n < 1 || p.d < 1 || p.block < 2 || p.topk < 1) return LLSA_ERR_SHAPE;
+  // pooled levels: L = floor(log_B n - 1) by default, and 1 <= L <= that maximum
+  const int lmax = floor_log(p.n, p.block) - 1;
+  if (lmax < 1) return LLSA_ERR_SHAPE;
+  const int L = p.levels == 0 ? lmax : p.levels;
+  if (L < 1 || L > lmax || L > llsa::kMaxLevels) return LLSA_ERR_SHAPE;
+  int64_t span = 1;
+  for (int l = 0; l < L; ++l) span *= p.block;
+  if (p.n % span != 0) return LLSA_ERR_SHAPE;
+  const int64_t nL = p.n / span;
+  if (p.topk > nL) return LLSA_ERR_SHAPE;
+  const int Le = p.enrich_levels == -1 ? L : p.enrich_levels;
+  if (Le < 0 || Le > L) return LLSA_ERR_SHAPE;
+  float scale = p.scale == 0.0f ? 1.0f / sqrtf((float)p.d) : p.scale;
+  if (!isfinite(scale)) return LLSA_ERR_PARAM;
+  // limits of the gfx950 kernels
+  if (p.d != llsa::kD || p.block != llsa::kB) return LLSA_ERR_UNSUPPORTED;
+  if (p.topk > 32 || nL > 512) return LLSA_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)p.batch * p.heads;
+  if (bh * p.n * p.d >= ((int64_t)1 << 31)) return LLSA_ERR_UNSUPPORTED;
+  p.levels = L;
+  p.enrich_levels = Le;
+  p.scale = scale;
+  if (r) {
+    r->p = p;
+    r->bh = bh;
+    Geom& g = r->g;
+    memset(&g, 0, sizeof(g));
+    g.bh = (int)bh;
+    g.n = p.n;
+    g.K = p.topk;
+    g.L = L;
+    g.Le = Le;
+    g.rows[0] = p.n;
+    int off = 0;
+    for (int l = 1; l <= L; ++l) {
+      g.rows[l] = g.rows[l - 1] / p.block;
+      g.off[l] = off;
+      off += g.rows[l];
+    }
+    g.off[L + 1] = off;
+    g.R = off;
+    g.scale = scale;
+    g.scale_log2 = scale * llsa::kLog2e;
+    CscGeom& cg = r->cg;
+    memset(&cg, 0, sizeof(cg));
+    cg.T = Le < 1 ? 1 : Le;
+    int cpo = 0, pmo = 0;
+    for (int l = 1; l <= cg.T; ++l) {
+      cg.cp_off[l] = cpo;
+      cg.pm_off[l] = pmo;
+      cpo += g.rows[l] + 1;
+      pmo += g.rows[l] * p.topk;
+    }
+    cg.cp_len = cpo;
+    cg.pm_len = pmo;
+  }
+  return LLSA_OK;
+}
+
+// The kernels are built for gfx950 only; check the current device once per device.
+int check_device() {
+  static int state[64];  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LLSA_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return LLSA_ERR_DEVICE;
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LLSA_ERR_DEVICE;
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return state[dev] == 1 ? LLSA_OK : LLSA_ERR_DEVICE;
+}
+
+int check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (!x) return LLSA_ERR_NULL;
+  for (const void* x : ptrs)
+    if (reinterpret_cast<uintptr_t>(x) & 15u) return LLSA_ERR_ALIGN;
+  return LLSA_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_LAUNCH; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t transpose_ws(const Resolved& r) {
+  return align256((size_t)r.bh * r.cg.cp_len * sizeof(int32_t)) + align256((size_t)r.bh * r.cg.pm_len * sizeof(int32_t));
+}
+
+#define LLSA_TRY(x)          \
+  do {                       \
+    const int _s = (x);      \
+    if (_s != LLSA_OK) return _s; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int llsa_resolve(const llsa_problem* prob, llsa_problem* out) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (out) *out = r.p;
+  return LLSA_OK;
+}
+
+int64_t llsa_pyramid_rows(const llsa_problem* prob) {
+  Resolved r;
+  const int s = resolve(prob, &r);
+  return s == LLSA_OK ? (int64_t)r.g.R : (int64_t)s;
+}
+
+int64_t llsa_colptr_len(const llsa_problem* prob) {
+  Resolved r;
+  const int s = resolve(prob, &r);
+  return s == LLSA_OK ? (int64_t)r.cg.cp_len : (int64_t)s;
+}
+
+int64_t llsa_perm_len(const llsa_problem* prob) {
+  Resolved r;
+  const int s = resolve(prob, &r);
+  return s == LLSA_OK ? (int64_t)r.cg.pm_len : (int64_t)s;
+}
+
+size_t llsa_workspace_bytes(const llsa_problem* prob, int op) {
+  Resolved r;
+  if (resolve(prob, &r) != LLSA_OK) return 0;
+  if (op == LLSA_OP_INDEX_TRANSPOSE) return transpose_ws(r);
+  if (op == LLSA_OP_ATTN_BWD) return llsa::bwd_ws_layout(r.g, nullptr, nullptr);
+  return 0;
+}
+
+const char* llsa_status_string(int status) {
+  switch (status) {
+    case LLSA_OK: return "ok";
+    case LLSA_ERR_NULL: return "a required pointer is NULL";
+    case LLSA_ERR_SHAPE: return "invalid shape: need n mod B^L == 0, 1 <= L <= floor(log_B n - 1), 1 <= K <= n/B^L, 0 <= L_e <= L";
+    case LLSA_ERR_UNSUPPORTED: return "outside the limits of the gfx950 kernels (d = 64, B = 16, K <= 32, n/B^L <= 512, K*(L_e-1) <= 32, size < 2^31)";
+    case LLSA_ERR_DTYPE: return "unsupported dtype for this entry point";
+    case LLSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case LLSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LLSA_ERR_LAUNCH: return "kernel launch failed";
+    case LLSA_ERR_PARAM: return "scale is not finite";
+    case LLSA_ERR_DEVICE: return "the current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq, float* pk,
+                       float* pv, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({q, k, v, pq, pk, pv}));
+  LLSA_TRY(check_device());
+  return launched(llsa::launch_pyramid(r.g, r.p.dtype == LLSA_BF16, q, k, v, pq, pk, pv, (hipStream_t)stream));
+}
+
+int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({pq, pk, idx}));
+  LLSA_TRY(check_device());
+  return launched(llsa::launch_select(r.g, pq, pk, idx, (hipStream_t)stream));
+}
+
+int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
+                  const float* pv, const int32_t* idx, void* o, float* lse, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({q, k, v, pk, pv, idx, o, lse}));
+  LLSA_TRY(check_device());
+  return launched(
+      llsa::launch_attn_fwd(r.g, r.p.dtype == LLSA_BF16, q, k, v, pk, pv, idx, o, lse, (hipStream_t)stream));
+}
+
+int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({idx, col_ptr, perm}));
+  const size_t need = transpose_ws(r);
+  if (!ws || ws_bytes < need) return LLSA_ERR_WORKSPACE;
+  LLSA_TRY(check_ptrs({ws}));
+  LLSA_TRY(check_device());
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  int32_t* tmp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256((size_t)r.bh * r.cg.cp_len * sizeof(int32_t)));
+  return launched(llsa::launch_index_transpose(r.g, r.cg, idx, col_ptr, perm, cnt, tmp, (hipStream_t)stream));
+}
+
+int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, const float* pk, const float* pv, const int32_t* idx,
+                  const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
+                  size_t ws_bytes, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
+  if (r.g.Le >= 2 && r.g.K * (r.g.Le - 1) > 32) return LLSA_ERR_UNSUPPORTED;
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({q, k, v, o, lse, dout, pk, pv, idx, col_ptr, perm, dq, dk, dv}));
+  const size_t need = llsa::bwd_ws_layout(r.g, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return LLSA_ERR_WORKSPACE;
+  LLSA_TRY(check_ptrs({ws}));
+  LLSA_TRY(check_device());
+  llsa::BwdWs w;
+  llsa::bwd_ws_layout(r.g, &w, ws);
+  return launched(llsa::launch_attn_bwd(r.g, r.cg, q, k, v, o, lse, dout, pk, pv, idx, col_ptr, perm, dq, dk, dv, w,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

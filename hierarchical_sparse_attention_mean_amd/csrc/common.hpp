@@ -1,0 +1,122 @@
+// common.hpp -- device-side building blocks shared by the gfx950 kernels of the LLSA hot path.
+//
+// Lane layouts used throughout (64-lane wavefront, lane = 16*g + c, g = lane >> 4, c = lane & 15):
+//   v_mfma_f32_16x16x32_bf16: A lane holds A[row c][k = 8g..8g+7], B lane holds B[k = 8g..8g+7][col c],
+//                             D lane holds D[row 4g+r][col c], r = 0..3.
+//   v_mfma_f32_16x16x16_bf16: same with k = 4g..4g+3.
+//   v_mfma_f32_16x16x4_f32:   A lane holds A[row c][k = g], B lane holds B[k = g][col c], same D.
+//   ds_read_b64_tr_b16:        inside each 16-lane group, output lane j element e is element (j % 4) of
+//                             the 8-byte load addressed by lane 4e + j/4.  With lane i addressing
+//                             &M[r0 + i/4][c0 + 4*(i%4)] of a row-major bf16 matrix M, lane j receives
+//                             M[r0 + e][c0 + j], e = 0..3 -- a transposed 4x16 sub-block.
+// Because a dot product may visit its k index in any order, A and B operands are always loaded with
+// the same (permuted) k order, which lets every lane read contiguous 32-byte runs of a row.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint16_t bf16_t;
+
+constexpr int kD = 64;      // head dim handled by the GPU kernels
+constexpr int kB = 16;      // block / pooling factor handled by the GPU kernels
+constexpr int kMaxLevels = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Per-problem geometry passed by value to kernels.
+struct Geom {
+  int bh;                       // batch * heads
+  int n;                        // raw tokens per slice
+  int K;                        // top-k
+  int L;                        // pooled levels
+  int Le;                       // enrichment levels
+  int R;                        // pyramid rows per slice
+  int rows[kMaxLevels + 1];     // rows[l] = n / B^l (rows[0] = n)
+  int off[kMaxLevels + 2];      // off[l] = first pyramid row of level l (l >= 1)
+  float scale_log2;             // sigma * log2(e)
+  float scale;                  // sigma
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4x16 bf16 read from LDS (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Reduce over the four 16-lane groups (lanes c, c+16, c+32, c+48); every lane gets the result.
+__device__ __forceinline__ float group_sum(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+
+// Workgroup ids are dispatched round-robin over the 8 XCDs; remap so that consecutive logical ids
+// land on the same XCD (and share its L2).  A bijection on [0, G).
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+  const int full = (G / 8) * 8;
+  if (b >= full) return b;
+  return (b % 8) * (G / 8) + b / 8;
+}
+
+// 16-byte global loads / stores.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Eight consecutive fp32 values -> bf16x8 (RNE).
+__device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const float4 a, const float4 b) {
+  uint4 u;
+  u.x = pack_bf16x2(a.x, a.y);
+  u.y = pack_bf16x2(a.z, a.w);
+  u.z = pack_bf16x2(b.x, b.y);
+  u.w = pack_bf16x2(b.z, b.w);
+  return as_bf16x8(u);
+}
+
+}  // namespace llsa

@@ -1,0 +1,43 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal to libllsa.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace llsa {
+
+// Per-level offsets of the concatenated CSC arrays (levels 1..T).
+struct CscGeom {
+  int T;                        // transposed levels
+  int cp_len, pm_len;           // per-slice lengths of col_ptr and perm
+  int cp_off[kMaxLevels + 1];   // cp_off[l]: first col_ptr entry of level l
+  int pm_off[kMaxLevels + 1];   // pm_off[l]: first perm entry of level l
+};
+
+hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
+                          float* pk, float* pv, hipStream_t stream);
+hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream);
+hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v,
+                           const float* pk, const float* pv, const int32_t* idx, void* o, float* lse,
+                           hipStream_t stream);
+hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_t* idx, int32_t* col_ptr,
+                                  int32_t* perm, int32_t* ws_cnt, int32_t* ws_tmp, hipStream_t stream);
+
+// Backward workspace carve-up (all fp32): delta [bh][n]; partials of pooled-token gradients for levels
+// >= 2 [bh][n_2][K*(Le-1)][d] (K and V); reduced pooled gradients of levels >= 2 [bh][R - n_1][d] (K, V).
+struct BwdWs {
+  float* delta;
+  float* part_k;
+  float* part_v;
+  float* gk;
+  float* gv;
+};
+size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base);
+hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, const float* pk, const float* pv,
+                           const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk,
+                           void* dv, const BwdWs& ws, hipStream_t stream);
+
+}  // namespace llsa

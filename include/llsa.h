@@ -1,0 +1,153 @@
+/*
+ * llsa.h -- C ABI of the MI355X (gfx950) Log-linear Sparse Attention hot path.
+ *
+ * Source of the method: the pith.science review page of arXiv 2512.16615, "Trainable Log-linear
+ * Sparse Attention for Efficient Diffusion Transformers" (cited below as "LLSA review").  The
+ * problem is stated there as sparse attention on Q, K, V with a block size B, a Top-K parameter K,
+ * L pooled levels and L_e enrichment levels (parameter ledger; Figure 1 caption).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are device pointers into caller-owned memory.  Raw tensors Q, K, V, O, dO, dQ, dK, dV are
+ * [batch][heads][n][d], contiguous, d fastest, stored as fp32 or bf16 (llsa_problem.dtype).
+ * The pooled pyramid is fp32 [batch*heads][R][d] with R = sum_{l=1..L} n_l and n_l = n / B^l; level l
+ * starts at row sum_{l'<l} n_l'.  Selection indices are int32 [batch*heads][R][K] (same row order),
+ * each row ascending.  The CSC of level l (l = 1..T, T = max(1, L_e)) is col_ptr (n_l + 1 entries,
+ * relative to the level) and perm (n_l * K entries, each a CSR position p = u*K + k, ascending within
+ * a column); levels are concatenated per batch*head in level order.
+ *
+ * Ownership: the caller allocates and owns every buffer, including workspaces; the library allocates
+ * nothing on these paths, keeps no pointer after returning and holds no state beyond a cached
+ * per-device property query.  Calls are re-entrant.
+ * Asynchrony: each call validates on the host, then enqueues kernels on `stream` (a hipStream_t;
+ * NULL means the default stream) and returns without synchronising.  Outputs are complete when the
+ * stream reaches that point; they are overwritten, never accumulated.
+ * Errors: each call returns LLSA_OK (0) or a negative LLSA_ERR_* code; on a validation error nothing
+ * is launched.  No exception crosses the ABI.  Non-finite inputs give unspecified outputs.
+ * Pointers must be 16-byte aligned (LLSA_ERR_ALIGN).
+ * GPU limits of this version: d = 64, B = 16, 1 <= K <= n_L, K <= 64, n_L <= 1024, batch*heads*n*d < 2^31.
+ */
+#ifndef LLSA_H
+#define LLSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LLSA_F32 = 0, LLSA_BF16 = 1 } llsa_dtype;
+
+enum {
+  LLSA_OK = 0,
+  LLSA_ERR_NULL = -1,        /* a required pointer is NULL                                        */
+  LLSA_ERR_SHAPE = -2,       /* n mod B^L != 0, L or K or L_e out of range, bad batch/heads/n     */
+  LLSA_ERR_UNSUPPORTED = -3, /* valid for the method but outside this GPU version (d, B, sizes)   */
+  LLSA_ERR_DTYPE = -4,       /* unknown dtype, or a dtype an entry point does not implement      */
+  LLSA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                                  */
+  LLSA_ERR_WORKSPACE = -6,   /* workspace pointer NULL or ws_bytes smaller than required          */
+  LLSA_ERR_LAUNCH = -7,      /* a kernel launch failed (hipGetLastError)                           */
+  LLSA_ERR_PARAM = -8,       /* scale not finite                                                   */
+  LLSA_ERR_DEVICE = -9       /* current device is not gfx950                                       */
+};
+
+/* Problem description; every entry point takes the same struct. */
+typedef struct {
+  int32_t batch, heads, n, d; /* raw tensors [batch][heads][n][d]                                  */
+  int32_t block;              /* B: pooling factor and attention block size                          */
+  int32_t topk;               /* K: blocks kept per query unit at every level                        */
+  int32_t levels;             /* L; 0 selects floor(log_B n - 1) [LLSA review, parameter ledger]     */
+  int32_t enrich_levels;      /* L_e in [0, L]; -1 selects L [LLSA review, parameter ledger]         */
+  int32_t dtype;              /* llsa_dtype of the raw tensors                                        */
+  float scale;                /* softmax scale sigma; 0 selects 1/sqrt(d)                             */
+} llsa_problem;
+
+/* Operation ids for llsa_workspace_bytes. */
+enum { LLSA_OP_INDEX_TRANSPOSE = 1, LLSA_OP_ATTN_BWD = 2 };
+
+/*
+ * llsa_build_pyramid -- hierarchical compression [LLSA review, "Core claim"; "What carries the
+ * argument"]: X^(l)[j] = mean of B consecutive tokens of X^(l-1), l = 1..L, X^(0) = X, for X in
+ * {Q, K, V}.  Accumulation and storage in fp32.
+ *   q, k, v   in : raw tensors (dtype).
+ *   pq, pk, pv out: fp32 pyramids [batch*heads][R][d].
+ */
+int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq,
+                       float* pk, float* pv, void* stream);
+
+/*
+ * llsa_select -- hierarchical Top-K [LLSA review, "Core claim"; "What carries the argument";
+ * referee major comment 1 on Algorithm 1]: every level-L unit scores all n_L pooled key blocks with
+ * the dot product of pooled query and pooled key and keeps the best K; at l = L-1..1 unit u scores
+ * only the B children of each block its parent u/B kept and keeps the best K.  Ties go to the lower
+ * block index.  Scores are computed in fp32.
+ *   pq, pk in : fp32 pyramids from llsa_build_pyramid.
+ *   idx    out: int32 [batch*heads][R][K], each row ascending.
+ */
+int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, void* stream);
+
+/*
+ * llsa_attn_fwd -- sparse block attention with hierarchical KV enrichment [LLSA review, "Core
+ * claim"; "What carries the argument"; abstract]: raw query t in fine block i = t/B attends the B
+ * raw tokens of every level-1 block in idx row i (logit sigma*q.k) and, for l = 1..L_e, the level-l
+ * pooled tokens kept by its level-l ancestor unit i/B^(l-1) (logit sigma*q.k + l*ln B, i.e. weight
+ * B^l).  Only the sparse indices are read; no dense mask exists.
+ *   q, k, v in : raw tensors (dtype).  pk, pv in: fp32 pyramids.  idx in: from llsa_select.
+ *   o   out: [batch][heads][n][d] (dtype).
+ *   lse out: fp32 [batch*heads][n], natural-log log-sum-exp of each query's logits (for backward).
+ * bf16 runs the products on bf16 MFMA with fp32 accumulation (pooled K/V rounded to bf16 for the
+ * products, probabilities rounded to bf16 for the PV product); fp32 computes in fp32.
+ */
+int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
+                  const float* pv, const int32_t* idx, void* o, float* lse, void* stream);
+
+/*
+ * llsa_index_transpose -- CSR -> CSC of the selection of levels 1..T, T = max(1, L_e) [LLSA review,
+ * "What carries the argument": a CSR-to-CSC scan gives each key block its query blocks without a
+ * dense N x N mask].  Column j of level l lists the CSR positions p = u*K + k with idx = j, ascending.
+ *   idx     in : from llsa_select.
+ *   col_ptr out: int32 [batch*heads][llsa_colptr_len].
+ *   perm    out: int32 [batch*heads][llsa_perm_len].
+ *   ws      scratch of llsa_workspace_bytes(prob, LLSA_OP_INDEX_TRANSPOSE) bytes (caller-owned).
+ */
+int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * llsa_attn_bwd -- gradients of the enriched sparse attention [LLSA review, "If this is right"
+ * (backward over sparse indices only); abstract]: with Delta_t = dO_t . O_t and P = exp(z - lse),
+ * dV_e += P dO_t, dS = P (dO_t . v_e - Delta_t), dQ_t += sigma dS k_e, dK_e += sigma dS q_t over each
+ * query's entry set; gradients of pooled level-l tokens reach the raw tokens they pool with factor
+ * B^-l.  No gradient flows through the Top-K choice or into pooled queries.  Key-side gradients are
+ * gathered per key block through the CSC (no atomics).  bf16 only in this version (LLSA_ERR_DTYPE for
+ * fp32).
+ *   q, k, v, o, dout in: raw tensors (dtype); lse in: from llsa_attn_fwd; pk, pv, idx: as forward;
+ *   col_ptr, perm in: from llsa_index_transpose.
+ *   dq, dk, dv out: raw tensors (dtype).
+ *   ws scratch of llsa_workspace_bytes(prob, LLSA_OP_ATTN_BWD) bytes (caller-owned).
+ */
+int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, const float* pk, const float* pv, const int32_t* idx,
+                  const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* ---- host-only helpers (no GPU work) ---------------------------------------------------------- */
+
+/* Validate `prob` and fill the defaults (levels, enrich_levels, scale) into `out`.  Returns a status. */
+int llsa_resolve(const llsa_problem* prob, llsa_problem* out);
+/* R = sum_{l=1..L} n / B^l (rows of one pyramid slice); < 0 on an invalid problem. */
+int64_t llsa_pyramid_rows(const llsa_problem* prob);
+/* sum_{l=1..T} (n/B^l + 1), T = max(1, L_e): col_ptr entries per batch*head; < 0 if invalid. */
+int64_t llsa_colptr_len(const llsa_problem* prob);
+/* sum_{l=1..T} (n/B^l) * K: perm entries per batch*head; < 0 if invalid. */
+int64_t llsa_perm_len(const llsa_problem* prob);
+/* Workspace bytes for `op` (LLSA_OP_*); O(n) per batch*head, never O(n^2).  0 for an invalid problem. */
+size_t llsa_workspace_bytes(const llsa_problem* prob, int op);
+/* Static, NUL-terminated description of a status code. */
+const char* llsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLSA_H */

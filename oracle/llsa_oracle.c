@@ -147,55 +147,67 @@ int64_t llsa_ref_select(int64_t bh, int64_t n, int d, int B, int L, int K, const
   const int64_t R = llsa_ref_pyramid_rows(n, B, L);
   int64_t pairs = 0;
   for (int64_t i = 0; i < bh * R * K; ++i) idx[i] = -1;
-#pragma omp parallel for schedule(static) reduction(+ : pairs)
+  int64_t maxc = level_rows(n, B, L);
+  if ((int64_t)K * B > maxc) maxc = (int64_t)K * B;
   for (int64_t s = 0; s < bh; ++s) {
     const double* Q = pq + s * R * d;
     const double* Kp = pk + s * R * d;
     int32_t* I = idx + s * R * K;
-    int64_t maxc = level_rows(n, B, L);
-    if ((int64_t)K * B > maxc) maxc = (int64_t)K * B;
-    double* score = (double*)malloc(sizeof(double) * (size_t)maxc);
-    int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)maxc);
-    unsigned char* taken = (unsigned char*)malloc((size_t)maxc);
-
     /* coarsest level: candidates are all n_L blocks */
     {
       const int64_t nL = level_rows(n, B, L), off = level_off(n, B, L);
       const int kL = level_k(n, B, L, K);
-      for (int64_t u = 0; u < nL; ++u) {
-        for (int64_t j = 0; j < nL; ++j) {
-          double acc = 0.0;
-          for (int c = 0; c < d; ++c) acc += Q[(off + u) * d + c] * Kp[(off + j) * d + c];
-          score[j] = acc;
-          cand[j] = j;
+#pragma omp parallel reduction(+ : pairs)
+      {
+        double* score = (double*)malloc(sizeof(double) * (size_t)maxc);
+        int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)maxc);
+        unsigned char* taken = (unsigned char*)malloc((size_t)maxc);
+#pragma omp for schedule(static)
+        for (int64_t u = 0; u < nL; ++u) {
+          for (int64_t j = 0; j < nL; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += Q[(off + u) * d + c] * Kp[(off + j) * d + c];
+            score[j] = acc;
+            cand[j] = j;
+          }
+          pairs += nL;
+          topk_select(score, cand, (int)nL, kL, I + (off + u) * K, taken);
         }
-        pairs += nL;
-        topk_select(score, cand, (int)nL, kL, I + (off + u) * K, taken);
+        free(score);
+        free(cand);
+        free(taken);
       }
     }
-    /* descent */
+    /* descent: level l depends on level l+1, units of one level are independent */
     for (int l = L - 1; l >= 1; --l) {
       const int64_t nl = level_rows(n, B, l), off = level_off(n, B, l), offp = level_off(n, B, l + 1);
       const int kp = level_k(n, B, l + 1, K), kl = level_k(n, B, l, K);
-      for (int64_t u = 0; u < nl; ++u) {
-        const int64_t p = u / B;
-        int nc = 0;
-        for (int k = 0; k < kp; ++k) {
-          const int64_t c = I[(offp + p) * K + k];
-          for (int t = 0; t < B; ++t) cand[nc++] = c * B + t;
+#pragma omp parallel reduction(+ : pairs)
+      {
+        double* score = (double*)malloc(sizeof(double) * (size_t)maxc);
+        int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)maxc);
+        unsigned char* taken = (unsigned char*)malloc((size_t)maxc);
+#pragma omp for schedule(static)
+        for (int64_t u = 0; u < nl; ++u) {
+          const int64_t p = u / B;
+          int nc = 0;
+          for (int k = 0; k < kp; ++k) {
+            const int64_t c = I[(offp + p) * K + k];
+            for (int t = 0; t < B; ++t) cand[nc++] = c * B + t;
+          }
+          for (int c = 0; c < nc; ++c) {
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += Q[(off + u) * d + e] * Kp[(off + cand[c]) * d + e];
+            score[c] = acc;
+          }
+          pairs += nc;
+          topk_select(score, cand, nc, kl, I + (off + u) * K, taken);
         }
-        for (int c = 0; c < nc; ++c) {
-          double acc = 0.0;
-          for (int e = 0; e < d; ++e) acc += Q[(off + u) * d + e] * Kp[(off + cand[c]) * d + e];
-          score[c] = acc;
-        }
-        pairs += nc;
-        topk_select(score, cand, nc, kl, I + (off + u) * K, taken);
+        free(score);
+        free(cand);
+        free(taken);
       }
     }
-    free(score);
-    free(cand);
-    free(taken);
   }
   return pairs;
 }
@@ -346,50 +358,76 @@ void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
                        double* dpv) {
   const int64_t R = llsa_ref_pyramid_rows(n, B, L);
   const int me = max_entries(B, L, K, Le);
-#pragma omp parallel for schedule(dynamic, 1)
+  int nthr = 1;
+#ifdef _OPENMP
+  nthr = omp_get_max_threads();
+#endif
+  /* per-thread accumulators of the scatter-add (raw dK, dV and pooled-token gradients), summed in
+     thread order afterwards so the result does not depend on scheduling */
+  const int64_t acc_len = (n + R) * d;
+  double* acc_k = (double*)malloc(sizeof(double) * (size_t)(acc_len * nthr));
+  double* acc_v = (double*)malloc(sizeof(double) * (size_t)(acc_len * nthr));
   for (int64_t s = 0; s < bh; ++s) {
-    entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
-    double* gk = (double*)calloc((size_t)(R * d), sizeof(double)); /* pooled-token gradients */
-    double* gv = (double*)calloc((size_t)(R * d), sizeof(double));
     const int32_t* I = idx + s * R * K;
     double* DQ = dq + s * n * d;
     double* DK = dk + s * n * d;
     double* DV = dv + s * n * d;
-    for (int64_t t = 0; t < n * d; ++t) { DQ[t] = 0.0; DK[t] = 0.0; DV[t] = 0.0; }
-    for (int64_t qi = 0; qi < n; ++qi) {
-      const double* qv = q + (s * n + qi) * d;
-      const double* ov = o + (s * n + qi) * d;
-      const double* gov = dout + (s * n + qi) * d;
-      double delta = 0.0;
-      for (int c = 0; c < d; ++c) delta += gov[c] * ov[c];
-      const int ne = build_entries(n, B, L, K, Le, I, qi, E);
-      for (int e = 0; e < ne; ++e) {
-        const double *kv, *vv;
-        double *gkd, *gvd;
-        if (E[e].level == 0) {
-          kv = k + (s * n + E[e].row) * d;
-          vv = v + (s * n + E[e].row) * d;
-          gkd = DK + E[e].row * d;
-          gvd = DV + E[e].row * d;
-        } else {
-          const int64_t r = level_off(n, B, E[e].level) + E[e].row;
-          kv = pk + (s * R + r) * d;
-          vv = pv + (s * R + r) * d;
-          gkd = gk + r * d;
-          gvd = gv + r * d;
-        }
-        double dot = 0.0;
-        for (int c = 0; c < d; ++c) dot += qv[c] * kv[c];
-        const double P = exp(sigma * dot + E[e].bias - lse[s * n + qi]);
-        double dP = 0.0;
-        for (int c = 0; c < d; ++c) dP += gov[c] * vv[c];
-        const double dS = P * (dP - delta);
-        for (int c = 0; c < d; ++c) {
-          gvd[c] += P * gov[c];
-          DQ[qi * d + c] += sigma * dS * kv[c];
-          gkd[c] += sigma * dS * qv[c];
+#pragma omp parallel
+    {
+      int tid = 0;
+#ifdef _OPENMP
+      tid = omp_get_thread_num();
+#endif
+      double* ak = acc_k + tid * acc_len; /* rows 0..n-1 raw tokens, n..n+R-1 pooled tokens */
+      double* av = acc_v + tid * acc_len;
+      for (int64_t t = 0; t < acc_len; ++t) { ak[t] = 0.0; av[t] = 0.0; }
+      entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
+#pragma omp for schedule(static)
+      for (int64_t qi = 0; qi < n; ++qi) {
+        const double* qv = q + (s * n + qi) * d;
+        const double* ov = o + (s * n + qi) * d;
+        const double* gov = dout + (s * n + qi) * d;
+        double delta = 0.0;
+        for (int c = 0; c < d; ++c) delta += gov[c] * ov[c];
+        for (int c = 0; c < d; ++c) DQ[qi * d + c] = 0.0;
+        const int ne = build_entries(n, B, L, K, Le, I, qi, E);
+        for (int e = 0; e < ne; ++e) {
+          const double *kv, *vv;
+          int64_t arow;
+          if (E[e].level == 0) {
+            kv = k + (s * n + E[e].row) * d;
+            vv = v + (s * n + E[e].row) * d;
+            arow = E[e].row;
+          } else {
+            const int64_t r = level_off(n, B, E[e].level) + E[e].row;
+            kv = pk + (s * R + r) * d;
+            vv = pv + (s * R + r) * d;
+            arow = n + r;
+          }
+          double dot = 0.0;
+          for (int c = 0; c < d; ++c) dot += qv[c] * kv[c];
+          const double P = exp(sigma * dot + E[e].bias - lse[s * n + qi]);
+          double dP = 0.0;
+          for (int c = 0; c < d; ++c) dP += gov[c] * vv[c];
+          const double dS = P * (dP - delta);
+          for (int c = 0; c < d; ++c) {
+            av[arow * d + c] += P * gov[c];
+            DQ[qi * d + c] += sigma * dS * kv[c];
+            ak[arow * d + c] += sigma * dS * qv[c];
+          }
         }
       }
+      free(E);
+    }
+    /* sum the thread accumulators in thread order */
+    double* gk = (double*)calloc((size_t)(R * d), sizeof(double));
+    double* gv = (double*)calloc((size_t)(R * d), sizeof(double));
+    for (int64_t t = 0; t < n * d; ++t) { DK[t] = 0.0; DV[t] = 0.0; }
+    for (int th = 0; th < nthr; ++th) {
+      const double* ak = acc_k + th * acc_len;
+      const double* av = acc_v + th * acc_len;
+      for (int64_t t = 0; t < n * d; ++t) { DK[t] += ak[t]; DV[t] += av[t]; }
+      for (int64_t t = 0; t < R * d; ++t) { gk[t] += ak[n * d + t]; gv[t] += av[n * d + t]; }
     }
     /* pooling Jacobian: each pooled level-l token is the mean of B^l raw tokens */
     for (int l = 1; l <= L; ++l) {
@@ -406,8 +444,9 @@ void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
     if (dpv) memcpy(dpv + s * R * d, gv, sizeof(double) * (size_t)(R * d));
     free(gk);
     free(gv);
-    free(E);
   }
+  free(acc_k);
+  free(acc_v);
 }
 
 int llsa_ref_num_threads(void) {

@@ -1,0 +1,110 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point declared in
+include/llsa.h, and its host-side validation returns the documented status codes before any GPU call
+(no compute is issued here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from hierarchical_sparse_attention_mean_amd import llsa
+    return llsa
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "llsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(llsa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(L.lib(), n), n
+
+
+def test_resolve_defaults(L):
+    r = L.resolve(L.problem(1, 16, 65536))
+    assert (r.levels, r.enrich_levels, r.topk) == (3, 3, 8)
+    assert abs(r.scale - 0.125) < 1e-9
+    assert L.pyramid_rows(r) == 4096 + 256 + 16
+    assert L.colptr_len(r) == (4096 + 1) + (256 + 1) + (16 + 1)
+    assert L.perm_len(r) == (4096 + 256 + 16) * 8
+    r = L.resolve(L.problem(1, 2, 4096, dtype=L.F32))
+    assert (r.levels, r.enrich_levels) == (2, 2)
+    r = L.resolve(L.problem(1, 8, 262144, topk=16))
+    assert r.levels == 3 and L.pyramid_rows(r) == 16384 + 1024 + 64
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=4096 + 16), "ERR_SHAPE"),          # n mod B^L != 0 at the default L = 2
+    (dict(n=4096, levels=3), "ERR_SHAPE"),     # L above floor(log_B n - 1)
+    (dict(n=200), "ERR_SHAPE"),                # n < B^2: no pooled level
+    (dict(n=4096, topk=17), "ERR_SHAPE"),      # K > n_L = 16
+    (dict(n=4096, topk=0), "ERR_SHAPE"),
+    (dict(n=4096, enrich_levels=3), "ERR_SHAPE"),
+    (dict(n=4096, enrich_levels=-2), "ERR_SHAPE"),
+    (dict(n=4096, d=32), "ERR_UNSUPPORTED"),
+    (dict(n=4096, block=8), "ERR_UNSUPPORTED"),
+    (dict(n=1 << 20, levels=1, topk=8), "ERR_UNSUPPORTED"),  # n_L = 65536 > 512
+    (dict(n=4096, dtype=7), "ERR_DTYPE"),
+    (dict(n=4096, scale=float("inf")), "ERR_PARAM"),
+])
+def test_validation_codes(L, kw, code):
+    base = dict(batch=1, heads=2)
+    base.update(kw)
+    p = L.problem(**base)
+    assert L.lib().llsa_resolve(ctypes.byref(p), None) == getattr(L, code)
+    # the entry points return the same status and launch nothing
+    assert L.lib().llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None) == getattr(L, code)
+    assert L.workspace_bytes(p, L.OP_ATTN_BWD) == 0
+
+
+def test_null_and_alignment_checked_before_the_device(L):
+    p = L.problem(1, 2, 4096)
+    f = L.lib()
+    assert f.llsa_attn_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None) == L.ERR_NULL
+    assert f.llsa_build_pyramid(ctypes.byref(p), 16, 32, 48, 64, 80, 88, None) == L.ERR_ALIGN
+    assert f.llsa_select(None, 16, 16, 16, None) == L.ERR_NULL
+
+
+def test_workspace_checked_before_the_device(L):
+    p = L.problem(1, 2, 4096)
+    need = L.workspace_bytes(p, L.OP_INDEX_TRANSPOSE)
+    assert need > 0
+    f = L.lib()
+    assert f.llsa_index_transpose(ctypes.byref(p), 16, 32, 48, 64, need - 1, None) == L.ERR_WORKSPACE
+    assert f.llsa_index_transpose(ctypes.byref(p), 16, 32, 48, None, need, None) == L.ERR_WORKSPACE
+    nb = L.workspace_bytes(p, L.OP_ATTN_BWD)
+    args = [16] * 14
+    assert f.llsa_attn_bwd(ctypes.byref(p), *args, 64, nb - 1, None) == L.ERR_WORKSPACE
+    pf = L.problem(1, 2, 4096, dtype=L.F32)
+    assert f.llsa_attn_bwd(ctypes.byref(pf), *args, 64, nb, None) == L.ERR_DTYPE
+
+
+def test_empty_batch_is_a_no_op(L):
+    p = L.problem(0, 4, 4096)
+    f = L.lib()
+    assert f.llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None) == L.OK
+    assert f.llsa_attn_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None) == L.OK
+
+
+def test_workspace_is_linear_in_n(L):
+    """No dense N x N structure anywhere: workspaces grow linearly with the sequence length."""
+    a = L.problem(1, 1, 65536, topk=8)
+    b = L.problem(1, 1, 16 * 65536, topk=8, levels=3)
+    for op in (L.OP_INDEX_TRANSPOSE, L.OP_ATTN_BWD):
+        wa, wb = L.workspace_bytes(a, op), L.workspace_bytes(b, op)
+        assert wb <= 16 * wa * 1.01 + 4096, (op, wa, wb)
+
+
+def test_status_strings(L):
+    for s in range(0, -10, -1):
+        assert L.status_string(s) != "unknown status"
+    assert L.status_string(-99) == "unknown status"

@@ -1,0 +1,200 @@
+"""GPU parity of every hot-path step against the fp64 oracle, through the C ABI.
+
+Stage-wise: pyramid vs oracle pyramid; selection vs oracle selection under the selection-parity rule
+(rows compared where the parent matched and the K-th / (K+1)-th oracle scores differ by > 1e-3
+relative; ties toward the lower block index); forward, transpose and backward fed the *oracle's*
+selection so that they are compared element by element (fp32: 1e-4 max abs; bf16: per slice
+2e-2 x max |ref|; integer outputs bit-exact).  End-to-end: the GPU's own chain, outputs compared on
+query blocks whose whole selection chain matched.  Shapes span several tiles and ragged tails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check_close, dev, flat, host, selection_parity
+from hierarchical_sparse_attention_mean_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_sparse_attention_mean_amd import llsa
+    return llsa
+
+
+# (name, workload, levels, enrich_levels)
+CASES = [
+    ("tiny_f32_n4096", inputs.WORKLOADS["tiny_fwd_f32_n4096"], 2, -1),
+    ("bf16_n4096_h2", inputs.custom(1, 2, 4096, 64, "bf16", seed=11, topk=8, levels=2, backward=True), 2, -1),
+    ("bf16_ragged_n592_L1_K3", inputs.custom(1, 3, 592, 64, "bf16", seed=12, topk=3, levels=1, backward=True), 1, -1),
+    ("f32_ragged_n592_L1_K3", inputs.custom(1, 3, 592, 64, "f32", seed=13, topk=3, levels=1), 1, -1),
+    ("bf16_ragged_n5120_K5_b2", inputs.custom(2, 1, 5120, 64, "bf16", seed=14, topk=5, levels=2, backward=True), 2, -1),
+    ("bf16_n4096_Le0", inputs.custom(1, 2, 4096, 64, "bf16", seed=15, topk=8, levels=2, backward=True), 2, 0),
+    ("bf16_n4096_Le1", inputs.custom(1, 2, 4096, 64, "bf16", seed=16, topk=8, levels=2, backward=True), 2, 1),
+    ("bf16_n4096_fullK16", inputs.custom(1, 1, 4096, 64, "bf16", seed=17, topk=16, levels=2, backward=True), 2, -1),
+    ("f32_n4096_K7_Le1", inputs.custom(1, 2, 4096, 64, "f32", seed=18, topk=7, levels=2), 2, 1),
+    ("bf16_field_n65536_L3_h1", inputs.custom(1, 1, 65536, 64, "bf16", seed=19, kind="field", topk=8, levels=3,
+                                              backward=True), 3, -1),
+]
+_cache = {}
+
+
+def _prepare(name, w, levels, Le):
+    if name in _cache:
+        return _cache[name]
+    x = inputs.make_inputs(w)
+    ex = {k_: flat(t.exact) for k_, t in x.items()}
+    Le_ref = levels if Le == -1 else Le
+    ref = oracle.run(ex["q"], ex["k"], ex["v"], w.block, w.topk, levels=levels, enrich_levels=Le_ref,
+                     dout=ex.get("dout"))
+    _cache[name] = (x, ex, ref)
+    return _cache[name]
+
+
+def _prob(L, w, levels, Le):
+    return L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, levels, Le, L.BF16 if w.dtype == "bf16" else L.F32)
+
+
+@pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
+def test_pyramid(L, name, w, levels, Le):
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le), backward=False)
+    L.build_pyramid(b.prob, dev(x["q"]), dev(x["k"]), dev(x["v"]), b.pq, b.pk, b.pv)
+    torch.cuda.synchronize()
+    for nm, got in (("pq", b.pq), ("pk", b.pk), ("pv", b.pv)):
+        err = np.abs(host(got) - ref[nm]).max()
+        assert err <= 1e-5 * max(1.0, np.abs(ref[nm]).max()), (nm, err)
+
+
+@pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
+def test_select(L, name, w, levels, Le):
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le), backward=False)
+    L.build_pyramid(b.prob, dev(x["q"]), dev(x["k"]), dev(x["v"]), b.pq, b.pk, b.pv)
+    L.select(b.prob, b.pq, b.pk, b.idx)
+    torch.cuda.synchronize()
+    idx = b.idx.cpu().numpy()
+    compared, total = selection_parity(idx, ref["idx"], ref["pq"], ref["pk"], w.n, w.block, levels, w.topk)
+    print(f"{name}: selection rows compared {compared}/{total}")
+    assert compared >= 0.9 * total
+    # structure of every GPU row: distinct, ascending, in range
+    for l in range(1, levels + 1):
+        nl, off = w.n // w.block ** l, oracle.level_offset(w.n, w.block, l)
+        rows = idx[:, off:off + nl]
+        assert np.all(np.diff(rows, axis=2) > 0) and rows.min() >= 0 and rows.max() < nl
+
+
+@pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
+def test_forward_with_oracle_selection(L, name, w, levels, Le):
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le), backward=False)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    L.build_pyramid(b.prob, q, k, v, b.pq, b.pk, b.pv)
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    L.attn_fwd(b.prob, q, k, v, b.pk, b.pv, idx, b.o, b.lse)
+    torch.cuda.synchronize()
+    worst = check_close("O", flat(host(b.o)), ref["o"], w.dtype)
+    lse_err = np.abs(host(b.lse) - ref["lse"]).max()
+    assert lse_err <= (1e-4 if w.dtype == "f32" else 2e-2), lse_err
+    print(f"{name}: O worst {worst:.2e}, lse max err {lse_err:.2e}")
+
+
+def _backward_cases():
+    return [c for c in CASES if c[1].backward]
+
+
+@pytest.mark.parametrize("name,w,levels,Le", _backward_cases(), ids=[c[0] for c in _backward_cases()])
+def test_transpose_bit_exact(L, name, w, levels, Le):
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le))
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    L.index_transpose(b.prob, idx, b.col_ptr, b.perm, b.ws_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.col_ptr.cpu().numpy(), ref["col_ptr"])
+    assert np.array_equal(b.perm.cpu().numpy(), ref["perm"])
+
+
+@pytest.mark.parametrize("name,w,levels,Le", _backward_cases(), ids=[c[0] for c in _backward_cases()])
+def test_backward_with_oracle_selection(L, name, w, levels, Le):
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le))
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    L.build_pyramid(b.prob, q, k, v, b.pq, b.pk, b.pv)
+    b.idx.copy_(torch.from_numpy(ref["idx"]))
+    L.attn_fwd(b.prob, q, k, v, b.pk, b.pv, b.idx, b.o, b.lse)
+    b.backward(q, k, v, do)
+    torch.cuda.synchronize()
+    msg = []
+    for nm, got in (("dq", b.dq), ("dk", b.dk), ("dv", b.dv)):
+        worst = check_close(nm, flat(host(got)), ref[nm], w.dtype)
+        msg.append(f"{nm} {worst:.2e}")
+    print(f"{name}: " + ", ".join(msg))
+
+
+@pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
+def test_end_to_end_chain(L, name, w, levels, Le):
+    """The GPU's own selection feeds the forward; O is compared on every fine query block whose
+    selection rows (at all levels) equal the oracle's."""
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le), backward=False)
+    b.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]))
+    torch.cuda.synchronize()
+    idx = b.idx.cpu().numpy()
+    n1 = w.n // w.block
+    clean = np.ones((w.bh, n1), bool)
+    for l in range(1, levels + 1):
+        off, nl = oracle.level_offset(w.n, w.block, l), w.n // w.block ** l
+        same = np.all(idx[:, off:off + nl] == ref["idx"][:, off:off + nl], axis=2)
+        clean &= same[:, np.arange(n1) // w.block ** (l - 1)]
+    assert clean.mean() >= 0.9
+    o = flat(host(b.o)).reshape(w.bh, n1, w.block, w.d)
+    r = ref["o"].reshape(w.bh, n1, w.block, w.d)
+    tol = 1e-4 if w.dtype == "f32" else 2e-2
+    for s in range(w.bh):
+        err = np.abs(o[s][clean[s]] - r[s][clean[s]]).max()
+        lim = tol if w.dtype == "f32" else tol * np.abs(r[s]).max()
+        assert err <= lim, (s, err, lim)
+
+
+@pytest.mark.parametrize("name,w,levels,Le", _backward_cases()[:3], ids=[c[0] for c in _backward_cases()[:3]])
+def test_deterministic(L, name, w, levels, Le):
+    """Two runs of the whole chain are bitwise identical (no floating-point atomics anywhere)."""
+    x, ex, ref = _prepare(name, w, levels, Le)
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    outs = []
+    for _ in range(2):
+        b = L.Buffers(_prob(L, w, levels, Le))
+        b.forward(q, k, v)
+        b.backward(q, k, v, do)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (b.idx, b.o, b.lse, b.col_ptr, b.perm, b.dq, b.dk, b.dv)])
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
+
+
+def test_tie_rule_on_gpu(L):
+    """Every pooled key equal: all scores tie exactly, every unit keeps the lowest block indices."""
+    n, K = 4096, 8
+    w = inputs.custom(1, 1, n, 64, "bf16", seed=20, topk=K, levels=2)
+    x = inputs.make_inputs(w)
+    kconst = np.broadcast_to(x["k"].store[:, :, :1, :], x["k"].store.shape).copy()
+    b = L.Buffers(L.problem(1, 1, n, topk=K, levels=2), backward=False)
+    kt = torch.from_numpy(kconst.view(np.int16)).cuda().view(torch.bfloat16)
+    b.forward(dev(x["q"]), kt, dev(x["v"]))
+    torch.cuda.synchronize()
+    idx = b.idx.cpu().numpy()[0]
+    assert np.all(idx[256:272] == np.arange(K))     # level 2: blocks 0..7
+    assert np.all(idx[:256] == np.arange(K))         # level 1: children 0..7 of block 0
+
+
+def test_empty_batch(L):
+    p = L.problem(0, 2, 4096)
+    e = torch.empty(0, device="cuda")
+    L.build_pyramid(p, e, e, e, e, e, e)
+    L.attn_fwd(p, e, e, e, e, e, e.int(), e, e)
