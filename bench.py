@@ -1,0 +1,210 @@
+"""Benchmark of the LLSA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input already resident in HBM:
+pyramid -> hierarchical selection -> enriched attention forward -> CSR->CSC transpose -> backward,
+each through the C ABI of libllsa.so on torch's current stream.  The workload is the N = 65536
+forward+backward configuration (batch 1, 16 heads, head dim 64, bf16, B = 16, K = 8, L = 3, smooth
+2-D Gaussian-random-field inputs on a 256x256 grid plus 0.1 noise, dO ~ N(0, 1)).
+
+Prints ONE JSON line: the metric (ms per fwd+bwd step, lower is better), a per-stage breakdown, the
+roofline of the dominant kernel (algorithmic bytes / its average launch time, timed with events on
+the launch stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "LLSA fwd+bwd ms at N=65536 (MFMA util %, selection HBM GB/s)"
+WORKLOAD = "fwdbwd_bf16_n65536"
+
+
+KERNEL_SYMBOL = {"pool": "pool_levels123<bf16>", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
+                 "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "coarse_reduce",
+                 "bwd_dkdv": "bwd_dkdv_bf16"}
+
+
+def algorithmic(w, levels, enrich):
+    """Algorithmic bytes and flops per step of every kernel family: each tensor is counted once (a gathered
+    K/V block read by many query blocks counts once), products at their exact sizes (no padding)."""
+    bh, n, d, B, K = w.bh, w.n, w.d, w.block, w.topk
+    s = 2  # bf16 bytes
+    tokens = bh * n
+    rows = [n // B ** l for l in range(1, levels + 1)]
+    R = sum(rows)
+    pooled_frac = sum(B ** -l for l in range(1, levels + 1))
+    fine = K * B                                       # raw keys per query
+    coarse = K * enrich                                # enrichment tokens per query
+    nhigh = K * max(0, enrich - 1)                     # enrichment tokens of levels >= 2 per query
+    pooled_kv = 2 * bh * R * d * 4                     # both fp32 pyramids of K and V
+    out = {}
+    # pyramid: read Q, K, V once, write three fp32 pyramids
+    out["pool"] = dict(bytes=tokens * (3 * d * s + 3 * d * 4 * pooled_frac), flops=0.0)
+    # selection: per pooled query unit read its pooled query and key rows (fp32), its parent row and write
+    # K indices; flops of the scored (unit, block) pairs
+    out["select"] = dict(bytes=bh * R * (2 * d * 4 + 2 * K * 4),
+                         flops=2.0 * d * bh * (rows[-1] ** 2 + sum(rows[l - 1] * K * B for l in range(1, levels))))
+    # forward: read Q, K, V, write O (bf16), write LSE, read the pooled K/V once; QK^T and PV products
+    out["attn_fwd"] = dict(bytes=tokens * (4 * d * s + 4) + pooled_kv, flops=4.0 * d * (fine + coarse) * tokens)
+    # transpose: read each CSR entry, write it to the CSC, write col_ptr
+    T = max(1, min(enrich, levels))
+    nnz = bh * sum(rows[l - 1] * K for l in range(1, T + 1))
+    out["transpose"] = dict(bytes=8.0 * nnz + 4.0 * bh * sum(rows[l - 1] + 1 for l in range(1, T + 1)), flops=0.0)
+    # backward dQ kernel: read Q, K, V, O, dO, LSE, pooled K/V; write dQ, Delta, pooled-token partials;
+    # products S, dP, dQ over every entry plus the pooled dK/dV partials of levels >= 2
+    n2 = rows[1] if levels >= 2 else 0
+    part = 2 * bh * n2 * nhigh * d * 4
+    out["bwd_dq"] = dict(bytes=tokens * (6 * d * s + 8) + pooled_kv + part,
+                         flops=6.0 * d * (fine + coarse) * tokens + 4.0 * d * nhigh * tokens)
+    # pooled-gradient reduction: read the partials, write the reduced pooled gradients of levels >= 2
+    out["bwd_reduce"] = dict(bytes=part + 2 * bh * (R - rows[0]) * d * 4, flops=0.0)
+    # backward dK/dV kernel: read K, V, Q, dO, LSE, Delta, level-1 pooled K/V and reduced gradients; write dK, dV;
+    # products S, dP, dV, dK over the fine entries plus the level-1 pooled token
+    out["bwd_dkdv"] = dict(bytes=tokens * (6 * d * s + 8) + 2 * bh * rows[0] * d * 4 + 2 * bh * (R - rows[0]) * d * 4,
+                           flops=8.0 * d * fine * tokens + 6.0 * d * K * tokens)
+    return out
+
+
+def oracle_baseline(w, x, budget_s=20.0):
+    """Oracle chain timed on whole (batch, head) slices until ~budget_s of CPU work; scaled to one step."""
+    import oracle
+    t_all = 0.0
+    done = 0
+    for h in range(w.bh):
+        q, k, v, do = (x[nm].exact.reshape(w.bh, w.n, w.d)[h:h + 1] for nm in ("q", "k", "v", "dout"))
+        t0 = time.perf_counter()
+        oracle.run(q, k, v, w.block, w.topk, levels=w.levels, dout=do)
+        t_all += time.perf_counter() - t0
+        done += 1
+        if t_all >= budget_s:
+            break
+    ms_full = t_all / done * w.bh * 1e3
+    return {"value": round(ms_full, 1), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.bh} (batch, head) slices of the {WORKLOAD} workload, full chain "
+                      f"(pool, select, forward, transpose, backward) in fp64; {t_all:.1f} s measured, "
+                      f"scaled by {w.bh}/{done} to one step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
+              "(batch x heads) with no exchange, but only the one-GPU share is built and measured)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hierarchical_sparse_attention_mean_amd import inputs, llsa
+
+    w = inputs.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    x = inputs.make_inputs(w, with_dout=True)
+    gen_s = time.perf_counter() - t0
+
+    def dev(t):
+        return torch.from_numpy(t.store.view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    b = llsa.Buffers(llsa.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    p = b.prob
+    stream = torch.cuda.current_stream()
+
+    def step():
+        llsa.build_pyramid(p, q, k, v, b.pq, b.pk, b.pv, stream)
+        llsa.select(p, b.pq, b.pk, b.idx, stream)
+        llsa.attn_fwd(p, q, k, v, b.pk, b.pv, b.idx, b.o, b.lse, stream)
+        llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
+        llsa.attn_bwd(p, q, k, v, b.o, b.lse, do, b.pk, b.pv, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv, b.ws_b,
+                      stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # Second timed region over the same work with the library's per-kernel event timing switched on: every
+    # kernel launch is bracketed by hipEvents recorded on the stream it is launched on.
+    llsa.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step_events = (time.perf_counter() - t0) * 1e3 / args.steps
+    fam = llsa.timing_read()
+    llsa.timing_enable(False)
+
+    alg = algorithmic(w, p.levels, p.enrich_levels)
+    kernels = {}
+    for nm, (tot, cnt) in fam.items():
+        if cnt == 0:
+            continue
+        per_step = tot / args.steps
+        a = alg[nm]
+        kernels[nm] = {"ms_per_step": round(per_step, 4), "launches_per_step": cnt // args.steps,
+                       "avg_launch_ms": round(tot / cnt, 4),
+                       "alg_GBps": round(a["bytes"] / (per_step * 1e-3) / 1e9, 1),
+                       "alg_TFLOPs": round(a["flops"] / (per_step * 1e-3) / 1e12, 2)}
+    dom = max(kernels, key=lambda nm: kernels[nm]["ms_per_step"])
+    dk = kernels[dom]
+    a_gbs = alg[dom]["bytes"] / (dk["avg_launch_ms"] * 1e-3) / 1e9 if dk["launches_per_step"] == 1 else dk["alg_GBps"]
+    roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": KERNEL_SYMBOL[dom], "kernel_avg_ms": dk["avg_launch_ms"],
+                "alg_bytes_per_launch": alg[dom]["bytes"], "alg_flops_per_launch": alg[dom]["flops"],
+                "mfma_frac": round(alg[dom]["flops"] / (dk["avg_launch_ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+    attn = ("attn_fwd", "bwd_dq", "bwd_reduce", "bwd_dkdv")
+    attn_flops = sum(alg[nm]["flops"] for nm in attn)
+    attn_ms = sum(kernels[nm]["ms_per_step"] for nm in attn if nm in kernels)
+    mfma_util = attn_flops / (attn_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+    sel_gbs = kernels["select"]["alg_GBps"]
+    pool_gbs = kernels["pool"]["alg_GBps"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = oracle_baseline(w, x)
+
+    rec = {
+        "metric": METRIC, "value": round(ms_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n, "head_dim": w.d,
+                   "block": w.block, "topk": w.topk, "levels": p.levels, "enrich_levels": p.enrich_levels,
+                   "grid": list(w.grid), "inputs": "2-D Gaussian random field (l=16 px) projected to 64 dims + 0.1 noise",
+                   "parallelism": "none (one GPU)"},
+        "mfma_util_pct_attention": round(100 * mfma_util, 2),
+        "selection_alg_GBps": round(sel_gbs, 1),
+        "pyramid_alg_GBps": round(pool_gbs, 1),
+        "ms_per_step_with_kernel_events": round(ms_step_events, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

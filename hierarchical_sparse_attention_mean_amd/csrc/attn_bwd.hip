@@ -484,18 +484,25 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
                            void* dv, const BwdWs& ws, hipStream_t stream) {
   const int n1 = g.rows[1];
   const int groups = g.bh * ((n1 + 15) / 16);
-  bwd_dq_bf16<<<groups, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
+  {
+    LaunchTimer timer(kBwdDq, stream);
+    bwd_dq_bf16<<<groups, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
                                           lse, (const bf16_t*)dout, pk, pv, idx, (bf16_t*)dq, ws.delta, ws.part_k,
                                           ws.part_v, g);
+  }
   if (g.Le >= 2) {
     int tokens = 0;
     for (int l = 2; l <= g.Le; ++l) tokens += g.rows[l];
+    LaunchTimer timer(kBwdReduce, stream);
     coarse_reduce<<<dim3(tokens, g.bh), 64, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, g,
                                                           cg);
   }
-  bwd_dkdv_bf16<<<(g.bh * n1 + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+  {
+    LaunchTimer timer(kBwdDkdv, stream);
+    bwd_dkdv_bf16<<<(g.bh * n1 + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                                                          (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm,
                                                          ws.gk, ws.gv, (bf16_t*)dk, (bf16_t*)dv, g, cg);
+  }
   return hipGetLastError();
 }
 

@@ -305,6 +305,7 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
                            hipStream_t stream) {
   const int nb = g.bh * g.rows[1];
   const int grid = (nb + 3) / 4;
+  LaunchTimer timer(kAttnFwd, stream);
   if (dtype_bf16)
     attn_fwd_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pk, pv, idx,
                                             (bf16_t*)o, lse, g);

@@ -8,6 +8,23 @@
 
 namespace llsa {
 
+// Kernel-family ids (same values as LLSA_KERNEL_* in llsa.h).
+enum KernelFamily { kPool = 0, kSelect, kAttnFwd, kTranspose, kBwdDq, kBwdReduce, kBwdDkdv, kFamilies };
+
+// Brackets one kernel launch with hipEvents on its stream while timing is enabled (llsa_timing_enable).
+class LaunchTimer {
+ public:
+  LaunchTimer(int family, hipStream_t stream);
+  ~LaunchTimer();
+  LaunchTimer(const LaunchTimer&) = delete;
+  LaunchTimer& operator=(const LaunchTimer&) = delete;
+
+ private:
+  int family_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
 // Per-level offsets of the concatenated CSC arrays (levels 1..T).
 struct CscGeom {
   int T;                        // transposed levels

@@ -151,13 +151,19 @@ hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const vo
     units = (g.rows[1] + 15) / 16;
   }
   dim3 grid(units, g.bh, 3);
-  if (dtype_bf16)
-    pool_levels123<bf16_t><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pq,
-                                                      pk, pv, g, chunks);
-  else
-    pool_levels123<float><<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pq, pk,
-                                                     pv, g, chunks);
-  for (int l = 4; l <= g.L; ++l) pool_up<<<dim3(g.rows[l], g.bh, 3), 64, 0, stream>>>(pq, pk, pv, g, l);
+  {
+    LaunchTimer timer(kPool, stream);
+    if (dtype_bf16)
+      pool_levels123<bf16_t><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pq,
+                                                        pk, pv, g, chunks);
+    else
+      pool_levels123<float><<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pq, pk,
+                                                       pv, g, chunks);
+  }
+  for (int l = 4; l <= g.L; ++l) {
+    LaunchTimer timer(kPool, stream);
+    pool_up<<<dim3(g.rows[l], g.bh, 3), 64, 0, stream>>>(pq, pk, pv, g, l);
+  }
   return hipGetLastError();
 }
 

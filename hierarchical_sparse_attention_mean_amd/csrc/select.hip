@@ -150,12 +150,14 @@ hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_
     const int ncand = ((nL + 15) / 16) * 16;
     const int ldc = ncand + 4;
     dim3 grid((nL + 15) / 16, g.bh);
+    LaunchTimer timer(kSelect, stream);
     select_level<<<grid, 256, 16 * ldc * sizeof(float), stream>>>(pq, pk, idx, g, g.L, 1, nL, ldc);
   }
   for (int l = g.L - 1; l >= 1; --l) {
     const int ncand = g.K * kB;
     const int ldc = ncand + 4;
     dim3 grid(g.rows[l + 1], g.bh);
+    LaunchTimer timer(kSelect, stream);
     select_level<<<grid, 256, 16 * ldc * sizeof(float), stream>>>(pq, pk, idx, g, l, 0, ncand, ldc);
   }
   return hipGetLastError();

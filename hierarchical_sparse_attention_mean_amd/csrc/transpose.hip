@@ -128,12 +128,27 @@ __global__ __launch_bounds__(256) void csc_order(const int32_t* __restrict__ idx
 hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_t* idx, int32_t* col_ptr,
                                   int32_t* perm, int32_t* ws_cnt, int32_t* ws_tmp, hipStream_t stream) {
   const int64_t ncnt = (int64_t)g.bh * cg.cp_len;
-  zero_i32<<<(int)((ncnt + 255) / 256 < 4096 ? (ncnt + 255) / 256 : 4096), 256, 0, stream>>>(ws_cnt, ncnt);
+  {
+    LaunchTimer timer(kTranspose, stream);
+    zero_i32<<<(int)((ncnt + 255) / 256 < 4096 ? (ncnt + 255) / 256 : 4096), 256, 0, stream>>>(ws_cnt, ncnt);
+  }
   const dim3 egrid((cg.pm_len + 255) / 256, g.bh);
-  csc_count<<<egrid, 256, 0, stream>>>(idx, ws_cnt, g, cg);
-  csc_scan<<<dim3(cg.T, g.bh), 1024, 0, stream>>>(ws_cnt, col_ptr, g, cg);
-  csc_scatter<<<egrid, 256, 0, stream>>>(idx, ws_cnt, ws_tmp, g, cg);
-  csc_order<<<egrid, 256, 0, stream>>>(idx, col_ptr, ws_tmp, perm, g, cg);
+  {
+    LaunchTimer timer(kTranspose, stream);
+    csc_count<<<egrid, 256, 0, stream>>>(idx, ws_cnt, g, cg);
+  }
+  {
+    LaunchTimer timer(kTranspose, stream);
+    csc_scan<<<dim3(cg.T, g.bh), 1024, 0, stream>>>(ws_cnt, col_ptr, g, cg);
+  }
+  {
+    LaunchTimer timer(kTranspose, stream);
+    csc_scatter<<<egrid, 256, 0, stream>>>(idx, ws_cnt, ws_tmp, g, cg);
+  }
+  {
+    LaunchTimer timer(kTranspose, stream);
+    csc_order<<<egrid, 256, 0, stream>>>(idx, col_ptr, ws_tmp, perm, g, cg);
+  }
   return hipGetLastError();
 }
 

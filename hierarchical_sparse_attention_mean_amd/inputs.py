@@ -22,6 +22,7 @@ Recipe
 """
 from __future__ import annotations
 
+import concurrent.futures
 import math
 from dataclasses import dataclass, field
 
@@ -142,12 +143,19 @@ def make_inputs(w: Workload, heads: list | None = None, with_dout: bool | None =
     (bh indices); the values of a slice never depend on which other slices are drawn."""
     slices = list(range(w.bh)) if heads is None else list(heads)
     with_dout = w.backward if with_dout is None else with_dout
-    qs, ks, vs, dos = [], [], [], []
-    for s in slices:
+
+    def one(s):
         q, k, v = _slice_values(w, s, w.d)
-        qs.append(q); ks.append(k); vs.append(v)
-        if with_dout:
-            dos.append(rng(w.seed, s, STREAM_DO).standard_normal((w.n, w.d)))
+        do = rng(w.seed, s, STREAM_DO).standard_normal((w.n, w.d)) if with_dout else None
+        return q, k, v, do
+
+    # slices are independent streams, so drawing them concurrently gives the same values
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(slices)) or 1) as ex:
+        drawn = list(ex.map(one, slices))
+    qs = [t[0] for t in drawn]
+    ks = [t[1] for t in drawn]
+    vs = [t[2] for t in drawn]
+    dos = [t[3] for t in drawn] if with_dout else []
     shape = (1, len(slices), w.n, w.d) if heads is not None else (w.batch, w.heads, w.n, w.d)
     out = {name: to_dtype(np.stack(arr).reshape(shape), w.dtype)
            for name, arr in (("q", qs), ("k", ks), ("v", vs)) if arr}

@@ -24,6 +24,7 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_PARAM, ERR_DEVICE = \
     -1, -2, -3, -4, -5, -6, -7, -8, -9
 OP_INDEX_TRANSPOSE, OP_ATTN_BWD = 1, 2
+KERNELS = ("pool", "select", "attn_fwd", "transpose", "bwd_dq", "bwd_reduce", "bwd_dkdv")  # LLSA_KERNEL_* order
 
 
 class Problem(ctypes.Structure):
@@ -65,6 +66,10 @@ for _f in ("llsa_pyramid_rows", "llsa_colptr_len", "llsa_perm_len"):
     getattr(_lib, _f).restype = ctypes.c_int64
 _lib.llsa_workspace_bytes.argtypes = [_P, ctypes.c_int]
 _lib.llsa_workspace_bytes.restype = ctypes.c_size_t
+_lib.llsa_timing_enable.argtypes = [ctypes.c_int]
+_lib.llsa_timing_enable.restype = ctypes.c_int
+_lib.llsa_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+_lib.llsa_timing_read.restype = ctypes.c_int
 _lib.llsa_status_string.argtypes = [ctypes.c_int]
 _lib.llsa_status_string.restype = ctypes.c_char_p
 
@@ -102,6 +107,21 @@ def perm_len(prob: Problem) -> int:
 
 def workspace_bytes(prob: Problem, op: int) -> int:
     return int(_lib.llsa_workspace_bytes(ctypes.byref(prob), op))
+
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel launch with hipEvents on its stream (clears earlier records)."""
+    _check(_lib.llsa_timing_enable(1 if on else 0), "llsa_timing_enable")
+
+
+def timing_read() -> dict:
+    """{kernel family: (total ms, launches)} of the launches recorded since timing_enable."""
+    out = {}
+    for i, name in enumerate(KERNELS):
+        t, c = ctypes.c_double(), ctypes.c_int64()
+        _check(_lib.llsa_timing_read(i, ctypes.byref(t), ctypes.byref(c)), "llsa_timing_read")
+        out[name] = (t.value, c.value)
+    return out
 
 
 def _ptr(t):

@@ -18,14 +18,16 @@
  *
  * Ownership: the caller allocates and owns every buffer, including workspaces; the library allocates
  * nothing on these paths, keeps no pointer after returning and holds no state beyond a cached
- * per-device property query.  Calls are re-entrant.
+ * per-device property query (and, only while llsa_timing_enable is on, its timing events).  Calls are
+ * re-entrant.
  * Asynchrony: each call validates on the host, then enqueues kernels on `stream` (a hipStream_t;
  * NULL means the default stream) and returns without synchronising.  Outputs are complete when the
  * stream reaches that point; they are overwritten, never accumulated.
  * Errors: each call returns LLSA_OK (0) or a negative LLSA_ERR_* code; on a validation error nothing
  * is launched.  No exception crosses the ABI.  Non-finite inputs give unspecified outputs.
  * Pointers must be 16-byte aligned (LLSA_ERR_ALIGN).
- * GPU limits of this version: d = 64, B = 16, 1 <= K <= n_L, K <= 64, n_L <= 1024, batch*heads*n*d < 2^31.
+ * GPU limits of this version: d = 64, B = 16, 1 <= K <= n_L, K <= 32, n_L <= 512, K*(L_e-1) <= 32 for the
+ * backward, batch*heads*n*d < 2^31.
  */
 #ifndef LLSA_H
 #define LLSA_H
@@ -146,6 +148,27 @@ int64_t llsa_perm_len(const llsa_problem* prob);
 size_t llsa_workspace_bytes(const llsa_problem* prob, int op);
 /* Static, NUL-terminated description of a status code. */
 const char* llsa_status_string(int status);
+
+
+/* ---- kernel timing (for benchmarks) ------------------------------------------------------------ */
+/* Kernel families of this library, for llsa_timing_read. */
+enum {
+  LLSA_KERNEL_POOL = 0,       /* pyramid pooling                                   */
+  LLSA_KERNEL_SELECT = 1,     /* hierarchical Top-K, one launch per level          */
+  LLSA_KERNEL_ATTN_FWD = 2,   /* enriched attention forward                        */
+  LLSA_KERNEL_TRANSPOSE = 3,  /* CSR -> CSC: zero, count, scan, scatter, order     */
+  LLSA_KERNEL_BWD_DQ = 4,     /* backward: dQ, Delta, pooled-token partials        */
+  LLSA_KERNEL_BWD_REDUCE = 5, /* backward: pooled-token gradient reduction         */
+  LLSA_KERNEL_BWD_DKDV = 6,   /* backward: dK, dV through the CSC                  */
+  LLSA_KERNEL_COUNT = 7
+};
+/* While enabled, every kernel this library launches is bracketed by two hipEvents recorded on its
+ * launch stream (process-wide switch; off by default).  Enabling clears earlier records.  The events
+ * are library-owned and released by the next llsa_timing_enable call.  Returns a status. */
+int llsa_timing_enable(int on);
+/* Waits for the recorded events of kernel family `kernel` and returns the summed duration (ms) and
+ * the number of launches recorded since timing was enabled. */
+int llsa_timing_read(int kernel, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -108,3 +108,13 @@ def test_status_strings(L):
     for s in range(0, -10, -1):
         assert L.status_string(s) != "unknown status"
     assert L.status_string(-99) == "unknown status"
+
+
+def test_timing_api_without_launches(L):
+    L.timing_enable(True)
+    rec = L.timing_read()
+    assert set(rec) == set(L.KERNELS) and all(v == (0.0, 0) for v in rec.values())
+    L.timing_enable(False)
+    t, c = ctypes.c_double(), ctypes.c_int64()
+    assert L.lib().llsa_timing_read(99, ctypes.byref(t), ctypes.byref(c)) == L.ERR_PARAM
+    assert L.lib().llsa_timing_read(0, None, None) == L.ERR_NULL
