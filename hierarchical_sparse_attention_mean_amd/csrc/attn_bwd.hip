@@ -22,6 +22,7 @@
 //      added before the bf16 store.
 // Every gradient element is owned by one wavefront: no floating-point atomics, bitwise reproducible.
 #include "common.hpp"
+#include "entries.hpp"
 #include "launch.hpp"
 
 namespace llsa {
@@ -32,23 +33,10 @@ constexpr int kLd = kD + 8;   // bf16 row stride of K / Q / dO tiles in LDS
 constexpr int kSt = 16 + 8;   // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
 constexpr int kMaxHigh = 32;  // enrichment entries of levels >= 2 per query (K * (Le - 1))
 
-__device__ __forceinline__ void coarse_entry(const Geom& g, int e, int* level, int* slot) {
-  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
-  if (e < nhigh) {
-    *level = 2 + e / g.K;
-    *slot = e % g.K;
-  } else {
-    *level = 1;
-    *slot = e - nhigh;
-  }
-}
-
+// Pyramid row of enrichment entry e for fine block i, and its level.
 __device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e, int* level) {
-  int l, s;
-  coarse_entry(g, e, &l, &s);
-  *level = l;
-  const int unit = i >> (4 * (l - 1));
-  return g.off[l] + I[(size_t)(g.off[l] + unit) * g.K + s];
+  *level = coarse_level(g, e);
+  return coarse_row(g, I, i, e);
 }
 
 __device__ __forceinline__ float dot16_bf16(uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
@@ -64,11 +52,9 @@ __device__ __forceinline__ float dot16_bf16(uint4 a0, uint4 a1, uint4 b0, uint4 
 }
 
 __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
+  const uint2 u = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   bf16x4 r;
-  r[0] = (short)f32_to_bf16(a);
-  r[1] = (short)f32_to_bf16(b);
-  r[2] = (short)f32_to_bf16(c);
-  r[3] = (short)f32_to_bf16(d);
+  __builtin_memcpy(&r, &u, 8);
   return r;
 }
 
@@ -175,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16(const bf16_t* __restrict__ q,
         const bool ok = t2 == 0 || has1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = ok ? exp2f(s[r] * g.scale_log2 - lse2) : 0.f;
+          const float p = ok ? fast_exp2(s[r] * g.scale_log2 - lse2) : 0.f;
           ds[4 * t2 + r] = p * (dpv[r] - dlt);
         }
       }
@@ -213,7 +199,7 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16(const bf16_t* __restrict__ q,
           const int e = e0 + 16 * t2 + 4 * gq + r;
           int lvl, slot;
           coarse_entry(g, e, &lvl, &slot);
-          const float p = e < ncoarse ? exp2f(s[r] * g.scale_log2 + 4.0f * (float)lvl - lse2) : 0.f;
+          const float p = e < ncoarse ? fast_exp2(s[r] * g.scale_log2 + 4.0f * (float)lvl - lse2) : 0.f;
           pr[4 * t2 + r] = p;
           ds[4 * t2 + r] = p * (dpv[r] - dlt);
         }
@@ -343,28 +329,42 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
                                                      bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
   __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kLd];
   __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kLd];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
   const int gb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
   if (gb >= g.bh * n1) return;  // no workgroup barrier below
   const int slice = gb / n1, j = gb - slice * n1;
   const size_t base = (size_t)slice * g.n * kD;
-  const size_t krow = base + (size_t)(16 * j + c) * kD + 16 * gq;
-  const bf16x8 kb0 = as_bf16x8(ld16(k + krow)), kb1 = as_bf16x8(ld16(k + krow + 8));
-  const bf16x8 vb0 = as_bf16x8(ld16(v + krow)), vb1 = as_bf16x8(ld16(v + krow + 8));
-  // level-1 pooled token of this block, rounded to bf16 as in the forward products
-  uint4 pk1[2], pv1[2];
+  const bf16_t* Q = q + base;
+  const bf16_t* DO = dout + base;
+  const float* LS = lse + (size_t)slice * g.n;
+  const float* DL = delta + (size_t)slice * g.n;
+
+  // B operands (natural order) of this key block: K and V rows 16j + c
+  bf16x8 kb0, kb1, vb0, vb1;
+  {
+    uint4 a0, a1;
+    load_natural(k + base, 16u * j + c, lane, a0, a1);
+    kb0 = as_bf16x8(a0);
+    kb1 = as_bf16x8(a1);
+    load_natural(v + base, 16u * j + c, lane, a0, a1);
+    vb0 = as_bf16x8(a0);
+    vb1 = as_bf16x8(a1);
+  }
+  // level-1 pooled token of this block as a broadcast B operand (every column holds it), rounded to bf16
+  // as in the forward products: its scores land in the same [query 4g+r] layout as the raw keys' scores
   const bool enrich1 = g.Le >= 1;
-  if (enrich1) {
-    const float4* kp = reinterpret_cast<const float4*>(pk + ((size_t)slice * g.R + g.off[1] + j) * kD + 16 * gq);
-    const float4* vp = reinterpret_cast<const float4*>(pv + ((size_t)slice * g.R + g.off[1] + j) * kD + 16 * gq);
-    bf16x8 a = f32x8_to_bf16x8(kp[0], kp[1]), b = f32x8_to_bf16x8(kp[2], kp[3]);
-    __builtin_memcpy(&pk1[0], &a, 16);
-    __builtin_memcpy(&pk1[1], &b, 16);
-    a = f32x8_to_bf16x8(vp[0], vp[1]);
-    b = f32x8_to_bf16x8(vp[2], vp[3]);
-    __builtin_memcpy(&pv1[0], &a, 16);
-    __builtin_memcpy(&pv1[1], &b, 16);
+  bf16x8 k1b0, k1b1, v1b0, v1b1;
+  {
+    const float* kp = pk + ((size_t)slice * g.R + g.off[1] + j) * kD + 8 * gq;
+    const float* vp = pv + ((size_t)slice * g.R + g.off[1] + j) * kD + 8 * gq;
+    const float4* k4 = reinterpret_cast<const float4*>(kp);
+    const float4* v4 = reinterpret_cast<const float4*>(vp);
+    k1b0 = f32x8_to_bf16x8(k4[0], k4[1]);
+    k1b1 = f32x8_to_bf16x8(k4[8], k4[9]);
+    v1b0 = f32x8_to_bf16x8(v4[0], v4[1]);
+    v1b1 = f32x8_to_bf16x8(v4[8], v4[9]);
   }
   f32x4 dk_acc[4], dv_acc[4];
 #pragma unroll
@@ -372,49 +372,63 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
 
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
   const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[1];
-  const float* LS = lse + (size_t)slice * g.n;
-  const float* DL = delta + (size_t)slice * g.n;
-  const bf16_t* qr = qs[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-  const bf16_t* dr = dos[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-  const int y1 = cp[j + 1];
-  for (int y = cp[j]; y < y1; ++y) {
-    const int i = pm[y] / g.K;  // query block that kept this key block
-    const size_t qrow = base + (size_t)(16 * i + c) * kD + 16 * gq;
-    const uint4 q0 = ld16(q + qrow), q1 = ld16(q + qrow + 8);
-    const uint4 d0 = ld16(dout + qrow), d1 = ld16(dout + qrow + 8);
-    const float4 ls4 = *reinterpret_cast<const float4*>(LS + 16 * i + 4 * gq);
-    const float4 dl4 = *reinterpret_cast<const float4*>(DL + 16 * i + 4 * gq);
+  const int y0 = cp[j], y1 = cp[j + 1];
+  bf16_t* qt = qs[w];
+  bf16_t* dt = dos[w];
+  const bf16_t* qr = qt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+  const bf16_t* dr = dt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+
+  // One stage = one query block of the column: natural-order Q and dO rows 16i + c, LSE and Delta of
+  // queries 16i + 4g .. +3 (the rows of the S layout).
+  struct QStage {
+    uint4 q0, q1, d0, d1;
+    float4 ls, dl;
+  };
+  auto issue = [&](int i, QStage& st) {
+    load_natural(Q, 16u * i + c, lane, st.q0, st.q1);
+    load_natural(DO, 16u * i + c, lane, st.d0, st.d1);
+    st.ls = *reinterpret_cast<const float4*>(LS + 16 * i + 4 * gq);
+    st.dl = *reinterpret_cast<const float4*>(DL + 16 * i + 4 * gq);
+  };
+  auto consume = [&](const QStage& st) {
     {
-      uint4* qd = reinterpret_cast<uint4*>(qs[w] + c * kLd + 16 * gq);
-      uint4* dd = reinterpret_cast<uint4*>(dos[w] + c * kLd + 16 * gq);
-      qd[0] = q0; qd[1] = q1; dd[0] = d0; dd[1] = d1;
+      uint4* qd = reinterpret_cast<uint4*>(qt + c * kLd + 8 * gq);
+      uint4* dd = reinterpret_cast<uint4*>(dt + c * kLd + 8 * gq);
+      qd[0] = st.q0;
+      qd[4] = st.q1;  // +32 elements
+      dd[0] = st.d0;
+      dd[4] = st.d1;
     }
+    const bf16x8 qa0 = as_bf16x8(st.q0), qa1 = as_bf16x8(st.q1);
+    const bf16x8 da0 = as_bf16x8(st.d0), da1 = as_bf16x8(st.d1);
     f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
-    s = mfma_bf16_k32(as_bf16x8(q0), kb0, s);
-    s = mfma_bf16_k32(as_bf16x8(q1), kb1, s);
-    dpv = mfma_bf16_k32(as_bf16x8(d0), vb0, dpv);
-    dpv = mfma_bf16_k32(as_bf16x8(d1), vb1, dpv);
+    s = mfma_bf16_k32(qa0, kb0, s);
+    s = mfma_bf16_k32(qa1, kb1, s);
+    dpv = mfma_bf16_k32(da0, vb0, dpv);
+    dpv = mfma_bf16_k32(da1, vb1, dpv);
     // s[r] = S[query 4g + r][key c]
-    const float ls[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
-    const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+    const float ls[4] = {st.ls.x, st.ls.y, st.ls.z, st.ls.w};
+    const float dl[4] = {st.dl.x, st.dl.y, st.dl.z, st.dl.w};
     float p[4], ds[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = exp2f(s[r] * g.scale_log2 - ls[r] * kLog2e);
+      const float lse2 = ls[r] * kLog2e;
+      p[r] = fast_exp2(s[r] * g.scale_log2 - lse2);
       ds[r] = p[r] * (dpv[r] - dl[r]);
     }
     if (enrich1) {
-      // level-1 pooled token of this block for query c: logit sigma q.k1 + ln B
-      const float zq = group_sum(dot16_bf16(q0, q1, pk1[0], pk1[1]));
-      const float dq1 = group_sum(dot16_bf16(d0, d1, pv1[0], pv1[1]));
-      const float lc = LS[16 * i + c] * kLog2e, dc = DL[16 * i + c];
-      const float pc = exp2f(zq * g.scale_log2 + 4.0f - lc);
-      const float dsc = pc * (dq1 - dc);
+      // the query block also attends this block's level-1 pooled token (logit + ln B); each raw key of
+      // the block receives B^-1 of that token's gradient, folded into the same products
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dpc = {0.f, 0.f, 0.f, 0.f};
+      sc = mfma_bf16_k32(qa0, k1b0, sc);
+      sc = mfma_bf16_k32(qa1, k1b1, sc);
+      dpc = mfma_bf16_k32(da0, v1b0, dpc);
+      dpc = mfma_bf16_k32(da1, v1b1, dpc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // each raw key of the block receives B^-1 of the pooled token's gradient
-        p[r] += __shfl(pc, 4 * gq + r, 64) * (1.0f / (float)kB);
-        ds[r] += __shfl(dsc, 4 * gq + r, 64) * (1.0f / (float)kB);
+        const float pc = fast_exp2(sc[r] * g.scale_log2 + 4.0f - ls[r] * kLog2e);
+        p[r] += pc * (1.0f / (float)kB);
+        ds[r] += pc * (dpc[r] - dl[r]) * (1.0f / (float)kB);
       }
     }
     const bf16x4 pb = pack4(p[0], p[1], p[2], p[3]);
@@ -424,9 +438,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
       dv_acc[t] = mfma_bf16_k16(lds_read_tr16(dr + 16 * t), pb, dv_acc[t]);
       dk_acc[t] = mfma_bf16_k16(lds_read_tr16(qr + 16 * t), db, dk_acc[t]);
     }
+  };
+
+  // The column's CSR positions are fetched 64 at a time into lanes and broadcast with readlane; each
+  // query block's rows are issued one stage ahead (always, clamped, so the waits stay exact).
+  for (int yb = y0; yb < y1; yb += 64) {
+    const int cnt = min(64, y1 - yb);
+    const int pv_lane = pm[yb + min(lane, cnt - 1)] / g.K;  // query block of entry yb + lane
+    QStage A, B;
+    issue(__builtin_amdgcn_readlane(pv_lane, 0), A);
+    for (int t = 0; t < cnt; t += 2) {
+      issue(__builtin_amdgcn_readlane(pv_lane, min(t + 1, cnt - 1)), B);
+      consume(A);
+      issue(__builtin_amdgcn_readlane(pv_lane, min(t + 2, cnt - 1)), A);
+      if (t + 1 < cnt) consume(B);
+    }
   }
+
   // lane holds d = 16t + 4g + r of key c; add the B^-l share of the level >= 2 pooled tokens
-  const size_t orow = base + (size_t)(16 * j + c) * kD + 4 * gq;
+  bf16_t* dkrow = dk + base + (size_t)(16 * j + c) * kD + 4 * gq;
+  bf16_t* dvrow = dv + base + (size_t)(16 * j + c) * kD + 4 * gq;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float kx[4], vx[4];
@@ -444,13 +475,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
       kx[0] += gk4.x * wgt; kx[1] += gk4.y * wgt; kx[2] += gk4.z * wgt; kx[3] += gk4.w * wgt;
       vx[0] += gv4.x * wgt; vx[1] += gv4.y * wgt; vx[2] += gv4.z * wgt; vx[3] += gv4.w * wgt;
     }
-    uint2 uk, uv;
-    uk.x = pack_bf16x2(kx[0], kx[1]);
-    uk.y = pack_bf16x2(kx[2], kx[3]);
-    uv.x = pack_bf16x2(vx[0], vx[1]);
-    uv.y = pack_bf16x2(vx[2], vx[3]);
-    *reinterpret_cast<uint2*>(dk + orow + 16 * t) = uk;
-    *reinterpret_cast<uint2*>(dv + orow + 16 * t) = uv;
+    *reinterpret_cast<uint2*>(dkrow + 16 * t) = make_uint2(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]));
+    *reinterpret_cast<uint2*>(dvrow + 16 * t) = make_uint2(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]));
   }
 }
 

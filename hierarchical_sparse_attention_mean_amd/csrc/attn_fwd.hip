@@ -20,6 +20,7 @@
 // fp32 design: same wavefront-per-block mapping on the VALU (lane = query x 16-dim quarter), for the
 // small fp32 workloads that need 1e-4 agreement.
 #include "common.hpp"
+#include "entries.hpp"
 #include "launch.hpp"
 
 namespace llsa {
@@ -27,31 +28,12 @@ namespace llsa {
 namespace {
 
 constexpr int kLd = kD + 8;  // LDS row stride (bf16 elements): 144 bytes, 16-byte aligned rows
-
-// Enrichment entry e (0 <= e < K*Le) -> (level, slot): levels 2..Le first, then level 1.
-__device__ __forceinline__ void coarse_entry(const Geom& g, int e, int* level, int* slot) {
-  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
-  if (e < nhigh) {
-    *level = 2 + e / g.K;
-    *slot = e % g.K;
-  } else {
-    *level = 1;
-    *slot = e - nhigh;
-  }
-}
-
-// Pyramid row (within the slice) of enrichment entry e for fine block i.
-__device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e, int* level) {
-  int l, s;
-  coarse_entry(g, e, &l, &s);
-  *level = l;
-  const int unit = i >> (4 * (l - 1));  // i / B^(l-1), B = 16
-  return g.off[l] + I[(size_t)(g.off[l] + unit) * g.K + s];
-}
+constexpr int kMaxCoarse = 256;  // K * L_e enrichment entries per fine block (K <= 32, L_e <= 8)
 
 struct Softmax {
-  float m = -INFINITY;  // running max (log2 domain), identical in the 4 lanes of a query
-  float l = 0.f;        // this lane's partial running sum
+  float m = -INFINITY;  // reference max (log2 domain), identical in the 4 lanes of a query
+  float l = 0.f;        // this lane's partial running sum of 2^(x - m)
+  bool first = true;    // wave-uniform: no logits folded in yet
   f32x4 acc[4];         // O^T[d = 16t + 4g + r][query c]
 
   __device__ void init() {
@@ -59,23 +41,42 @@ struct Softmax {
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // x: 8 logits (log2 domain) of this lane's query for keys {4g+r} of the two 16-key tiles; vt: LDS tile
-  // of 32 value rows (row = 16*tile + key).
-  __device__ void step(const float x[8], const bf16_t* vt, int c, int gq) {
+  // Folds a new block of N logits of this lane's query into the running state and returns their
+  // probabilities (relative to the running reference max) in p.  The reference max only moves when some
+  // query of the wave has grown by more than 2^8 (log2 domain), so the accumulator rescale -- a round trip
+  // of the MFMA accumulators through the VALU -- is rare; unnormalised probabilities stay below 2^8.
+  template <int N>
+  __device__ void update(const float* x, float* p) {
     float mx = x[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    for (int e = 1; e < N; ++e) mx = fmaxf(mx, x[e]);
     mx = group_max(mx);
-    const float m_new = fmaxf(m, mx);
-    const float alpha = exp2f(m - m_new);
-    float p[8], ps = 0.f;
+    if (first) {
+      m = mx;
+      first = false;
+    } else if (__ballot(mx > m + 8.0f)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(x[e] - m_new);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] *= alpha;
+      m = m_new;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      p[e] = fast_exp2(x[e] - m);
       ps += p[e];
     }
-    l = l * alpha + ps;
-    m = m_new;
+    l += ps;
+  }
+
+  // 32 keys: x[r] = key 4g+r of tile 0, x[4+r] = key 4g+r of tile 1; V rows 0..31 in the LDS tile.
+  __device__ void step32(const float x[8], const bf16_t* vt, int c, int gq) {
+    float p[8];
+    update<8>(x, p);
     uint4 pu;
     pu.x = pack_bf16x2(p[0], p[1]);
     pu.y = pack_bf16x2(p[2], p[3]);
@@ -86,129 +87,128 @@ struct Softmax {
     const bf16_t* r1 = r0 + 16 * kLd;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] *= alpha;
       const bf16x8 va = cat4(lds_read_tr16(r0 + 16 * t), lds_read_tr16(r1 + 16 * t));
       acc[t] = mfma_bf16_k32(va, pb, acc[t]);
     }
   }
+
+  // 16 keys: x[r] = key 4g+r; V rows 0..15 in the LDS tile (16x16x16 product over the keys).
+  __device__ void step16(const float x[4], const bf16_t* vt, int c, int gq) {
+    float p[4];
+    update<4>(x, p);
+    const uint2 pu = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    bf16x4 pb;
+    __builtin_memcpy(&pb, &pu, 8);
+    const bf16_t* r0 = vt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_k16(lds_read_tr16(r0 + 16 * t), pb, acc[t]);
+  }
 };
 
 // grid.x = ceil(bh * n_1 / 4); 256 threads; wave w handles fine block 4 * (remapped block id) + w.
-__global__ __launch_bounds__(256) void attn_fwd_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const float* __restrict__ pk,
                                                      const float* __restrict__ pv, const int32_t* __restrict__ idx,
                                                      bf16_t* __restrict__ o, float* __restrict__ lse, Geom g) {
   __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  __shared__ int erows[4][kMaxCoarse];
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = g.bh * g.rows[1];
   const int gb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
   if (gb >= nb) return;  // no workgroup barrier is used below
   const int slice = gb / g.rows[1], i = gb - slice * g.rows[1];
   const size_t base = (size_t)slice * g.n * kD;
-  const bf16_t* Qs = q + base;
-  const bf16_t* Ks = k + base;
-  const bf16_t* Vs = v + base;
   const float* PK = pk + (size_t)slice * g.R * kD;
   const float* PV = pv + (size_t)slice * g.R * kD;
   const int32_t* I = idx + (size_t)slice * g.R * g.K;
+  const int32_t* I1 = I + (size_t)(g.off[1] + i) * g.K;
   bf16_t* vt = vs[w];
+  int* erow = erows[w];
+  const Plan plan = make_plan(g);
 
-  // B operand of S^T: Q[16i + c][16g .. 16g+15]
-  const uint4* qp = reinterpret_cast<const uint4*>(Qs + (size_t)(16 * i + c) * kD + 16 * gq);
-  const bf16x8 qa0 = as_bf16x8(qp[0]), qa1 = as_bf16x8(qp[1]);
+  // prologue: enrichment rows (to LDS), Q, and the first stage in flight
+  stage_entry_rows(g, I, i, plan.ncoarse, lane, erow);
+  // query-side B operands in both orders (natural for raw keys, coarse for pyramid rows)
+  bf16x8 qa0, qa1, qc0, qc1;
+  {
+    uint4 u0, u1;
+    load_natural(q + base, 16u * i + c, lane, u0, u1);
+    qa0 = as_bf16x8(u0);
+    qa1 = as_bf16x8(u1);
+    load_coarse_bf16(q + base, 16u * i + c, lane, qc0, qc1);
+  }
+  const bf16_t* Kraw = k + base;
+  const bf16_t* Vraw = v + base;
 
   Softmax sm;
   sm.init();
-  const int32_t* I1 = I + (size_t)(g.off[1] + i) * g.K;
-  const int kr = lane >> 1, half = lane & 1;  // LDS fill: row kr (0..31), dims 32*half .. +31
 
-  for (int kk = 0; kk < g.K; kk += 2) {
-    const int b0 = I1[kk];
-    const bool has1 = kk + 1 < g.K;
-    const int b1 = has1 ? I1[kk + 1] : b0;
-    const uint4* k0 = reinterpret_cast<const uint4*>(Ks + (size_t)(16 * b0 + c) * kD + 16 * gq);
-    const uint4* k1 = reinterpret_cast<const uint4*>(Ks + (size_t)(16 * b1 + c) * kD + 16 * gq);
-    const bf16x8 a00 = as_bf16x8(k0[0]), a01 = as_bf16x8(k0[1]);
-    const bf16x8 a10 = as_bf16x8(k1[0]), a11 = as_bf16x8(k1[1]);
+  auto consume_fine = [&](int s, const Stage& st) {
+    const bool has1 = 2 * s + 1 < g.K;
     {
-      const int blk = kr < 16 ? b0 : b1;
-      const uint4* vp = reinterpret_cast<const uint4*>(Vs + (size_t)(16 * blk + (kr & 15)) * kD + 32 * half);
-      const uint4 x0 = vp[0], x1 = vp[1], x2 = vp[2], x3 = vp[3];
-      uint4* dst = reinterpret_cast<uint4*>(vt + kr * kLd + 32 * half);
-      dst[0] = x0; dst[1] = x1; dst[2] = x2; dst[3] = x3;
+      // V rows 8m + lane/8 of the 32 keys, 16 bytes at column 8*(lane%8)
+      bf16_t* dst = vt + (lane >> 3) * kLd + 8 * (lane & 7);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) *reinterpret_cast<uint4*>(dst + 8 * m * kLd) = st.r[4 + m];
     }
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma_bf16_k32(a00, qa0, s0);
-    s0 = mfma_bf16_k32(a01, qa1, s0);
-    s1 = mfma_bf16_k32(a10, qa0, s1);
-    s1 = mfma_bf16_k32(a11, qa1, s1);
+    s0 = mfma_bf16_k32(as_bf16x8(st.r[0]), qa0, s0);
+    s0 = mfma_bf16_k32(as_bf16x8(st.r[1]), qa1, s0);
+    s1 = mfma_bf16_k32(as_bf16x8(st.r[2]), qa0, s1);
+    s1 = mfma_bf16_k32(as_bf16x8(st.r[3]), qa1, s1);
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       x[r] = s0[r] * g.scale_log2;
       x[4 + r] = has1 ? s1[r] * g.scale_log2 : -INFINITY;
     }
-    sm.step(x, vt, c, gq);
-  }
-
-  // Enrichment tokens, 32 per step.
-  const int ncoarse = g.K * g.Le;
-  for (int e0 = 0; e0 < ncoarse; e0 += 32) {
-    bf16x8 a[2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int e = e0 + 16 * t2 + c;
-      int lvl;
-      const int row = e < ncoarse ? coarse_row(g, I, i, e, &lvl) : g.off[1];
-      const float4* src = reinterpret_cast<const float4*>(PK + (size_t)row * kD + 16 * gq);
-      a[t2][0] = f32x8_to_bf16x8(src[0], src[1]);
-      a[t2][1] = f32x8_to_bf16x8(src[2], src[3]);
-    }
+    sm.step32(x, vt, c, gq);
+  };
+  auto consume_coarse = [&](int e0, const Stage& st) {
     {
-      const int e = e0 + kr;
-      uint4* dst = reinterpret_cast<uint4*>(vt + kr * kLd + 32 * half);
-      if (e < ncoarse) {
-        int lvl;
-        const int row = coarse_row(g, I, i, e, &lvl);
-        const float4* src = reinterpret_cast<const float4*>(PV + (size_t)row * kD + 32 * half);
-        float4 f[8];
+      // V rows (fp32) -> bf16 LDS tile: instruction m brought entry 4m + lane/16, dims 4*(lane%16)..+3
 #pragma unroll
-        for (int m = 0; m < 8; ++m) f[m] = src[m];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          uint4 u;
-          u.x = pack_bf16x2(f[2 * m].x, f[2 * m].y);
-          u.y = pack_bf16x2(f[2 * m].z, f[2 * m].w);
-          u.z = pack_bf16x2(f[2 * m + 1].x, f[2 * m + 1].y);
-          u.w = pack_bf16x2(f[2 * m + 1].z, f[2 * m + 1].w);
-          dst[m] = u;
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dst[m] = make_uint4(0, 0, 0, 0);
+      for (int m = 0; m < 4; ++m) {
+        const int row = 4 * m + (lane >> 4);
+        float4 f;
+        __builtin_memcpy(&f, &st.r[4 + m], 16);
+        const uint2 u = e0 + row < plan.ncoarse ? make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w))
+                                                : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(vt + row * kLd + 4 * (lane & 15)) = u;
       }
     }
-    f32x4 s[2];
+    bf16x8 a0, a1;
+    coarse_ops(&st.r[0], a0, a1);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+    s0 = mfma_bf16_k32(a0, qc0, s0);
+    s0 = mfma_bf16_k32(a1, qc1, s0);
+    float x[4];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      s[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[t2] = mfma_bf16_k32(a[t2][0], qa0, s[t2]);
-      s[t2] = mfma_bf16_k32(a[t2][1], qa1, s[t2]);
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 4 * gq + r;
+      // level-l weight B^l = 16^l -> + 4l in the log2 domain
+      x[r] = e < plan.ncoarse ? s0[r] * g.scale_log2 + 4.0f * (float)coarse_level(g, e) : -INFINITY;
     }
-    float x[8];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = e0 + 16 * t2 + 4 * gq + r;
-        int lvl, slot;
-        coarse_entry(g, e, &lvl, &slot);
-        // level-l weight B^l = 16^l -> + 4l in the log2 domain
-        x[4 * t2 + r] = e < ncoarse ? s[t2][r] * g.scale_log2 + 4.0f * (float)lvl : -INFINITY;
-      }
-    }
-    sm.step(x, vt, c, gq);
+    sm.step16(x, vt, c, gq);
+  };
+
+  // Stage s+1 is always issued (clamped to the last stage) before stage s is consumed, so that both
+  // branches of every iteration leave the same loads in flight and the waits stay exact.
+  auto consume = [&](int s, const Stage& st) {
+    if (s < plan.nfine)
+      consume_fine(s, st);
+    else
+      consume_coarse(16 * (s - plan.nfine), st);
+  };
+  const int last = plan.nstages - 1;
+  Stage A, B;
+  issue_stage<true>(plan, 0, I1, g.K, Kraw, Vraw, PK, PV, erow, lane, A);
+  for (int s = 0; s < plan.nstages; s += 2) {
+    issue_stage<true>(plan, min(s + 1, last), I1, g.K, Kraw, Vraw, PK, PV, erow, lane, B);
+    consume(s, A);
+    issue_stage<true>(plan, min(s + 2, last), I1, g.K, Kraw, Vraw, PK, PV, erow, lane, A);
+    if (s + 1 < plan.nstages) consume(s + 1, B);
   }
 
   const float lt = group_sum(sm.l);
@@ -286,9 +286,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
   }
   const int ncoarse = g.K * g.Le;
   for (int e = 0; e < ncoarse; ++e) {
-    int lvl;
-    const int row = coarse_row(g, I, i, e, &lvl);
-    visit(PK + (size_t)row * kD, PV + (size_t)row * kD, 4.0f * (float)lvl);
+    const int row = coarse_row(g, I, i, e);
+    visit(PK + (size_t)row * kD, PV + (size_t)row * kD, 4.0f * (float)coarse_level(g, e));
   }
   const float inv = 1.0f / lrun;
   float4* op = reinterpret_cast<float4*>(o + base + (size_t)(16 * i + c) * kD + 16 * gq);
