@@ -5,18 +5,21 @@
 // in idx row i and (b) for l = 1..L_e, the K level-l pooled tokens kept by its level-l ancestor unit
 // i / B^(l-1), whose logits carry + l*ln B (weight B^l).  Only sparse indices are read.
 //
-// bf16 design (one wavefront = one fine query block of 16 queries):
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K rows as the A operand and Q rows as the B operand,
-//     both loaded straight from HBM/L2 into registers (each lane reads a 32-byte run of one row).  Its
-//     result leaves every lane holding 4 keys x 1 query, which is exactly the B-operand layout of
+// bf16 design (one wavefront = one fine query block of 16 queries at a time, persistent):
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K rows as the A operand and Q rows as the B operand.
+//     Its result leaves every lane holding 4 keys x 1 query, which is exactly the B-operand layout of
 //     O^T = V^T P^T, so probabilities never leave registers.
-//   * V^T comes from a wave-private LDS tile read with ds_read_b64_tr_b16 (transposed 4x16 reads).
-//   * Keys go two fine blocks (32 keys) per step; enrichment tokens (fp32 pyramid rows, rounded to
-//     bf16 for the products) go 32 per step with a per-entry logit bias and a validity mask.
+//   * Gathered K and V rows are loaded with coalesced instructions (each quarter-wave reads whole 128-byte
+//     lines) and put into operand order through wave-private LDS tiles: K read back as the MFMA A operand,
+//     V^T read with ds_read_b64_tr_b16 (transposed 4x16 reads).  Loading the operands directly in MFMA
+//     order would make each quarter-wave touch 16 rows, and the vector L1 is bound by such accesses.
+//   * Keys go two fine blocks (32 keys) per stage; enrichment tokens (fp32 pyramid rows, rounded to bf16
+//     for the products) go 16 per stage with a per-entry logit bias and a validity mask.
 //   * Online softmax in the log2 domain with fp32 running max / sum; O rounded to bf16 at the end,
 //     natural-log LSE stored for the backward pass.
-//   * Four waves per workgroup take four consecutive fine blocks (siblings share candidate key blocks);
-//     workgroup ids are remapped so that neighbouring workgroups run on the same XCD and share its L2.
+//   * Persistent waves: each XCD sweeps a contiguous range of fine blocks with all its resident waves, and
+//     each wave pipelines its blocks' stages back to back (the next block's first stage is in flight while
+//     the current block finishes; its Q rows and indices are copied to LDS a whole block ahead).
 // fp32 design: same wavefront-per-block mapping on the VALU (lane = query x 16-dim quarter), for the
 // small fp32 workloads that need 1e-4 agreement.
 #include "common.hpp"
@@ -28,7 +31,7 @@ namespace llsa {
 namespace {
 
 constexpr int kLd = kD + 8;  // LDS row stride (bf16 elements): 144 bytes, 16-byte aligned rows
-constexpr int kMaxCoarse = 256;  // K * L_e enrichment entries per fine block (K <= 32, L_e <= 8)
+constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a limit of the GPU path)
 
 struct Softmax {
   float m = -INFINITY;  // reference max (log2 domain), identical in the 4 lanes of a query
@@ -105,123 +108,267 @@ struct Softmax {
   }
 };
 
-// grid.x = ceil(bh * n_1 / 4); 256 threads; wave w handles fine block 4 * (remapped block id) + w.
+// Fine blocks of one wave.  Workgroup b runs on XCD b % 8 (round-robin dispatch); XCD x owns the
+// contiguous range [x*nb/8, (x+1)*nb/8) of fine blocks, and its S = 4 * (grid / 8) resident waves sweep
+// that range together: wave slot r takes blocks lo + r, lo + r + S, ...  At any moment one XCD thus works
+// on a window of S consecutive fine blocks, whose selections overlap, and that window's key blocks stay
+// in the XCD's L2.
+struct WaveBlocks {
+  int first, stride, count;
+};
+__device__ __forceinline__ WaveBlocks wave_blocks(int nb, int w) {
+  const int g8 = gridDim.x / 8;
+  const int x = blockIdx.x % 8, r = 4 * (blockIdx.x / 8) + w;
+  const int lo = (int)(((int64_t)x * nb) / 8), hi = (int)(((int64_t)(x + 1) * nb) / 8);
+  WaveBlocks wb;
+  wb.first = lo + r;
+  wb.stride = 4 * g8;
+  wb.count = r < hi - lo ? (hi - lo - r + wb.stride - 1) / wb.stride : 0;
+  return wb;
+}
+
+// Asynchronous global -> LDS copies that hold no registers: lane l's 16 (4) bytes land at dst + 16 l (4 l).
+// They are written as inline assembly so that the compiler does not see them: it models an LDS DMA as a
+// flat access of unknown order and would then drain all outstanding loads (vmcnt(0)) at every later wait.
+// The hardware counts them on vmcnt in issue order with the other vector loads, so the kernel waits for
+// them itself (wait_dma) at the one point where their data is first read; the compiler's own waits, which
+// do not count them, only get stricter by their presence.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_dma16(const void* src, const void* dst) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, const void* dst) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
+
+// Persistent kernel: grid = 8 * (workgroups resident per XCD), 256 threads; each wave runs the fine blocks
+// of wave_blocks() back to back.  Its stage list is the concatenation of the blocks' stages, and the loads
+// of stage t+1 (possibly the next block's first stage) are in flight while stage t is consumed.  The next
+// block's Q rows, selection row and enrichment entries are copied into a second set of LDS buffers a whole
+// block ahead, with DMA loads that hold no registers.  So the latency chain index -> gather -> product of
+// one block hides behind the work of the previous one.
 __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const float* __restrict__ pk,
                                                      const float* __restrict__ pv, const int32_t* __restrict__ idx,
                                                      bf16_t* __restrict__ o, float* __restrict__ lse, Geom g) {
-  __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];
-  __shared__ int erows[4][kMaxCoarse];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];      // V tile (read transposed)
+  __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];      // K tile (read as MFMA A operand)
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];       // Q rows of the next block
+  __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row, two slots
+  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nb = g.bh * g.rows[1];
-  const int gb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-  if (gb >= nb) return;  // no workgroup barrier is used below
-  const int slice = gb / g.rows[1], i = gb - slice * g.rows[1];
-  const size_t base = (size_t)slice * g.n * kD;
-  const float* PK = pk + (size_t)slice * g.R * kD;
-  const float* PV = pv + (size_t)slice * g.R * kD;
-  const int32_t* I = idx + (size_t)slice * g.R * g.K;
-  const int32_t* I1 = I + (size_t)(g.off[1] + i) * g.K;
+  const WaveBlocks wb = wave_blocks(g.bh * g.rows[1], w);
+  if (wb.count == 0) return;  // no workgroup barrier is used below
   bf16_t* vt = vs[w];
-  int* erow = erows[w];
+  bf16_t* kt = ks[w];
   const Plan plan = make_plan(g);
+  const int nst = plan.nstages;
+  const size_t slice_elems = (size_t)g.n * kD, slice_rows = (size_t)g.R * kD;
+  const float sl2 = g.scale_log2;
 
-  // prologue: enrichment rows (to LDS), Q, and the first stage in flight
-  stage_entry_rows(g, I, i, plan.ncoarse, lane, erow);
-  // query-side B operands in both orders (natural for raw keys, coarse for pyramid rows)
-  bf16x8 qa0, qa1, qc0, qc1;
-  {
-    uint4 u0, u1;
-    load_natural(q + base, 16u * i + c, lane, u0, u1);
-    qa0 = as_bf16x8(u0);
-    qa1 = as_bf16x8(u1);
-    load_coarse_bf16(q + base, 16u * i + c, lane, qc0, qc1);
-  }
-  const bf16_t* Kraw = k + base;
-  const bf16_t* Vraw = v + base;
+  // copy the inputs of the wave's j-th block (clamped to the last) into slot p (Q: the single Q slot)
+  auto prefetch = [&](int j, int p) {
+    const int gb = wb.first + wb.stride * min(j, wb.count - 1);
+    const int slice = gb / g.rows[1], i = gb - slice * g.rows[1];
+    const bf16_t* qrows = q + slice * slice_elems + (size_t)16 * i * kD;  // 2 KB, contiguous
+    lds_dma16(qrows + 8 * lane, &qs[w][0]);
+    lds_dma16(qrows + 512 + 8 * lane, &qs[w][512]);
+    const int32_t* I = idx + (size_t)slice * g.R * g.K;
+    if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + i) * g.K + lane, &is1[w][p][0]);
+#pragma unroll
+    for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
+      if (64 * jj < plan.ncoarse) {
+        const int e = min(lane + 64 * jj, plan.ncoarse - 1);
+        lds_dma4(I + (coarse_sel_pos(g, i, e)), &es[w][p][64 * jj]);
+      }
+    }
+  };
+  auto block_slice = [&](int j) { return (wb.first + wb.stride * j) / g.rows[1]; };
+
+  // Stage s of the block in slot p (slice `slice`).  Every load instruction is coalesced: a quarter-wave
+  // (16 lanes) reads whole 128-byte lines (two bf16 rows, or half an fp32 row), and the rows are put into
+  // MFMA operand order through the LDS tiles.  The branch only forms two uniform base pointers and eight
+  // per-lane byte offsets; the eight loads then follow on one straight path, so that every stage leaves
+  // the same loads in flight in the same registers and the compiler's waits stay exact.
+  //   fine:   instruction m reads key rows 8m .. 8m+7 of the 32 keys (rows 0..15 of block b0, 16..31 of
+  //           block b1), lane l row 8m + l/8, bytes 16 (l%8) -- K into r[m], V into r[4+m];
+  //   coarse: instruction m reads the fp32 rows of enrichment entries e0 + 4m + l/16, bytes 16 (l%16).
+  auto issue = [&](int p, int slice, int s, Stage& st) {
+    const char* kb;
+    const char* vb;
+    uint32_t off[4];
+    if (s < plan.nfine) {
+      const int b0 = __builtin_amdgcn_readfirstlane(is1[w][p][2 * s]);
+      const int b1 = __builtin_amdgcn_readfirstlane(is1[w][p][min(2 * s + 1, g.K - 1)]);
+      kb = reinterpret_cast<const char*>(k + slice * slice_elems);
+      vb = reinterpret_cast<const char*>(v + slice * slice_elems);
+      const uint32_t sub = (uint32_t)lane >> 3, col = 16u * (lane & 7);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) off[m] = (16u * (m < 2 ? b0 : b1) + 8u * (m & 1) + sub) * (2 * kD) + col;
+    } else {
+      const int e0 = 16 * (s - plan.nfine) + (lane >> 4);
+      kb = reinterpret_cast<const char*>(pk + slice * slice_rows);
+      vb = reinterpret_cast<const char*>(pv + slice * slice_rows);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = min(e0 + 4 * m, plan.ncoarse - 1);
+        off[m] = (uint32_t)(es[w][p][e] + coarse_off(g, e)) * (4 * kD) + 16u * (lane & 15);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.r[m] = ld16(kb + off[m]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.r[4 + m] = ld16(vb + off[m]);
+  };
+
+  int par = 0;                       // slot of the block being consumed
+  int cj = 0, cs = 0;                // block / stage being consumed
+  int ij = 0, is = 0;                // block / stage last issued
+  int cslice = block_slice(0), nslice = block_slice(min(1, wb.count - 1));
+  uint4 q0, q1;
+  // Q operands of the block whose rows sit in the Q slot; the slot is refilled right after, so the reads
+  // must have completed before the next DMA is issued
+  auto read_q = [&]() {
+    const bf16_t* qr = &qs[w][c * kD + 8 * gq];
+    q0 = *reinterpret_cast<const uint4*>(qr);
+    q1 = *reinterpret_cast<const uint4*>(qr + 32);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  prefetch(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_q();
+  prefetch(1, 1);
 
   Softmax sm;
   sm.init();
 
+  auto issue_next = [&](Stage& st) {
+    if (++is == nst) {
+      is = 0;
+      ++ij;
+    }
+    if (ij >= wb.count)
+      issue(par, cslice, nst - 1, st);  // past the end: an in-bounds reload that is never consumed
+    else if (is == 0) {
+      // first stage of the next block (the current one is in its last stage): its selection row was copied at
+      // the start of the current block, and every stage issued since (nst - 1 of them) is newer
+      if (nst >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      issue(par ^ 1, nslice, 0, st);
+    }
+    else
+      issue(par, cslice, is, st);
+  };
+
+  auto finish_block = [&]() {
+    const int gb = wb.first + wb.stride * cj;
+    const int i = gb - cslice * g.rows[1];
+    const float lt = group_sum(sm.l);
+    const float inv = 1.0f / lt;
+    bf16_t* orow = o + cslice * slice_elems + (size_t)(16 * i + c) * kD + 4 * gq;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint2 u;
+      u.x = pack_bf16x2(sm.acc[t][0] * inv, sm.acc[t][1] * inv);
+      u.y = pack_bf16x2(sm.acc[t][2] * inv, sm.acc[t][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * t) = u;
+    }
+    if (gq == 0) lse[(size_t)cslice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
+  };
+
   auto consume_fine = [&](int s, const Stage& st) {
     const bool has1 = 2 * s + 1 < g.K;
     {
-      // V rows 8m + lane/8 of the 32 keys, 16 bytes at column 8*(lane%8)
-      bf16_t* dst = vt + (lane >> 3) * kLd + 8 * (lane & 7);
+      // key rows 8m + lane/8 of the 32 keys, 16 bytes at column 8*(lane%8), into the K and V tiles
+      const int o = (lane >> 3) * kLd + 8 * (lane & 7);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) *reinterpret_cast<uint4*>(dst + 8 * m * kLd) = st.r[4 + m];
+      for (int m = 0; m < 4; ++m) {
+        *reinterpret_cast<uint4*>(kt + o + 8 * m * kLd) = st.r[m];
+        *reinterpret_cast<uint4*>(vt + o + 8 * m * kLd) = st.r[4 + m];
+      }
     }
+    // A operands: key row c (block b0) and 16 + c (block b1), dims 8g..8g+7 and 32+8g..32+8g+7
+    const bf16_t* kr = kt + c * kLd + 8 * gq;
+    const bf16x8 k00 = *reinterpret_cast<const bf16x8*>(kr), k01 = *reinterpret_cast<const bf16x8*>(kr + 32);
+    const bf16x8 k10 = *reinterpret_cast<const bf16x8*>(kr + 16 * kLd);
+    const bf16x8 k11 = *reinterpret_cast<const bf16x8*>(kr + 16 * kLd + 32);
+    const bf16x8 qa0 = as_bf16x8(q0), qa1 = as_bf16x8(q1);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma_bf16_k32(as_bf16x8(st.r[0]), qa0, s0);
-    s0 = mfma_bf16_k32(as_bf16x8(st.r[1]), qa1, s0);
-    s1 = mfma_bf16_k32(as_bf16x8(st.r[2]), qa0, s1);
-    s1 = mfma_bf16_k32(as_bf16x8(st.r[3]), qa1, s1);
+    s0 = mfma_bf16_k32(k00, qa0, s0);
+    s0 = mfma_bf16_k32(k01, qa1, s0);
+    s1 = mfma_bf16_k32(k10, qa0, s1);
+    s1 = mfma_bf16_k32(k11, qa1, s1);
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = s0[r] * g.scale_log2;
-      x[4 + r] = has1 ? s1[r] * g.scale_log2 : -INFINITY;
+      x[r] = s0[r] * sl2;
+      x[4 + r] = has1 ? s1[r] * sl2 : -INFINITY;
     }
     sm.step32(x, vt, c, gq);
   };
   auto consume_coarse = [&](int e0, const Stage& st) {
     {
-      // V rows (fp32) -> bf16 LDS tile: instruction m brought entry 4m + lane/16, dims 4*(lane%16)..+3
+      // fp32 rows of entries 4m + lane/16, dims 4 (lane%16) .. +3 -> bf16 K and V tile rows; rows past the end
+      // of the list hold a valid duplicate whose probability is exactly 0
+      const int o = (lane >> 4) * kLd + 4 * (lane & 15);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int row = 4 * m + (lane >> 4);
-        float4 f;
-        __builtin_memcpy(&f, &st.r[4 + m], 16);
-        const uint2 u = e0 + row < plan.ncoarse ? make_uint2(pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w))
-                                                : make_uint2(0u, 0u);
-        *reinterpret_cast<uint2*>(vt + row * kLd + 4 * (lane & 15)) = u;
+        float4 fk, fv;
+        __builtin_memcpy(&fk, &st.r[m], 16);
+        __builtin_memcpy(&fv, &st.r[4 + m], 16);
+        *reinterpret_cast<uint2*>(kt + o + 4 * m * kLd) = make_uint2(pack_bf16x2(fk.x, fk.y), pack_bf16x2(fk.z, fk.w));
+        *reinterpret_cast<uint2*>(vt + o + 4 * m * kLd) = make_uint2(pack_bf16x2(fv.x, fv.y), pack_bf16x2(fv.z, fv.w));
       }
     }
-    bf16x8 a0, a1;
-    coarse_ops(&st.r[0], a0, a1);
+    const bf16_t* kr = kt + c * kLd + 8 * gq;
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr), a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma_bf16_k32(a0, qc0, s0);
-    s0 = mfma_bf16_k32(a1, qc1, s0);
+    s0 = mfma_bf16_k32(a0, as_bf16x8(q0), s0);
+    s0 = mfma_bf16_k32(a1, as_bf16x8(q1), s0);
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = e0 + 4 * gq + r;
       // level-l weight B^l = 16^l -> + 4l in the log2 domain
-      x[r] = e < plan.ncoarse ? s0[r] * g.scale_log2 + 4.0f * (float)coarse_level(g, e) : -INFINITY;
+      x[r] = e < plan.ncoarse ? s0[r] * sl2 + 4.0f * (float)coarse_level(g, e) : -INFINITY;
     }
     sm.step16(x, vt, c, gq);
   };
 
-  // Stage s+1 is always issued (clamped to the last stage) before stage s is consumed, so that both
-  // branches of every iteration leave the same loads in flight and the waits stay exact.
-  auto consume = [&](int s, const Stage& st) {
-    if (s < plan.nfine)
-      consume_fine(s, st);
+  auto consume = [&](const Stage& st) {
+    if (cs < plan.nfine)
+      consume_fine(cs, st);
     else
-      consume_coarse(16 * (s - plan.nfine), st);
+      consume_coarse(16 * (cs - plan.nfine), st);
+    if (++cs == nst) {
+      finish_block();
+      cs = 0;
+      if (++cj < wb.count) {
+        par ^= 1;
+        cslice = nslice;
+        nslice = block_slice(min(cj + 1, wb.count - 1));
+        read_q();
+        prefetch(cj + 1, par ^ 1);
+        sm = Softmax();
+        sm.init();
+      }
+    }
   };
-  const int last = plan.nstages - 1;
-  Stage A, B;
-  issue_stage<true>(plan, 0, I1, g.K, Kraw, Vraw, PK, PV, erow, lane, A);
-  for (int s = 0; s < plan.nstages; s += 2) {
-    issue_stage<true>(plan, min(s + 1, last), I1, g.K, Kraw, Vraw, PK, PV, erow, lane, B);
-    consume(s, A);
-    issue_stage<true>(plan, min(s + 2, last), I1, g.K, Kraw, Vraw, PK, PV, erow, lane, A);
-    if (s + 1 < plan.nstages) consume(s + 1, B);
-  }
 
-  const float lt = group_sum(sm.l);
-  const float inv = 1.0f / lt;
-  bf16_t* orow = o + base + (size_t)(16 * i + c) * kD + 4 * gq;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    uint2 u;
-    u.x = pack_bf16x2(sm.acc[t][0] * inv, sm.acc[t][1] * inv);
-    u.y = pack_bf16x2(sm.acc[t][2] * inv, sm.acc[t][3] * inv);
-    *reinterpret_cast<uint2*>(orow + 16 * t) = u;
+  const int T = wb.count * nst;
+  Stage A, B;
+  issue(0, cslice, 0, A);
+  for (int t = 0; t < T; t += 2) {
+    issue_next(B);
+    consume(A);
+    issue_next(A);
+    if (t + 1 < T) consume(B);
   }
-  if (gq == 0) lse[(size_t)slice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
 }
 
 // fp32 path: wave per fine block, lane = (query c, dims 16g .. 16g+15), entries one at a time on the VALU.
@@ -306,7 +453,7 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
   const int grid = (nb + 3) / 4;
   LaunchTimer timer(kAttnFwd, stream);
   if (dtype_bf16)
-    attn_fwd_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pk, pv, idx,
+    attn_fwd_bf16<<<persistent_grid((const void*)attn_fwd_bf16, 256, grid), 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pk, pv, idx,
                                             (bf16_t*)o, lse, g);
   else
     attn_fwd_f32<<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pk, pv, idx,

@@ -52,7 +52,7 @@ int resolve(const llsa_problem* in, Resolved* r) {
   if (!isfinite(scale)) return LLSA_ERR_PARAM;
   // limits of the gfx950 kernels
   if (p.d != llsa::kD || p.block != llsa::kB) return LLSA_ERR_UNSUPPORTED;
-  if (p.topk > 32 || nL > 512) return LLSA_ERR_UNSUPPORTED;
+  if (p.topk > 32 || nL > 512 || (int64_t)p.topk * Le > 128) return LLSA_ERR_UNSUPPORTED;
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh * p.n * p.d >= ((int64_t)1 << 31)) return LLSA_ERR_UNSUPPORTED;
   p.levels = L;
@@ -173,7 +173,7 @@ const char* llsa_status_string(int status) {
     case LLSA_OK: return "ok";
     case LLSA_ERR_NULL: return "a required pointer is NULL";
     case LLSA_ERR_SHAPE: return "invalid shape: need n mod B^L == 0, 1 <= L <= floor(log_B n - 1), 1 <= K <= n/B^L, 0 <= L_e <= L";
-    case LLSA_ERR_UNSUPPORTED: return "outside the limits of the gfx950 kernels (d = 64, B = 16, K <= 32, n/B^L <= 512, K*(L_e-1) <= 32, size < 2^31)";
+    case LLSA_ERR_UNSUPPORTED: return "outside the limits of the gfx950 kernels (d = 64, B = 16, K <= 32, n/B^L <= 512, K*L_e <= 128, K*(L_e-1) <= 32, size < 2^31)";
     case LLSA_ERR_DTYPE: return "unsupported dtype for this entry point";
     case LLSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case LLSA_ERR_WORKSPACE: return "workspace missing or too small";

@@ -31,13 +31,34 @@ __device__ __forceinline__ int coarse_level(const Geom& g, int e) {
   return l;
 }
 
+// First pyramid row of level l (1 <= l <= L) for a per-lane l, computed as sum_{m<l} n / 16^m: indexing the
+// offset array with a per-lane value would read the kernel arguments from memory inside the loop.
+__device__ __forceinline__ int level_off(const Geom& g, int l) {
+  int o = 0;
+#pragma unroll
+  for (int m = 1; m < kMaxLevels; ++m) o += m < l ? (g.n >> (4 * m)) : 0;
+  return o;
+}
+
 // Pyramid row (within the slice) of enrichment entry e for fine block i.
 __device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e) {
   int l, s;
   coarse_entry(g, e, &l, &s);
   const int unit = i >> (4 * (l - 1));  // i / B^(l-1), B = 16
-  return g.off[l] + I[(size_t)(g.off[l] + unit) * g.K + s];
+  const int off = level_off(g, l);
+  return off + I[(size_t)(off + unit) * g.K + s];
 }
+
+// Position within the slice's selection array of the entry behind enrichment entry e of fine block i, and
+// the level offset to add to that entry: split so that a caller can copy the entry early and add the offset
+// when it is used.
+__device__ __forceinline__ int coarse_sel_pos(const Geom& g, int i, int e) {
+  int l, s;
+  coarse_entry(g, e, &l, &s);
+  const int unit = i >> (4 * (l - 1));
+  return (level_off(g, l) + unit) * g.K + s;
+}
+__device__ __forceinline__ int coarse_off(const Geom& g, int e) { return level_off(g, coarse_level(g, e)); }
 
 // One stage of gathered rows: 8 x 16 bytes per lane.
 struct Stage {
@@ -155,6 +176,31 @@ __device__ __forceinline__ void issue_stage(const Plan& p, int s, const int32_t*
   } else {
     issue_coarse<kVTile>(16 * (s - p.nfine), p.ncoarse, PK, PV, erow, lane, st);
   }
+}
+
+// Loads of one enrichment stage in natural order (forward): 16 tokens, lane (c, g) reading token c's pyramid
+// rows `prow` (rows past the end of the list duplicate a valid row and are masked by the consumer):
+//   r[0..3]: K dims 8g..8g+3, 8g+4..8g+7, 32+8g..32+8g+3, 32+8g+4..32+8g+7;   r[4..7]: the same of V.
+// Per instruction this touches one 128-byte line per row, as the raw bf16 loads do.
+__device__ __forceinline__ void issue_coarse_nat(int prow, const float* __restrict__ PK, const float* __restrict__ PV,
+                                                 int lane, Stage& st) {
+  const uint32_t o = (uint32_t)prow * kD + 8u * (uint32_t)(lane >> 4);
+  st.r[0] = ld16(PK + o);
+  st.r[1] = ld16(PK + o + 4);
+  st.r[2] = ld16(PK + o + 32);
+  st.r[3] = ld16(PK + o + 36);
+  st.r[4] = ld16(PV + o);
+  st.r[5] = ld16(PV + o + 4);
+  st.r[6] = ld16(PV + o + 32);
+  st.r[7] = ld16(PV + o + 36);
+}
+
+// Natural-order fp32 operand (dims 8g..8g+7 in r[0..1], 32+8g..32+8g+7 in r[2..3]) -> two bf16x8 operands.
+__device__ __forceinline__ void nat_ops(const uint4* r, bf16x8& a0, bf16x8& a1) {
+  float4 f[4];
+  __builtin_memcpy(f, r, 64);
+  a0 = f32x8_to_bf16x8(f[0], f[1]);
+  a1 = f32x8_to_bf16x8(f[2], f[3]);
 }
 
 // Coarse-order fp32 operand (4 x 16 B, dims 16m+4g..+3) -> two bf16x8 MFMA operands (steps 0 and 1).

@@ -33,6 +33,13 @@ struct CscGeom {
   int pm_off[kMaxLevels + 1];   // pm_off[l]: first perm entry of level l
 };
 
+// Workgroups of `kernel` (at `threads` per workgroup, static LDS only) that the current device holds at
+// once; 0 if the runtime cannot tell.  Cached per device and kernel.
+int resident_workgroups(const void* kernel, int threads);
+// Grid of a persistent kernel that wants `wanted` workgroups of work: at most one resident wave of
+// workgroups, rounded up to a multiple of 8 (one per XCD), at least 8.
+int persistent_grid(const void* kernel, int threads, int64_t wanted);
+
 hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
                           float* pk, float* pv, hipStream_t stream);
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream);

@@ -26,8 +26,8 @@
  * Errors: each call returns LLSA_OK (0) or a negative LLSA_ERR_* code; on a validation error nothing
  * is launched.  No exception crosses the ABI.  Non-finite inputs give unspecified outputs.
  * Pointers must be 16-byte aligned (LLSA_ERR_ALIGN).
- * GPU limits of this version: d = 64, B = 16, 1 <= K <= n_L, K <= 32, n_L <= 512, K*(L_e-1) <= 32 for the
- * backward, batch*heads*n*d < 2^31.
+ * GPU limits of this version: d = 64, B = 16, 1 <= K <= n_L, K <= 32, n_L <= 512, K*L_e <= 128,
+ * K*(L_e-1) <= 32 for the backward, batch*heads*n*d < 2^31.
  */
 #ifndef LLSA_H
 #define LLSA_H
