@@ -270,14 +270,21 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     const int i = gb - cslice * g.rows[1];
     const float lt = group_sum(sm.l);
     const float inv = 1.0f / lt;
-    bf16_t* orow = o + cslice * slice_elems + (size_t)(16 * i + c) * kD + 4 * gq;
+    // O^T[d][query c] -> bf16 rows of the K tile (query c, dims 16t + 4g .. +3), then coalesced 16-byte stores
+    // of whole rows (lane l: query l/8 and 8 + l/8, bytes 16 (l%8))
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint2 u;
       u.x = pack_bf16x2(sm.acc[t][0] * inv, sm.acc[t][1] * inv);
       u.y = pack_bf16x2(sm.acc[t][2] * inv, sm.acc[t][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * t) = u;
+      *reinterpret_cast<uint2*>(kt + c * kLd + 16 * t + 4 * gq) = u;
     }
+    bf16_t* ob = o + cslice * slice_elems + (size_t)16 * i * kD;
+    const int ro = (lane >> 3) * kLd + 8 * (lane & 7), go = (lane >> 3) * kD + 8 * (lane & 7);
+    const uint4 o0 = *reinterpret_cast<const uint4*>(kt + ro);
+    const uint4 o1 = *reinterpret_cast<const uint4*>(kt + ro + 8 * kLd);
+    st16(ob + go, o0);
+    st16(ob + go + 8 * kD, o1);
     if (gq == 0) lse[(size_t)cslice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
   };
 
