@@ -24,14 +24,13 @@
 #include "common.hpp"
 #include "entries.hpp"
 #include "launch.hpp"
+#include "persist.hpp"
 
 namespace llsa {
 
 namespace {
 
 constexpr int kLd = kD + 8;   // bf16 row stride of K / Q / dO tiles in LDS
-constexpr int kSt = 16 + 8;   // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
-constexpr int kMaxHigh = 32;  // enrichment entries of levels >= 2 per query (K * (Le - 1))
 
 // Pyramid row of enrichment entry e for fine block i, and its level.
 __device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e, int* level) {
@@ -60,221 +59,373 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
 
 // ------------------------------------------------------------------------------------------------
 // 1. dQ, Delta and the level >= 2 pooled-token partials.
-// grid.x = bh * ceil(n_1 / 16) (remapped), 256 threads; wave w takes blocks 16u + w + 4jj, jj = 0..3.
+// Persistent: grid = 8 * (workgroups resident per XCD), 256 threads.  A workgroup takes level-2 units
+// (16 fine blocks each) from its XCD's sweep; wave w runs blocks w, w+4, w+8, w+12 of each unit (ragged
+// units run clamped dummy blocks whose results are dropped), and its stage list is the concatenation of
+// those blocks' stages, the next block's first stage in flight while the current one finishes.  A block's
+// Q, dO, O rows, LSE and indices are copied to LDS a whole block ahead (LDS DMA).  Gathered K / V / pyramid
+// rows are loaded coalesced (issue_stage_coalesced) and reordered through swizzled LDS tiles.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dq_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
-                                                   const float* __restrict__ lse, const bf16_t* __restrict__ dout,
-                                                   const float* __restrict__ pk, const float* __restrict__ pv,
-                                                   const int32_t* __restrict__ idx, bf16_t* __restrict__ dq,
-                                                   float* __restrict__ delta, float* __restrict__ part_k,
-                                                   float* __restrict__ part_v, Geom g) {
-  __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t sts[4][32 * kSt];
-  __shared__ __attribute__((aligned(16))) bf16_t pts[4][32 * kSt];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a limit of the GPU path)
+constexpr int kSt = 16 + 8;      // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
+
+// kT: 16-entry tiles of level >= 2 enrichment entries whose partials are held in registers (K*(L_e-1) <= 16 kT).
+template <int kT>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
+                                                      const float* __restrict__ lse, const bf16_t* __restrict__ dout,
+                                                      const float* __restrict__ pk, const float* __restrict__ pv,
+                                                      const int32_t* __restrict__ idx, bf16_t* __restrict__ dq,
+                                                      float* __restrict__ delta, float* __restrict__ part_k,
+                                                      float* __restrict__ part_v, Geom g) {
+  __shared__ __attribute__((aligned(16))) bf16_t kts[4][32 * kD];      // K tiles (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t vts[4][32 * kD];      // V tiles (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t qsl[4][2][16 * kD];   // Q rows, two slots (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t dsl[4][2][16 * kD];   // dO rows, two slots (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t osl[4][16 * kD];      // O rows of the next block (swizzled)
+  __shared__ __attribute__((aligned(16))) float lsl[4][2][16];         // LSE of the block's queries
+  __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row
+  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
   const int gps = (n1 + 15) / 16;
-  const int grp = xcd_remap(blockIdx.x, gridDim.x);
-  const int slice = grp / gps, u2 = grp - slice * gps;
-  const size_t base = (size_t)slice * g.n * kD;
-  const float* PK = pk + (size_t)slice * g.R * kD;
-  const float* PV = pv + (size_t)slice * g.R * kD;
-  const int32_t* I = idx + (size_t)slice * g.R * g.K;
+  const Sweep su = xcd_sweep(g.bh * gps, blockIdx.x / 8, gridDim.x / 8);
+  if (su.count == 0) return;  // uniform over the workgroup
+  const int nblk = 4 * su.count;
+  bf16_t* kt = kts[w];
+  bf16_t* vt = vts[w];
+  const Plan plan = make_plan(g);
+  const int nst = plan.nstages;
   const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
-  const int ncoarse = g.K * g.Le;
-  bf16_t* kt = ks[w];
-  const int kr = lane >> 1, half = lane & 1;
+  const size_t slice_elems = (size_t)g.n * kD, slice_rows = (size_t)g.R * kD;
+  const float sl2 = g.scale_log2;
 
-  f32x4 gk_acc[2][4], gv_acc[2][4];
+  struct Blk {
+    int slice, u2, i;
+    bool valid;
+  };
+  // the wave's j-th block (clamped to the last)
+  auto blk = [&](int j) {
+    const int jc = min(j, nblk - 1);
+    const int U = su.first + su.stride * (jc >> 2);
+    Blk b;
+    b.slice = U / gps;
+    b.u2 = U - b.slice * gps;
+    const int i = 16 * b.u2 + w + 4 * (jc & 3);
+    b.valid = i < n1;
+    b.i = min(i, n1 - 1);
+    return b;
+  };
+  // copy the inputs of the wave's j-th block into slot p (O: the single O slot)
+  auto prefetch = [&](int j, int p) {
+    const Blk b = blk(j);
+    const size_t rb = b.slice * slice_elems + (size_t)16 * b.i * kD + swz_dma_src(lane);
+    lds_dma16(q + rb, &qsl[w][p][0]);
+    lds_dma16(q + rb + 8 * kD, &qsl[w][p][8 * kD]);
+    lds_dma16(dout + rb, &dsl[w][p][0]);
+    lds_dma16(dout + rb + 8 * kD, &dsl[w][p][8 * kD]);
+    lds_dma16(o + rb, &osl[w][0]);
+    lds_dma16(o + rb + 8 * kD, &osl[w][8 * kD]);
+    if (lane < 16) lds_dma4(lse + (size_t)b.slice * g.n + 16 * b.i + lane, &lsl[w][p][0]);
+    const int32_t* I = idx + (size_t)b.slice * g.R * g.K;
+    if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + b.i) * g.K + lane, &is1[w][p][0]);
 #pragma unroll
-  for (int T = 0; T < 2; ++T)
+    for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
+      if (64 * jj < plan.ncoarse) {
+        const int e = min(lane + 64 * jj, plan.ncoarse - 1);
+        lds_dma4(I + coarse_sel_pos(g, b.i, e), &es[w][p][64 * jj]);
+      }
+    }
+  };
+  auto issue = [&](int p, int slice, int s, Stage& st) {
+    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], k + slice * slice_elems, v + slice * slice_elems,
+                          pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
+  };
+
+  int par = 0;   // slot of the block being consumed
+  int cj = 0, cs = 0;
+  int ij = 0, is = 0;
+  Blk cur = blk(0), nxt = blk(1);
+  float dlt = 0.f, lse2 = 0.f;
+  // B operands (natural order) of the current block's Q and dO rows, re-read from their slots at each stage
+  // (holding them in registers would push the kernel past its register budget)
+  auto qd_ops = [&](bf16x8& qa0, bf16x8& qa1, bf16x8& da0, bf16x8& da1) {
+    const int c7 = c & 7;
+    const bf16_t* qr = &qsl[w][par][c * kD];
+    const bf16_t* dr = &dsl[w][par][c * kD];
+    qa0 = *reinterpret_cast<const bf16x8*>(qr + ((gq ^ c7) << 3));
+    qa1 = *reinterpret_cast<const bf16x8*>(qr + (((4 + gq) ^ c7) << 3));
+    da0 = *reinterpret_cast<const bf16x8*>(dr + ((gq ^ c7) << 3));
+    da1 = *reinterpret_cast<const bf16x8*>(dr + (((4 + gq) ^ c7) << 3));
+  };
+  f32x4 dq_acc[4], gk_acc[kT][4], gv_acc[kT][4];
+#pragma unroll
+  for (int T = 0; T < kT; ++T)
 #pragma unroll
     for (int t = 0; t < 4; ++t) gk_acc[T][t] = gv_acc[T][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int jj = 0; jj < 4; ++jj) {
-    const int i = 16 * u2 + w + 4 * jj;
-    if (i >= n1) continue;
-    const int row = 16 * i + c;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + base + (size_t)row * kD + 16 * gq);
-    const uint4* dp = reinterpret_cast<const uint4*>(dout + base + (size_t)row * kD + 16 * gq);
-    const uint4* op = reinterpret_cast<const uint4*>(o + base + (size_t)row * kD + 16 * gq);
-    const uint4 q0 = qp[0], q1 = qp[1], d0 = dp[0], d1 = dp[1];
-    const bf16x8 qa0 = as_bf16x8(q0), qa1 = as_bf16x8(q1), da0 = as_bf16x8(d0), da1 = as_bf16x8(d1);
-    const float dlt = group_sum(dot16_bf16(d0, d1, op[0], op[1]));
-    const float lse2 = lse[(size_t)slice * g.n + row] * kLog2e;
-    if (gq == 0) delta[(size_t)slice * g.n + row] = dlt;
-    if (nhigh > 0) {
-      uint4* qd = reinterpret_cast<uint4*>(qs[w] + c * kLd + 16 * gq);
-      uint4* dd = reinterpret_cast<uint4*>(dos[w] + c * kLd + 16 * gq);
-      qd[0] = q0; qd[1] = q1; dd[0] = d0; dd[1] = d1;
-    }
-    f32x4 dq_acc[4];
+  // start of block cj (inputs in slot par): B operands, Delta, LSE; then the next block's copies
+  auto begin_block = [&]() {
+    const int c7 = c & 7;
+    const bf16_t* qr = &qsl[w][par][c * kD];
+    const bf16_t* dr = &dsl[w][par][c * kD];
+    const bf16_t* orr = &osl[w][c * kD];
+    (void)qr;
+    const uint4 d0 = *reinterpret_cast<const uint4*>(dr + ((gq ^ c7) << 3));
+    const uint4 d1 = *reinterpret_cast<const uint4*>(dr + (((4 + gq) ^ c7) << 3));
+    const uint4 o0 = *reinterpret_cast<const uint4*>(orr + ((gq ^ c7) << 3));
+    const uint4 o1 = *reinterpret_cast<const uint4*>(orr + (((4 + gq) ^ c7) << 3));
+    lse2 = lsl[w][par][c] * kLog2e;
+    wait_lds();  // the O slot is refilled below
+    dlt = group_sum(dot16_bf16(d0, d1, o0, o1));
+    if (cur.valid && gq == 0) delta[(size_t)cur.slice * g.n + 16 * cur.i + c] = dlt;
+    prefetch(cj + 1, par ^ 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) dq_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
-    // dS^T for 2 key tiles -> dQ^T += K^T dS^T (K^T read transposed from the LDS tile kt)
-    auto accumulate_dq = [&](const float ds[8]) {
-      uint4 u;
-      u.x = pack_bf16x2(ds[0], ds[1]);
-      u.y = pack_bf16x2(ds[2], ds[3]);
-      u.z = pack_bf16x2(ds[4], ds[5]);
-      u.w = pack_bf16x2(ds[6], ds[7]);
-      const bf16x8 db = as_bf16x8(u);
-      const bf16_t* r0 = kt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-      const bf16_t* r1 = r0 + 16 * kLd;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8 ka = cat4(lds_read_tr16(r0 + 16 * t), lds_read_tr16(r1 + 16 * t));
-        dq_acc[t] = mfma_bf16_k32(ka, db, dq_acc[t]);
-      }
-    };
-
-    // fine key blocks, two per step
-    const int32_t* I1 = I + (size_t)(g.off[1] + i) * g.K;
-    for (int kk = 0; kk < g.K; kk += 2) {
-      const int b0 = I1[kk];
-      const bool has1 = kk + 1 < g.K;
-      const int b1 = has1 ? I1[kk + 1] : b0;
-      bf16x8 ka[2][2], va[2][2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const size_t r = base + (size_t)(16 * (t2 ? b1 : b0) + c) * kD + 16 * gq;
-        const uint4* kp = reinterpret_cast<const uint4*>(k + r);
-        const uint4* vp = reinterpret_cast<const uint4*>(v + r);
-        const uint4 k0 = kp[0], k1 = kp[1];
-        ka[t2][0] = as_bf16x8(k0); ka[t2][1] = as_bf16x8(k1);
-        va[t2][0] = as_bf16x8(vp[0]); va[t2][1] = as_bf16x8(vp[1]);
-        uint4* kd = reinterpret_cast<uint4*>(kt + (16 * t2 + c) * kLd + 16 * gq);
-        kd[0] = k0; kd[1] = k1;
-      }
-      float ds[8];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
-        s = mfma_bf16_k32(ka[t2][0], qa0, s);
-        s = mfma_bf16_k32(ka[t2][1], qa1, s);
-        dpv = mfma_bf16_k32(va[t2][0], da0, dpv);
-        dpv = mfma_bf16_k32(va[t2][1], da1, dpv);
-        const bool ok = t2 == 0 || has1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = ok ? fast_exp2(s[r] * g.scale_log2 - lse2) : 0.f;
-          ds[4 * t2 + r] = p * (dpv[r] - dlt);
-        }
-      }
-      accumulate_dq(ds);
+  auto issue_next = [&](Stage& st) {
+    if (++is == nst) {
+      is = 0;
+      ++ij;
     }
-
-    // enrichment tokens, 32 per step (levels >= 2 first, then level 1)
-    for (int e0 = 0; e0 < ncoarse; e0 += 32) {
-      bf16x8 ka[2][2], va[2][2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int e = e0 + 16 * t2 + c;
-        int lvl;
-        const int prow = e < ncoarse ? coarse_row(g, I, i, e, &lvl) : g.off[1];
-        const float4* kp = reinterpret_cast<const float4*>(PK + (size_t)prow * kD + 16 * gq);
-        const float4* vp = reinterpret_cast<const float4*>(PV + (size_t)prow * kD + 16 * gq);
-        ka[t2][0] = f32x8_to_bf16x8(kp[0], kp[1]);
-        ka[t2][1] = f32x8_to_bf16x8(kp[2], kp[3]);
-        va[t2][0] = f32x8_to_bf16x8(vp[0], vp[1]);
-        va[t2][1] = f32x8_to_bf16x8(vp[2], vp[3]);
-        bf16x8* kd = reinterpret_cast<bf16x8*>(kt + (16 * t2 + c) * kLd + 16 * gq);
-        kd[0] = ka[t2][0];
-        kd[1] = ka[t2][1];
-      }
-      float ds[8], pr[8];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
-        s = mfma_bf16_k32(ka[t2][0], qa0, s);
-        s = mfma_bf16_k32(ka[t2][1], qa1, s);
-        dpv = mfma_bf16_k32(va[t2][0], da0, dpv);
-        dpv = mfma_bf16_k32(va[t2][1], da1, dpv);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = e0 + 16 * t2 + 4 * gq + r;
-          int lvl, slot;
-          coarse_entry(g, e, &lvl, &slot);
-          const float p = e < ncoarse ? fast_exp2(s[r] * g.scale_log2 + 4.0f * (float)lvl - lse2) : 0.f;
-          pr[4 * t2 + r] = p;
-          ds[4 * t2 + r] = p * (dpv[r] - dlt);
-        }
-      }
-      accumulate_dq(ds);
-      if (e0 == 0 && nhigh > 0) {
-        // entries of levels >= 2 all sit in this first step: dK^(l)[e] += sum_q dS^T[e][q] q,
-        // dV^(l)[e] += sum_q P^T[e][q] dO over this block's 16 queries (16x16x16 MFMA, k = query)
-        bf16_t* st = sts[w];
-        bf16_t* pt = pts[w];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            st[(16 * t2 + 4 * gq + r) * kSt + c] = f32_to_bf16(ds[4 * t2 + r]);
-            pt[(16 * t2 + 4 * gq + r) * kSt + c] = f32_to_bf16(pr[4 * t2 + r]);
-          }
-        const bf16_t* qr = qs[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-        const bf16_t* dr = dos[w] + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          if (16 * T < nhigh) {
-            const bf16x4 as = *reinterpret_cast<const bf16x4*>(st + (16 * T + c) * kSt + 4 * gq);
-            const bf16x4 ap = *reinterpret_cast<const bf16x4*>(pt + (16 * T + c) * kSt + 4 * gq);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              gk_acc[T][t] = mfma_bf16_k16(as, lds_read_tr16(qr + 16 * t), gk_acc[T][t]);
-              gv_acc[T][t] = mfma_bf16_k16(ap, lds_read_tr16(dr + 16 * t), gv_acc[T][t]);
-            }
-          }
-        }
-      }
+    if (ij >= nblk) {
+      issue(par, cur.slice, nst - 1, st);  // past the end: an in-bounds reload that is never consumed
+    } else if (is == 0) {
+      // first stage of the next block: its indices were copied at the start of the current block, and every
+      // stage issued since (nst - 1 of them) is newer
+      if (nst >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      issue(par ^ 1, nxt.slice, 0, st);
+    } else {
+      issue(par, cur.slice, is, st);
     }
-    // dQ = sigma * dQ^T (lane holds d = 16t + 4g + r of query c)
-    bf16_t* qrow = dq + base + (size_t)row * kD + 4 * gq;
+  };
+
+  // dQ^T += K^T dS^T over 32 keys (k32; key order of the S tiles) or 16 entries (k16), K^T read transposed
+  auto dq_32 = [&](const float ds[8]) {
+    uint4 u;
+    u.x = pack_bf16x2(ds[0], ds[1]);
+    u.y = pack_bf16x2(ds[2], ds[3]);
+    u.z = pack_bf16x2(ds[4], ds[5]);
+    u.w = pack_bf16x2(ds[6], ds[7]);
+    const bf16x8 db = as_bf16x8(u);
+    const int r = 4 * gq + (c >> 2);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      uint2 u;
-      u.x = pack_bf16x2(dq_acc[t][0] * g.scale, dq_acc[t][1] * g.scale);
-      u.y = pack_bf16x2(dq_acc[t][2] * g.scale, dq_acc[t][3] * g.scale);
-      *reinterpret_cast<uint2*>(qrow + 16 * t) = u;
+      const int col = 16 * t + 4 * (c & 3);
+      const bf16x8 ka = cat4(lds_read_tr16(kt + swz(r, col)), lds_read_tr16(kt + swz(r + 16, col)));
+      dq_acc[t] = mfma_bf16_k32(ka, db, dq_acc[t]);
     }
-  }
+  };
+  auto dq_16 = [&](const float ds[4]) {
+    const bf16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
+    const int r = 4 * gq + (c >> 2);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dq_acc[t] = mfma_bf16_k16(lds_read_tr16(kt + swz(r, 16 * t + 4 * (c & 3))), db, dq_acc[t]);
+  };
 
-  if (nhigh == 0) return;  // uniform over the workgroup
-  // Fixed-order reduction of the four waves' partials through LDS, then one store per element.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&ks[0][0]);  // [2][kMaxHigh][kD] fp32 = 16 KB
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  auto consume_fine = [&](int s, const Stage& st) {
+    const bool has1 = 2 * s + 1 < g.K;
+    {
+      const int r = lane >> 3, ch = lane & 7;
 #pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 16 * T + 4 * gq + r, d = 16 * t + c;
-            float* rk = red + e * kD + d;
-            float* rv = red + (kMaxHigh + e) * kD + d;
-            if (ww == 0) {
-              *rk = gk_acc[T][t][r];
-              *rv = gv_acc[T][t][r];
-            } else {
-              *rk += gk_acc[T][t][r];
-              *rv += gv_acc[T][t][r];
-            }
-          }
+      for (int m = 0; m < 4; ++m) {
+        const int o2 = (8 * m + r) * kD + ((ch ^ r) << 3);
+        *reinterpret_cast<uint4*>(kt + o2) = st.r[m];
+        *reinterpret_cast<uint4*>(vt + o2) = st.r[4 + m];
+      }
     }
-    __syncthreads();
-  }
-  float* outk = part_k + ((size_t)slice * gps + u2) * nhigh * kD;
-  float* outv = part_v + ((size_t)slice * gps + u2) * nhigh * kD;
-  for (int x = threadIdx.x; x < nhigh * kD; x += 256) {
-    outk[x] = red[x] * g.scale;
-    outv[x] = red[kMaxHigh * kD + x];
+    const int c7 = c & 7;
+    const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
+    bf16x8 qa0, qa1, da0, da1;
+    qd_ops(qa0, qa1, da0, da1);
+    float ds[8];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int ro = 16 * kD * t2;
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + ro + a0), k1 = *reinterpret_cast<const bf16x8*>(kt + ro + a1);
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vt + ro + a0), v1 = *reinterpret_cast<const bf16x8*>(vt + ro + a1);
+      f32x4 sx = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
+      sx = mfma_bf16_k32(k0, qa0, sx);
+      sx = mfma_bf16_k32(k1, qa1, sx);
+      dpv = mfma_bf16_k32(v0, da0, dpv);
+      dpv = mfma_bf16_k32(v1, da1, dpv);
+      const bool ok = t2 == 0 || has1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = ok ? fast_exp2(sx[r] * sl2 - lse2) : 0.f;
+        ds[4 * t2 + r] = p * (dpv[r] - dlt);
+      }
+    }
+    dq_32(ds);
+  };
+
+  auto consume_coarse = [&](int sc, const Stage& st) {
+    const int e0 = 16 * sc;
+    {
+      // fp32 rows of entries 4m + lane/16, dims 4 (lane%16) .. +3 -> bf16 tile rows
+      const int r = lane >> 4, ch = (lane & 15) >> 1, hh = 4 * (lane & 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 4 * m + r;
+        const int o2 = row * kD + (((ch ^ row) & 7) << 3) + hh;
+        float4 fk, fv;
+        __builtin_memcpy(&fk, &st.r[m], 16);
+        __builtin_memcpy(&fv, &st.r[4 + m], 16);
+        *reinterpret_cast<uint2*>(kt + o2) = make_uint2(pack_bf16x2(fk.x, fk.y), pack_bf16x2(fk.z, fk.w));
+        *reinterpret_cast<uint2*>(vt + o2) = make_uint2(pack_bf16x2(fv.x, fv.y), pack_bf16x2(fv.z, fv.w));
+      }
+    }
+    const int c7 = c & 7;
+    const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + a0), k1 = *reinterpret_cast<const bf16x8*>(kt + a1);
+    const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vt + a0), v1 = *reinterpret_cast<const bf16x8*>(vt + a1);
+    bf16x8 qa0, qa1, da0, da1;
+    qd_ops(qa0, qa1, da0, da1);
+    f32x4 sx = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
+    sx = mfma_bf16_k32(k0, qa0, sx);
+    sx = mfma_bf16_k32(k1, qa1, sx);
+    dpv = mfma_bf16_k32(v0, da0, dpv);
+    dpv = mfma_bf16_k32(v1, da1, dpv);
+    float ds[4], pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 4 * gq + r;
+      const float p = e < plan.ncoarse ? fast_exp2(sx[r] * sl2 + 4.0f * (float)coarse_level(g, e) - lse2) : 0.f;
+      pr[r] = p;
+      ds[r] = p * (dpv[r] - dlt);
+    }
+    dq_16(ds);
+    if (e0 < nhigh && cur.valid) {
+      // entries of levels >= 2 (shared by the unit's 256 queries): dK^(l)[e] += sum_q dS^T[e][q] q and
+      // dV^(l)[e] += sum_q P^T[e][q] dO over this block's 16 queries (16x16x16, k = query); dS^T and P^T go
+      // through a small tile in the V tile's space, whose operand reads are complete
+      bf16_t* sttile = vt;
+      bf16_t* pttile = vt + 16 * kSt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sttile[(4 * gq + r) * kSt + c] = f32_to_bf16(ds[r]);
+        pttile[(4 * gq + r) * kSt + c] = f32_to_bf16(pr[r]);
+      }
+      const bf16x4 as = *reinterpret_cast<const bf16x4*>(sttile + c * kSt + 4 * gq);
+      const bf16x4 ap = *reinterpret_cast<const bf16x4*>(pttile + c * kSt + 4 * gq);
+      const bf16_t* qtile = qsl[w][par];
+      const bf16_t* dtile = dsl[w][par];
+      const int r = 4 * gq + (c >> 2);
+#pragma unroll
+      for (int T = 0; T < kT; ++T) {
+        if (sc == T) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int x = swz(r, 16 * t + 4 * (c & 3));
+            gk_acc[T][t] = mfma_bf16_k16(as, lds_read_tr16(qtile + x), gk_acc[T][t]);
+            gv_acc[T][t] = mfma_bf16_k16(ap, lds_read_tr16(dtile + x), gv_acc[T][t]);
+          }
+        }
+      }
+    }
+  };
+
+  // dQ = sigma * dQ^T (lane holds d = 16t + 4g + r of query c) -> bf16 rows through the K tile, then whole-row
+  // coalesced stores
+  auto finish_block = [&]() {
+    if (!cur.valid) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint2 u = make_uint2(pack_bf16x2(dq_acc[t][0] * g.scale, dq_acc[t][1] * g.scale),
+                                 pack_bf16x2(dq_acc[t][2] * g.scale, dq_acc[t][3] * g.scale));
+      *reinterpret_cast<uint2*>(kt + swz(c, 16 * t + 4 * gq)) = u;
+    }
+    const int r = lane >> 3, ch = lane & 7;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(kt + r * kD + ((ch ^ r) << 3));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(kt + (8 + r) * kD + ((ch ^ r) << 3));
+    bf16_t* ob = dq + cur.slice * slice_elems + (size_t)16 * cur.i * kD + r * kD + 8 * ch;
+    st16(ob, x0);
+    st16(ob + 8 * kD, x1);
+  };
+
+  // End of the workgroup's ju-th unit: fixed-order reduction of the four waves' partials through LDS (the
+  // K tiles' space), then one store per element.
+  auto unit_end = [&](int ju) {
+    if (nhigh == 0) return;
+    const int U = su.first + su.stride * ju;
+    const int slice = U / gps, u2 = U - slice * gps;
+    float* red = reinterpret_cast<float*>(&kts[0][0]);  // [2][32][kD] fp32 = 16 KB
+    barrier_lds();
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int T = 0; T < kT; ++T)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 16 * T + 4 * gq + r, d = 16 * t + c;
+              float* rk = red + e * kD + d;
+              float* rv = red + (32 + e) * kD + d;
+              if (ww == 0) {
+                *rk = gk_acc[T][t][r];
+                *rv = gv_acc[T][t][r];
+              } else {
+                *rk += gk_acc[T][t][r];
+                *rv += gv_acc[T][t][r];
+              }
+            }
+      }
+      barrier_lds();
+    }
+    float* outk = part_k + ((size_t)slice * gps + u2) * nhigh * kD;
+    float* outv = part_v + ((size_t)slice * gps + u2) * nhigh * kD;
+    // fully unrolled (no inner loop, whose preheader would make the compiler drain the loads in flight)
+#pragma unroll
+    for (int it = 0; it < 4 * kT; ++it) {
+      const int x = threadIdx.x + 256 * it;
+      if (x < nhigh * kD) {
+        outk[x] = red[x] * g.scale;
+        outv[x] = red[32 * kD + x];
+      }
+    }
+    barrier_lds();
+#pragma unroll
+    for (int T = 0; T < kT; ++T)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) gk_acc[T][t] = gv_acc[T][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto consume = [&](const Stage& st) {
+    if (cs < plan.nfine)
+      consume_fine(cs, st);
+    else
+      consume_coarse(cs - plan.nfine, st);
+    if (++cs == nst) {
+      finish_block();
+      cs = 0;
+      if ((cj & 3) == 3) unit_end(cj >> 2);
+      if (++cj < nblk) {
+        par ^= 1;
+        cur = nxt;
+        nxt = blk(cj + 1);
+        begin_block();
+      }
+    }
+  };
+
+  prefetch(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  begin_block();
+  const int T = nblk * nst;
+  Stage A, B;
+  issue(0, cur.slice, 0, A);
+  for (int t = 0; t < T; t += 2) {
+    issue_next(B);
+    consume(A);
+    issue_next(A);
+    if (t + 1 < T) consume(B);
   }
 }
 
@@ -512,9 +663,11 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   const int groups = g.bh * ((n1 + 15) / 16);
   {
     LaunchTimer timer(kBwdDq, stream);
-    bwd_dq_bf16<<<groups, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o,
-                                          lse, (const bf16_t*)dout, pk, pv, idx, (bf16_t*)dq, ws.delta, ws.part_k,
-                                          ws.part_v, g);
+    const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
+    auto kernel = nhigh <= 16 ? bwd_dq_bf16<1> : bwd_dq_bf16<2>;
+    kernel<<<persistent_grid((const void*)kernel, 256, groups), 256, 0, stream>>>(
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, lse, (const bf16_t*)dout, pk, pv,
+        idx, (bf16_t*)dq, ws.delta, ws.part_k, ws.part_v, g);
   }
   if (g.Le >= 2) {
     int tokens = 0;

@@ -25,6 +25,7 @@
 #include "common.hpp"
 #include "entries.hpp"
 #include "launch.hpp"
+#include "persist.hpp"
 
 namespace llsa {
 
@@ -108,43 +109,8 @@ struct Softmax {
   }
 };
 
-// Fine blocks of one wave.  Workgroup b runs on XCD b % 8 (round-robin dispatch); XCD x owns the
-// contiguous range [x*nb/8, (x+1)*nb/8) of fine blocks, and its S = 4 * (grid / 8) resident waves sweep
-// that range together: wave slot r takes blocks lo + r, lo + r + S, ...  At any moment one XCD thus works
-// on a window of S consecutive fine blocks, whose selections overlap, and that window's key blocks stay
-// in the XCD's L2.
-struct WaveBlocks {
-  int first, stride, count;
-};
-__device__ __forceinline__ WaveBlocks wave_blocks(int nb, int w) {
-  const int g8 = gridDim.x / 8;
-  const int x = blockIdx.x % 8, r = 4 * (blockIdx.x / 8) + w;
-  const int lo = (int)(((int64_t)x * nb) / 8), hi = (int)(((int64_t)(x + 1) * nb) / 8);
-  WaveBlocks wb;
-  wb.first = lo + r;
-  wb.stride = 4 * g8;
-  wb.count = r < hi - lo ? (hi - lo - r + wb.stride - 1) / wb.stride : 0;
-  return wb;
-}
-
-// Asynchronous global -> LDS copies that hold no registers: lane l's 16 (4) bytes land at dst + 16 l (4 l).
-// They are written as inline assembly so that the compiler does not see them: it models an LDS DMA as a
-// flat access of unknown order and would then drain all outstanding loads (vmcnt(0)) at every later wait.
-// The hardware counts them on vmcnt in issue order with the other vector loads, so the kernel waits for
-// them itself (wait_dma) at the one point where their data is first read; the compiler's own waits, which
-// do not count them, only get stricter by their presence.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_dma16(const void* src, const void* dst) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
-}
-__device__ __forceinline__ void lds_dma4(const void* src, const void* dst) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
-}
-
 // Persistent kernel: grid = 8 * (workgroups resident per XCD), 256 threads; each wave runs the fine blocks
-// of wave_blocks() back to back.  Its stage list is the concatenation of the blocks' stages, and the loads
+// of its xcd_sweep() back to back (wave slot 4 * (b / 8) + w of its XCD).  Its stage list is the concatenation of the blocks' stages, and the loads
 // of stage t+1 (possibly the next block's first stage) are in flight while stage t is consumed.  The next
 // block's Q rows, selection row and enrichment entries are copied into a second set of LDS buffers a whole
 // block ahead, with DMA loads that hold no registers.  So the latency chain index -> gather -> product of
@@ -160,7 +126,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const WaveBlocks wb = wave_blocks(g.bh * g.rows[1], w);
+  const Sweep wb = xcd_sweep(g.bh * g.rows[1], 4 * (blockIdx.x / 8) + w, 4 * (gridDim.x / 8));
   if (wb.count == 0) return;  // no workgroup barrier is used below
   bf16_t* vt = vs[w];
   bf16_t* kt = ks[w];
@@ -188,40 +154,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   };
   auto block_slice = [&](int j) { return (wb.first + wb.stride * j) / g.rows[1]; };
 
-  // Stage s of the block in slot p (slice `slice`).  Every load instruction is coalesced: a quarter-wave
-  // (16 lanes) reads whole 128-byte lines (two bf16 rows, or half an fp32 row), and the rows are put into
-  // MFMA operand order through the LDS tiles.  The branch only forms two uniform base pointers and eight
-  // per-lane byte offsets; the eight loads then follow on one straight path, so that every stage leaves
-  // the same loads in flight in the same registers and the compiler's waits stay exact.
-  //   fine:   instruction m reads key rows 8m .. 8m+7 of the 32 keys (rows 0..15 of block b0, 16..31 of
-  //           block b1), lane l row 8m + l/8, bytes 16 (l%8) -- K into r[m], V into r[4+m];
-  //   coarse: instruction m reads the fp32 rows of enrichment entries e0 + 4m + l/16, bytes 16 (l%16).
+  // stage s of the block in slot p (slice `slice`), coalesced (see issue_stage_coalesced)
   auto issue = [&](int p, int slice, int s, Stage& st) {
-    const char* kb;
-    const char* vb;
-    uint32_t off[4];
-    if (s < plan.nfine) {
-      const int b0 = __builtin_amdgcn_readfirstlane(is1[w][p][2 * s]);
-      const int b1 = __builtin_amdgcn_readfirstlane(is1[w][p][min(2 * s + 1, g.K - 1)]);
-      kb = reinterpret_cast<const char*>(k + slice * slice_elems);
-      vb = reinterpret_cast<const char*>(v + slice * slice_elems);
-      const uint32_t sub = (uint32_t)lane >> 3, col = 16u * (lane & 7);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) off[m] = (16u * (m < 2 ? b0 : b1) + 8u * (m & 1) + sub) * (2 * kD) + col;
-    } else {
-      const int e0 = 16 * (s - plan.nfine) + (lane >> 4);
-      kb = reinterpret_cast<const char*>(pk + slice * slice_rows);
-      vb = reinterpret_cast<const char*>(pv + slice * slice_rows);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int e = min(e0 + 4 * m, plan.ncoarse - 1);
-        off[m] = (uint32_t)(es[w][p][e] + coarse_off(g, e)) * (4 * kD) + 16u * (lane & 15);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) st.r[m] = ld16(kb + off[m]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) st.r[4 + m] = ld16(vb + off[m]);
+    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], k + slice * slice_elems, v + slice * slice_elems,
+                          pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
   };
 
   int par = 0;                       // slot of the block being consumed
