@@ -478,8 +478,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
                                                      const int32_t* __restrict__ perm, const float* __restrict__ gk,
                                                      const float* __restrict__ gv, bf16_t* __restrict__ dk,
                                                      bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
-  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kLd];
-  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kLd];
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];   // Q rows of the query block (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];  // dO rows (swizzled)
+  __shared__ __attribute__((aligned(16))) float lds_ld[4][64];     // LSE (0..15) and Delta (16..31) of the queries
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
@@ -526,40 +527,49 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
   const int y0 = cp[j], y1 = cp[j + 1];
   bf16_t* qt = qs[w];
   bf16_t* dt = dos[w];
-  const bf16_t* qr = qt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-  const bf16_t* dr = dt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+  float* ldt = lds_ld[w];
+  const int c7 = c & 7;
+  const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
+  const int trr = 4 * gq + (c >> 2);
 
-  // One stage = one query block of the column: natural-order Q and dO rows 16i + c, LSE and Delta of
-  // queries 16i + 4g .. +3 (the rows of the S layout).
+  // One stage = one query block of the column, loaded coalesced: Q and dO rows (lane l: rows l/8 and 8 + l/8,
+  // bytes 16 (l%8)), then LSE (lanes 0..15) and Delta (lanes 16..31) of its 16 queries.
   struct QStage {
     uint4 q0, q1, d0, d1;
-    float4 ls, dl;
+    float ld;
   };
+  const int ro = (lane >> 3) * kD + 8 * (lane & 7);
   auto issue = [&](int i, QStage& st) {
-    load_natural(Q, 16u * i + c, lane, st.q0, st.q1);
-    load_natural(DO, 16u * i + c, lane, st.d0, st.d1);
-    st.ls = *reinterpret_cast<const float4*>(LS + 16 * i + 4 * gq);
-    st.dl = *reinterpret_cast<const float4*>(DL + 16 * i + 4 * gq);
+    const bf16_t* qr = Q + (size_t)16 * i * kD + ro;
+    const bf16_t* dr = DO + (size_t)16 * i * kD + ro;
+    st.q0 = ld16(qr);
+    st.q1 = ld16(qr + 8 * kD);
+    st.d0 = ld16(dr);
+    st.d1 = ld16(dr + 8 * kD);
+    st.ld = (lane < 16 ? LS : DL)[16 * i + (lane & 15)];
   };
   auto consume = [&](const QStage& st) {
     {
-      uint4* qd = reinterpret_cast<uint4*>(qt + c * kLd + 8 * gq);
-      uint4* dd = reinterpret_cast<uint4*>(dt + c * kLd + 8 * gq);
-      qd[0] = st.q0;
-      qd[4] = st.q1;  // +32 elements
-      dd[0] = st.d0;
-      dd[4] = st.d1;
+      const int r = lane >> 3, ch = lane & 7;
+      const int o0 = r * kD + ((ch ^ r) << 3), o1 = o0 + 8 * kD;
+      *reinterpret_cast<uint4*>(qt + o0) = st.q0;
+      *reinterpret_cast<uint4*>(qt + o1) = st.q1;
+      *reinterpret_cast<uint4*>(dt + o0) = st.d0;
+      *reinterpret_cast<uint4*>(dt + o1) = st.d1;
+      ldt[lane] = st.ld;  // every lane writes (lanes 32..63 a duplicate): no divergent store before the reads
     }
-    const bf16x8 qa0 = as_bf16x8(st.q0), qa1 = as_bf16x8(st.q1);
-    const bf16x8 da0 = as_bf16x8(st.d0), da1 = as_bf16x8(st.d1);
+    const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(qt + a0), qa1 = *reinterpret_cast<const bf16x8*>(qt + a1);
+    const bf16x8 da0 = *reinterpret_cast<const bf16x8*>(dt + a0), da1 = *reinterpret_cast<const bf16x8*>(dt + a1);
     f32x4 s = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
     s = mfma_bf16_k32(qa0, kb0, s);
     s = mfma_bf16_k32(qa1, kb1, s);
     dpv = mfma_bf16_k32(da0, vb0, dpv);
     dpv = mfma_bf16_k32(da1, vb1, dpv);
     // s[r] = S[query 4g + r][key c]
-    const float ls[4] = {st.ls.x, st.ls.y, st.ls.z, st.ls.w};
-    const float dl[4] = {st.dl.x, st.dl.y, st.dl.z, st.dl.w};
+    const float4 ls4 = *reinterpret_cast<const float4*>(ldt + 4 * gq);
+    const float4 dl4 = *reinterpret_cast<const float4*>(ldt + 16 + 4 * gq);
+    const float ls[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+    const float dl[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
     float p[4], ds[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -586,8 +596,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
     const bf16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      dv_acc[t] = mfma_bf16_k16(lds_read_tr16(dr + 16 * t), pb, dv_acc[t]);
-      dk_acc[t] = mfma_bf16_k16(lds_read_tr16(qr + 16 * t), db, dk_acc[t]);
+      const int x = swz(trr, 16 * t + 4 * (c & 3));
+      dv_acc[t] = mfma_bf16_k16(lds_read_tr16(dt + x), pb, dv_acc[t]);
+      dk_acc[t] = mfma_bf16_k16(lds_read_tr16(qt + x), db, dk_acc[t]);
     }
   };
 
@@ -606,28 +617,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
     }
   }
 
-  // lane holds d = 16t + 4g + r of key c; add the B^-l share of the level >= 2 pooled tokens
-  bf16_t* dkrow = dk + base + (size_t)(16 * j + c) * kD + 4 * gq;
-  bf16_t* dvrow = dv + base + (size_t)(16 * j + c) * kD + 4 * gq;
+  // lane holds d = 16t + 4g + r of key c; add the B^-l share of the level >= 2 pooled tokens, then bf16 rows
+  // through the Q tile and whole-row coalesced stores
+  float kx[4][4], vx[4][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float kx[4], vx[4];
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      kx[r] = dk_acc[t][r] * g.scale;
-      vx[r] = dv_acc[t][r];
+      kx[t][r] = dk_acc[t][r] * g.scale;
+      vx[t][r] = dv_acc[t][r];
     }
-    for (int l = 2; l <= g.Le; ++l) {
-      const int a = j >> (4 * (l - 1));
-      const float wgt = 1.0f / (float)(1 << (4 * l));
-      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 16 * t + 4 * gq;
-      const float4 gk4 = *reinterpret_cast<const float4*>(gk + gr);
-      const float4 gv4 = *reinterpret_cast<const float4*>(gv + gr);
-      kx[0] += gk4.x * wgt; kx[1] += gk4.y * wgt; kx[2] += gk4.z * wgt; kx[3] += gk4.w * wgt;
-      vx[0] += gv4.x * wgt; vx[1] += gv4.y * wgt; vx[2] += gv4.z * wgt; vx[3] += gv4.w * wgt;
+  for (int l = 2; l <= g.Le; ++l) {
+    const int a = j >> (4 * (l - 1));
+    const float wgt = 1.0f / (float)(1 << (4 * l));
+    const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 4 * gq;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 gk4 = *reinterpret_cast<const float4*>(gk + gr + 16 * t);
+      const float4 gv4 = *reinterpret_cast<const float4*>(gv + gr + 16 * t);
+      kx[t][0] += gk4.x * wgt; kx[t][1] += gk4.y * wgt; kx[t][2] += gk4.z * wgt; kx[t][3] += gk4.w * wgt;
+      vx[t][0] += gv4.x * wgt; vx[t][1] += gv4.y * wgt; vx[t][2] += gv4.z * wgt; vx[t][3] += gv4.w * wgt;
     }
-    *reinterpret_cast<uint2*>(dkrow + 16 * t) = make_uint2(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]));
-    *reinterpret_cast<uint2*>(dvrow + 16 * t) = make_uint2(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]));
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    *reinterpret_cast<uint2*>(qt + swz(c, 16 * t + 4 * gq)) =
+        make_uint2(pack_bf16x2(kx[t][0], kx[t][1]), pack_bf16x2(kx[t][2], kx[t][3]));
+    *reinterpret_cast<uint2*>(dt + swz(c, 16 * t + 4 * gq)) =
+        make_uint2(pack_bf16x2(vx[t][0], vx[t][1]), pack_bf16x2(vx[t][2], vx[t][3]));
+  }
+  {
+    const int r = lane >> 3, ch = lane & 7;
+    const int o0 = r * kD + ((ch ^ r) << 3);
+    const size_t go = base + ((size_t)16 * j + r) * kD + 8 * ch;
+    st16(dk + go, *reinterpret_cast<const uint4*>(qt + o0));
+    st16(dk + go + 8 * kD, *reinterpret_cast<const uint4*>(qt + o0 + 8 * kD));
+    st16(dv + go, *reinterpret_cast<const uint4*>(dt + o0));
+    st16(dv + go + 8 * kD, *reinterpret_cast<const uint4*>(dt + o0 + 8 * kD));
   }
 }
 
