@@ -431,14 +431,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
 
 // ------------------------------------------------------------------------------------------------
 // 2. Pooled-token gradients of levels 2..Le from the per-(level-2 unit, slot) partials via the CSC.
-// grid.x = sum_{l=2..Le} n_l, grid.y = slice; 64 threads (one per dim).
+// grid.x = sum_{l=2..Le} n_l, grid.y = slice; 256 threads.  Token j of level l sums, over the CSR positions
+// p = u*K + s of its column, the partials of entry (l, s) of the B^(l-2) level-2 units under unit u.  Those
+// (position, unit) items are dealt round-robin to the four waves (lane = dim), each wave adds its items in
+// order with four items' loads in flight, and the wave sums are added in wave order: a fixed order, so
+// the result is reproducible.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void coarse_reduce(const int32_t* __restrict__ col_ptr,
-                                                    const int32_t* __restrict__ perm,
-                                                    const float* __restrict__ part_k,
-                                                    const float* __restrict__ part_v, float* __restrict__ gk,
-                                                    float* __restrict__ gv, Geom g, CscGeom cg) {
-  const int slice = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__ col_ptr,
+                                                     const int32_t* __restrict__ perm,
+                                                     const float* __restrict__ part_k,
+                                                     const float* __restrict__ part_v, float* __restrict__ gk,
+                                                     float* __restrict__ gv, Geom g, CscGeom cg) {
+  __shared__ float red[2][4][kD];
+  const int slice = blockIdx.y, d = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int x = blockIdx.x, l = 2;
   while (x >= g.rows[l]) {
     x -= g.rows[l];
@@ -449,21 +455,43 @@ __global__ __launch_bounds__(64) void coarse_reduce(const int32_t* __restrict__ 
   const int n2 = g.rows[2];
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[l];
   const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[l];
-  const int span = 1 << (4 * (l - 2));  // level-2 units per level-l unit
+  const int sh = 4 * (l - 2);  // level-2 units per level-l unit: 1 << sh
+  const int y0 = cp[j];
+  const int items = (cp[j + 1] - y0) << sh;
+  const float* PKs = part_k + (size_t)slice * n2 * nhigh * kD + d;
+  const float* PVs = part_v + (size_t)slice * n2 * nhigh * kD + d;
   float ak = 0.f, av = 0.f;
-  for (int y = cp[j]; y < cp[j + 1]; ++y) {
-    const int p = pm[y];
-    const int u = p / g.K, slot = p - u * g.K;
-    const int e = (l - 2) * g.K + slot;
-    for (int u2 = u * span; u2 < (u + 1) * span; ++u2) {
-      const size_t off = (((size_t)slice * n2 + u2) * nhigh + e) * kD + d;
-      ak += part_k[off];
-      av += part_v[off];
+  for (int q0 = w; q0 < items; q0 += 16) {
+    float xk[4], xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + 4 * i;
+      xk[i] = xv[i] = 0.f;
+      if (q < items) {
+        const int p = pm[y0 + (q >> sh)];
+        const int u = p / g.K, slot = p - u * g.K;
+        const int u2 = (u << sh) + (q & ((1 << sh) - 1));
+        const size_t off = ((size_t)u2 * nhigh + (l - 2) * g.K + slot) * kD;
+        xk[i] = PKs[off];
+        xv[i] = PVs[off];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ak += xk[i];
+      av += xv[i];
     }
   }
-  const size_t o = ((size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + j) * kD + d;
-  gk[o] = ak;
-  gv[o] = av;
+  red[0][w][d] = ak;
+  red[1][w][d] = av;
+  __syncthreads();
+  if (w == 0) {
+    const float sk = ((red[0][0][d] + red[0][1][d]) + red[0][2][d]) + red[0][3][d];
+    const float sv = ((red[1][0][d] + red[1][1][d]) + red[1][2][d]) + red[1][3][d];
+    const size_t o = ((size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + j) * kD + d;
+    gk[o] = sk;
+    gv[o] = sv;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -699,7 +727,7 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
     int tokens = 0;
     for (int l = 2; l <= g.Le; ++l) tokens += g.rows[l];
     LaunchTimer timer(kBwdReduce, stream);
-    coarse_reduce<<<dim3(tokens, g.bh), 64, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, g,
+    coarse_reduce<<<dim3(tokens, g.bh), 256, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, g,
                                                           cg);
   }
   {
