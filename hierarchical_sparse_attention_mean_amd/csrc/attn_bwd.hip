@@ -495,10 +495,19 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
 }
 
 // ------------------------------------------------------------------------------------------------
-// 3. dK, dV per fine key block over its level-1 CSC column.
-// grid.x = ceil(bh * n_1 / 4) (remapped), 256 threads; wave w handles key block 4 * id + w.
+// 3. dK, dV over the level-1 CSC, four consecutive key blocks per wavefront.
+// grid.x = ceil(bh * ceil(n_1 / 4) / 4) (remapped), 256 threads; wave w takes key-block group 4 * id + w,
+// i.e. key blocks 4*gi .. 4*gi+3 of one slice.  The group's columns are consecutive in perm, so the wave walks
+// one list of query blocks (its stages) across its key blocks, the next stage's loads in flight while a stage
+// is consumed.  A key block's own rows (K, V and its level-1 pooled token) are copied to LDS (DMA) while the
+// previous block is consumed; the levels >= 2 shares -- the same for the four blocks, whose ancestors coincide
+// -- are copied once.  One wavefront per group (not persistent) keeps the hardware's dynamic scheduling over
+// the very uneven column lengths.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+constexpr int kGroup = 4;       // key blocks per wavefront
+constexpr int kMaxShares = 4;   // levels 2..L_e with L_e <= 5 (implied by the size limit n * d < 2^31)
+
+__global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
                                                      const float* __restrict__ pk, const float* __restrict__ pv,
@@ -506,62 +515,147 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
                                                      const int32_t* __restrict__ perm, const float* __restrict__ gk,
                                                      const float* __restrict__ gv, bf16_t* __restrict__ dk,
                                                      bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
-  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];   // Q rows of the query block (swizzled)
-  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];  // dO rows (swizzled)
-  __shared__ __attribute__((aligned(16))) float lds_ld[4][64];     // LSE (0..15) and Delta (16..31) of the queries
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];          // Q rows of the query block (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];         // dO rows (swizzled)
+  __shared__ __attribute__((aligned(16))) float lds_ld[4][64];            // LSE (0..15) and Delta (16..31)
+  __shared__ __attribute__((aligned(16))) bf16_t kvs[4][2][16 * kD];      // K, V rows of the next key block
+  __shared__ __attribute__((aligned(16))) float p1s[4][2][kD];            // its level-1 pooled K, V rows
+  __shared__ __attribute__((aligned(16))) float shs[4][kMaxShares][2][kD];  // ancestors' pooled K, V gradients
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
-  const int gb = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-  if (gb >= g.bh * n1) return;  // no workgroup barrier below
-  const int slice = gb / n1, j = gb - slice * n1;
+  const int gps = (n1 + kGroup - 1) / kGroup;
+  const int gid = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
+  if (gid >= g.bh * gps) return;  // no workgroup barrier below
+  const int slice = gid / gps, j0 = kGroup * (gid - slice * gps);
+  const int nkb = min(kGroup, n1 - j0);
   const size_t base = (size_t)slice * g.n * kD;
   const bf16_t* Q = q + base;
   const bf16_t* DO = dout + base;
   const float* LS = lse + (size_t)slice * g.n;
   const float* DL = delta + (size_t)slice * g.n;
-
-  // B operands (natural order) of this key block: K and V rows 16j + c
-  bf16x8 kb0, kb1, vb0, vb1;
-  {
-    uint4 a0, a1;
-    load_natural(k + base, 16u * j + c, lane, a0, a1);
-    kb0 = as_bf16x8(a0);
-    kb1 = as_bf16x8(a1);
-    load_natural(v + base, 16u * j + c, lane, a0, a1);
-    vb0 = as_bf16x8(a0);
-    vb1 = as_bf16x8(a1);
-  }
-  // level-1 pooled token of this block as a broadcast B operand (every column holds it), rounded to bf16
-  // as in the forward products: its scores land in the same [query 4g+r] layout as the raw keys' scores
-  const bool enrich1 = g.Le >= 1;
-  bf16x8 k1b0, k1b1, v1b0, v1b1;
-  {
-    const float* kp = pk + ((size_t)slice * g.R + g.off[1] + j) * kD + 8 * gq;
-    const float* vp = pv + ((size_t)slice * g.R + g.off[1] + j) * kD + 8 * gq;
-    const float4* k4 = reinterpret_cast<const float4*>(kp);
-    const float4* v4 = reinterpret_cast<const float4*>(vp);
-    k1b0 = f32x8_to_bf16x8(k4[0], k4[1]);
-    k1b1 = f32x8_to_bf16x8(k4[8], k4[9]);
-    v1b0 = f32x8_to_bf16x8(v4[0], v4[1]);
-    v1b1 = f32x8_to_bf16x8(v4[8], v4[9]);
-  }
-  f32x4 dk_acc[4], dv_acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
   const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[1];
-  const int y0 = cp[j], y1 = cp[j + 1];
   bf16_t* qt = qs[w];
   bf16_t* dt = dos[w];
   float* ldt = lds_ld[w];
   const int c7 = c & 7;
   const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
   const int trr = 4 * gq + (c >> 2);
+  const bool enrich1 = g.Le >= 1;
+  const int nsh = max(0, min(g.Le, kMaxShares + 1) - 1);
 
-  // One stage = one query block of the column, loaded coalesced: Q and dO rows (lane l: rows l/8 and 8 + l/8,
-  // bytes 16 (l%8)), then LSE (lanes 0..15) and Delta (lanes 16..31) of its 16 queries.
+  // column starts of the group's key blocks (lane t: column j0 + t; lane nkb: the end of the last one)
+  const int cpl = cp[j0 + min(lane, nkb)];
+  const int y0 = __builtin_amdgcn_readfirstlane(cpl);
+  const int total = __builtin_amdgcn_readlane(cpl, nkb) - y0;
+  auto col_len = [&](int b) { return __builtin_amdgcn_readlane(cpl, b + 1) - __builtin_amdgcn_readlane(cpl, b); };
+  auto next_nonempty = [&](int b) {  // first block after b with a non-empty column, nkb if none
+    int nb = b + 1;
+    while (nb < nkb && col_len(nb) == 0) ++nb;
+    return nb;
+  };
+
+  // copies of one key block's rows into the (single) block slot, and of the shares
+  auto dma_block = [&](int b) {
+    const size_t r = base + (size_t)16 * (j0 + b) * kD + swz_dma_src(lane);
+    lds_dma16(k + r, &kvs[w][0][0]);
+    lds_dma16(k + r + 8 * kD, &kvs[w][0][8 * kD]);
+    lds_dma16(v + r, &kvs[w][1][0]);
+    lds_dma16(v + r + 8 * kD, &kvs[w][1][8 * kD]);
+    if (lane < 32)
+      lds_dma16((lane < 16 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 4 * (lane & 15), &p1s[w][0][0]);
+  };
+  if (lane < 32) {
+    for (int s = 0; s < nsh; ++s) {
+      const int l = s + 2, a = j0 >> (4 * (l - 1));
+      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 4 * (lane & 15);
+      lds_dma16((lane < 16 ? gk : gv) + gr, &shs[w][s][0][0]);
+    }
+  }
+
+  // B operands (natural order) of the current key block: its K and V rows, and its level-1 pooled token as a
+  // broadcast operand (every column holds it), rounded to bf16 as in the forward products
+  bf16x8 kb0, kb1, vb0, vb1, k1b0, k1b1, v1b0, v1b1;
+  auto read_block = [&]() {
+    kb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a0]);
+    kb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a1]);
+    vb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a0]);
+    vb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a1]);
+    const float* kp = &p1s[w][0][8 * gq];
+    const float* vp = &p1s[w][1][8 * gq];
+    k1b0 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(kp), *reinterpret_cast<const float4*>(kp + 4));
+    k1b1 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(kp + 32), *reinterpret_cast<const float4*>(kp + 36));
+    v1b0 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(vp), *reinterpret_cast<const float4*>(vp + 4));
+    v1b1 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(vp + 32), *reinterpret_cast<const float4*>(vp + 36));
+    wait_lds();  // the slot is refilled next
+  };
+
+  f32x4 dk_acc[4], dv_acc[4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dk_acc[t] = dv_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // dK = sigma dK^T + shares, dV = dV^T + shares (lane holds d = 16t + 4g + r of key c; with_acc false for a key
+  // block no query block kept) -> bf16 rows through the Q / dO tiles, then whole-row coalesced stores
+  auto finish = [&](int b, bool with_acc) {
+    float kx[4][4], vx[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kx[t][r] = with_acc ? dk_acc[t][r] * g.scale : 0.f;
+        vx[t][r] = with_acc ? dv_acc[t][r] : 0.f;
+      }
+    for (int s = 0; s < nsh; ++s) {
+      const float wgt = 1.0f / (float)(1 << (4 * (s + 2)));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 gk4 = *reinterpret_cast<const float4*>(&shs[w][s][0][16 * t + 4 * gq]);
+        const float4 gv4 = *reinterpret_cast<const float4*>(&shs[w][s][1][16 * t + 4 * gq]);
+        kx[t][0] += gk4.x * wgt; kx[t][1] += gk4.y * wgt; kx[t][2] += gk4.z * wgt; kx[t][3] += gk4.w * wgt;
+        vx[t][0] += gv4.x * wgt; vx[t][1] += gv4.y * wgt; vx[t][2] += gv4.z * wgt; vx[t][3] += gv4.w * wgt;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      *reinterpret_cast<uint2*>(qt + swz(c, 16 * t + 4 * gq)) =
+          make_uint2(pack_bf16x2(kx[t][0], kx[t][1]), pack_bf16x2(kx[t][2], kx[t][3]));
+      *reinterpret_cast<uint2*>(dt + swz(c, 16 * t + 4 * gq)) =
+          make_uint2(pack_bf16x2(vx[t][0], vx[t][1]), pack_bf16x2(vx[t][2], vx[t][3]));
+    }
+    const int r = lane >> 3, ch = lane & 7;
+    const int o0 = r * kD + ((ch ^ r) << 3);
+    const size_t go = base + ((size_t)16 * (j0 + b) + r) * kD + 8 * ch;
+    st16(dk + go, *reinterpret_cast<const uint4*>(qt + o0));
+    st16(dk + go + 8 * kD, *reinterpret_cast<const uint4*>(qt + o0 + 8 * kD));
+    st16(dv + go, *reinterpret_cast<const uint4*>(dt + o0));
+    st16(dv + go + 8 * kD, *reinterpret_cast<const uint4*>(dt + o0 + 8 * kD));
+  };
+
+  int cb = next_nonempty(-1);  // key block being consumed
+  if (cb < nkb) dma_block(cb);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int b = 0; b < cb; ++b) finish(b, false);  // leading key blocks nobody kept
+  if (cb >= nkb) return;
+  read_block();
+  int nb = next_nonempty(cb);  // the block whose rows sit in the slot next
+  if (nb < nkb) dma_block(nb);
+  zero_acc();
+
+  // query blocks of the group's stages, 64 at a time in lanes (read with readlane)
+  int chunk = 0;
+  int qb_lane = pm[y0 + min(lane, total - 1)] / g.K;
+  auto stage_qb = [&](int s) {
+    if (s >= chunk + 64) {
+      chunk += 64;
+      qb_lane = pm[y0 + min(chunk + lane, total - 1)] / g.K;
+    }
+    return __builtin_amdgcn_readlane(qb_lane, s - chunk);
+  };
+
+  // One stage = one query block, loaded coalesced: Q and dO rows (lane l: rows l/8 and 8 + l/8, bytes
+  // 16 (l%8)), then LSE (lanes 0..15) and Delta (lanes 16..31) of its 16 queries.
   struct QStage {
     uint4 q0, q1, d0, d1;
     float ld;
@@ -576,7 +670,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
     st.d1 = ld16(dr + 8 * kD);
     st.ld = (lane < 16 ? LS : DL)[16 * i + (lane & 15)];
   };
-  auto consume = [&](const QStage& st) {
+  int gi = 0;  // last issued stage
+  auto issue_next = [&](QStage& st) {
+    gi = min(gi + 1, total - 1);  // past the end: an in-bounds reload that is never consumed
+    issue(stage_qb(gi), st);
+  };
+
+  auto compute = [&](const QStage& st) {
     {
       const int r = lane >> 3, ch = lane & 7;
       const int o0 = r * kD + ((ch ^ r) << 3), o1 = o0 + 8 * kD;
@@ -630,58 +730,36 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16_t* __restrict__ 
     }
   };
 
-  // The column's CSR positions are fetched 64 at a time into lanes and broadcast with readlane; each
-  // query block's rows are issued one stage ahead (always, clamped, so the waits stay exact).
-  for (int yb = y0; yb < y1; yb += 64) {
-    const int cnt = min(64, y1 - yb);
-    const int pv_lane = pm[yb + min(lane, cnt - 1)] / g.K;  // query block of entry yb + lane
-    QStage A, B;
-    issue(__builtin_amdgcn_readlane(pv_lane, 0), A);
-    for (int t = 0; t < cnt; t += 2) {
-      issue(__builtin_amdgcn_readlane(pv_lane, min(t + 1, cnt - 1)), B);
-      consume(A);
-      issue(__builtin_amdgcn_readlane(pv_lane, min(t + 2, cnt - 1)), A);
-      if (t + 1 < cnt) consume(B);
+  int gc = 0;  // stages consumed
+  int cend = __builtin_amdgcn_readlane(cpl, cb + 1) - y0;
+  auto consume = [&](const QStage& st) {
+    compute(st);
+    if (++gc == cend) {
+      // key block cb is complete.  The next non-empty block's rows were copied while cb was consumed: that
+      // copy is older than the one stage (5 loads) issued since, so vmcnt(5) covers it.  Its operands are
+      // read before cb's results are stored, so the stores never sit between the copy and this wait.
+      const int prev = cb;
+      if (nb < nkb) {
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        read_block();
+        cb = nb;
+        nb = next_nonempty(cb);
+        if (nb < nkb) dma_block(nb);
+        cend = __builtin_amdgcn_readlane(cpl, cb + 1) - y0;
+      }
+      finish(prev, true);
+      for (int b = prev + 1; b < (cb > prev ? cb : nkb); ++b) finish(b, false);  // blocks nobody kept
+      zero_acc();
     }
-  }
+  };
 
-  // lane holds d = 16t + 4g + r of key c; add the B^-l share of the level >= 2 pooled tokens, then bf16 rows
-  // through the Q tile and whole-row coalesced stores
-  float kx[4][4], vx[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      kx[t][r] = dk_acc[t][r] * g.scale;
-      vx[t][r] = dv_acc[t][r];
-    }
-  for (int l = 2; l <= g.Le; ++l) {
-    const int a = j >> (4 * (l - 1));
-    const float wgt = 1.0f / (float)(1 << (4 * l));
-    const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 4 * gq;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4 gk4 = *reinterpret_cast<const float4*>(gk + gr + 16 * t);
-      const float4 gv4 = *reinterpret_cast<const float4*>(gv + gr + 16 * t);
-      kx[t][0] += gk4.x * wgt; kx[t][1] += gk4.y * wgt; kx[t][2] += gk4.z * wgt; kx[t][3] += gk4.w * wgt;
-      vx[t][0] += gv4.x * wgt; vx[t][1] += gv4.y * wgt; vx[t][2] += gv4.z * wgt; vx[t][3] += gv4.w * wgt;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    *reinterpret_cast<uint2*>(qt + swz(c, 16 * t + 4 * gq)) =
-        make_uint2(pack_bf16x2(kx[t][0], kx[t][1]), pack_bf16x2(kx[t][2], kx[t][3]));
-    *reinterpret_cast<uint2*>(dt + swz(c, 16 * t + 4 * gq)) =
-        make_uint2(pack_bf16x2(vx[t][0], vx[t][1]), pack_bf16x2(vx[t][2], vx[t][3]));
-  }
-  {
-    const int r = lane >> 3, ch = lane & 7;
-    const int o0 = r * kD + ((ch ^ r) << 3);
-    const size_t go = base + ((size_t)16 * j + r) * kD + 8 * ch;
-    st16(dk + go, *reinterpret_cast<const uint4*>(qt + o0));
-    st16(dk + go + 8 * kD, *reinterpret_cast<const uint4*>(qt + o0 + 8 * kD));
-    st16(dv + go, *reinterpret_cast<const uint4*>(dt + o0));
-    st16(dv + go + 8 * kD, *reinterpret_cast<const uint4*>(dt + o0 + 8 * kD));
+  QStage A, B;
+  issue(stage_qb(0), A);
+  for (int t = 0; t < total; t += 2) {
+    issue_next(B);
+    consume(A);
+    issue_next(A);
+    if (t + 1 < total) consume(B);
   }
 }
 
@@ -732,7 +810,8 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    bwd_dkdv_bf16<<<(g.bh * n1 + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+    const int groups = g.bh * ((n1 + kGroup - 1) / kGroup);
+    bwd_dkdv_bf16<<<(groups + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                                                          (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm,
                                                          ws.gk, ws.gv, (bf16_t*)dk, (bf16_t*)dv, g, cg);
   }
