@@ -27,10 +27,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "LLSA fwd+bwd ms at N=65536 (MFMA util %, selection HBM GB/s)"
+COPY_PROBE_BYTES = 256 << 20
 WORKLOAD = "fwdbwd_bf16_n65536"
 
 
-KERNEL_SYMBOL = {"pool": "pool_levels123<bf16>", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
+KERNEL_SYMBOL = {"pool": "pool_levels123", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
                  "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "coarse_reduce",
                  "bwd_dkdv": "bwd_dkdv_bf16"}
 
@@ -103,6 +104,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain device copy of COPY_PROBE_BYTES after the warm-up (calibrates rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE; see hierarchical_sparse_attention_mean_amd/profiling.py)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
@@ -111,7 +115,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from hierarchical_sparse_attention_mean_amd import inputs, llsa
+    from hierarchical_sparse_attention_mean_amd import inputs, llsa, profiling
 
     w = inputs.WORKLOADS[args.workload]
     t0 = time.perf_counter()
@@ -137,6 +141,12 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -170,8 +180,11 @@ def main():
     dom = max(kernels, key=lambda nm: kernels[nm]["ms_per_step"])
     dk = kernels[dom]
     a_gbs = alg[dom]["bytes"] / (dk["avg_launch_ms"] * 1e-3) / 1e9 if dk["launches_per_step"] == 1 else dk["alg_GBps"]
+    # HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (calibrated by a plain copy), from the
+    # committed summary under profiles/; None when absent or when the kernel's sources changed since
+    traffic = profiling.read_traffic(KERNEL_SYMBOL[dom], w.name)
     roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": KERNEL_SYMBOL[dom], "kernel_avg_ms": dk["avg_launch_ms"],
                 "alg_bytes_per_launch": alg[dom]["bytes"], "alg_flops_per_launch": alg[dom]["flops"],
                 "mfma_frac": round(alg[dom]["flops"] / (dk["avg_launch_ms"] * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
