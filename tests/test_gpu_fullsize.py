@@ -1,0 +1,77 @@
+"""GPU parity at the benchmark sizes, in the launch configuration bench.py times, on sampled slices.
+
+The whole chain runs on every (batch, head) slice of the N = 65536 forward+backward workload (16 heads, K = 8,
+L = 3) and of the N = 262144 one (8 heads, K = 16, L = 3 -- the backward's two-tile path for the level >= 2
+partials).  The fp64 oracle runs on a few sampled slices only:
+  * selection of the sampled slices under the selection-parity rule (see test_gpu_parity);
+  * then the sampled slices' selection rows are replaced by the oracle's (the others keep the GPU's) and the
+    forward, transpose and backward run again on all slices, so that O, LSE, dQ, dK, dV of the sampled slices
+    compare element by element with the oracle (bf16: per slice max abs <= 2e-2 x max |ref|), col_ptr and
+    perm bit-exactly;
+  * every slice's outputs are finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check_close, host, selection_parity
+from hierarchical_sparse_attention_mean_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_sparse_attention_mean_amd import llsa
+    return llsa
+
+
+def _dev(t):
+    return torch.from_numpy(t.store.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _run_sampled(L, w, samples):
+    x = inputs.make_inputs(w, with_dout=True)
+    q, k, v, do = (_dev(x[nm]) for nm in ("q", "k", "v", "dout"))
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    b.forward(q, k, v)
+    b.backward(q, k, v, do)
+    torch.cuda.synchronize()
+    for t in (b.o, b.lse, b.dq, b.dk, b.dv):
+        assert torch.isfinite(t.float()).all()
+    idx = b.idx.clone()
+    for s in samples:
+        ex = {nm: x[nm].exact.reshape(w.bh, w.n, w.d)[s:s + 1] for nm in ("q", "k", "v", "dout")}
+        ref = oracle.run(ex["q"], ex["k"], ex["v"], w.block, w.topk, levels=w.levels, dout=ex["dout"])
+        compared, total = selection_parity(idx[s:s + 1].cpu().numpy(), ref["idx"], ref["pq"], ref["pk"], w.n,
+                                           w.block, w.levels, w.topk)
+        print(f"{w.name} slice {s}: selection rows compared {compared}/{total}")
+        assert compared >= 0.9 * total
+        # the oracle's selection for this slice, everything after it on the GPU again (all slices)
+        idx2 = idx.clone()
+        idx2[s] = torch.from_numpy(ref["idx"][0]).cuda()
+        b.idx.copy_(idx2)
+        L.attn_fwd(b.prob, q, k, v, b.pk, b.pv, b.idx, b.o, b.lse)
+        b.backward(q, k, v, do)
+        torch.cuda.synchronize()
+        assert np.array_equal(b.col_ptr[s].cpu().numpy(), ref["col_ptr"][0])
+        assert np.array_equal(b.perm[s].cpu().numpy(), ref["perm"][0])
+        msg = []
+        for nm, got in (("O", b.o), ("dq", b.dq), ("dk", b.dk), ("dv", b.dv)):
+            g = host(got).reshape(w.bh, w.n, w.d)[s:s + 1]
+            worst = check_close(nm, g.reshape(1, -1), ref[nm.lower()].reshape(1, -1), w.dtype)
+            msg.append(f"{nm} {worst:.2e}")
+        lse_err = np.abs(host(b.lse).reshape(w.bh, w.n)[s] - ref["lse"][0]).max()
+        assert lse_err <= 2e-2, lse_err
+        print(f"{w.name} slice {s}: " + ", ".join(msg) + f", lse {lse_err:.2e}")
+
+
+def test_fullsize_n65536_16_heads(L):
+    _run_sampled(L, inputs.WORKLOADS["fwdbwd_bf16_n65536"], samples=(0, 11))
+
+
+def test_fullsize_n262144_K16(L):
+    _run_sampled(L, inputs.WORKLOADS["fwdbwd_bf16_n262144"], samples=(5,))
