@@ -97,6 +97,45 @@ def oracle_baseline(w, x, budget_s=20.0):
                       f"scaled by {w.bh}/{done} to one step"}
 
 
+def dense_sdpa(w, q, k, v, do, steps, llsa_fwd_ms, llsa_step_ms):
+    """Dense attention at the same shapes with PyTorch SDPA (flash or memory-efficient backend only -- the math
+    backend would materialise n x n scores), timed for the forward and the forward+backward; the ratio to the
+    LLSA chain puts the sparse path beside dense attention."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    shape = (w.batch, w.heads, w.n, w.d)
+    qq, kk, vv, gg = (t.view(shape) for t in (q, k, v, do))
+    errors = {}
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([backend]):
+                F.scaled_dot_product_attention(qq, kk, vv)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    F.scaled_dot_product_attention(qq, kk, vv)
+                e1.record()
+                torch.cuda.synchronize()
+                fwd_ms = e0.elapsed_time(e1) / steps
+                ql, kl, vl = (t.detach().requires_grad_(True) for t in (qq, kk, vv))
+                F.scaled_dot_product_attention(ql, kl, vl).backward(gg)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(steps):
+                    F.scaled_dot_product_attention(ql, kl, vl).backward(gg)
+                e1.record()
+                torch.cuda.synchronize()
+                fb_ms = e0.elapsed_time(e1) / steps
+            return {"backend": backend.name, "fwd_ms": round(fwd_ms, 3), "fwdbwd_ms": round(fb_ms, 3),
+                    "llsa_fwd_chain_ms": round(llsa_fwd_ms, 4), "llsa_fwdbwd_ms": round(llsa_step_ms, 4),
+                    "speedup_fwd": round(fwd_ms / llsa_fwd_ms, 2), "speedup_fwdbwd": round(fb_ms / llsa_step_ms, 2)}
+        except RuntimeError as e:  # backend not available for these shapes / this device
+            errors[backend.name] = str(e).splitlines()[0][:200]
+    return {"error": errors}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +143,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--dense", action="store_true",
+                    help="also time dense PyTorch SDPA (flash / memory-efficient backend) at the same shapes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of COPY_PROBE_BYTES after the warm-up (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE; see hierarchical_sparse_attention_mean_amd/profiling.py)")
@@ -195,6 +236,11 @@ def main():
     sel_gbs = kernels["select"]["alg_GBps"]
     pool_gbs = kernels["pool"]["alg_GBps"]
 
+    dense = None
+    if args.dense:
+        fwd_chain = sum(kernels[nm]["ms_per_step"] for nm in ("pool", "select", "attn_fwd"))
+        dense = dense_sdpa(w, q, k, v, do, max(3, args.steps // 4), fwd_chain, ms_step)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = oracle_baseline(w, x)
@@ -214,6 +260,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "dense_sdpa": dense,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec))

@@ -1,0 +1,68 @@
+"""The dense-attention comparison at the same shapes (bench.py --dense) and the exact special case that links it
+to the method: when K covers every block and no enrichment level is used (L_e = 0), the enriched sparse
+attention is dense attention (each query attends every raw token once, bias 0).
+
+  * the GPU path on n = 512, L = 1, K = n_1 = 32, L_e = 0 equals the oracle, and the oracle equals dense
+    attention computed in fp64 on the CPU;
+  * PyTorch SDPA on the GPU (flash / memory-efficient backend, as bench.py times it) equals the same fp64
+    dense attention -- the comparator computes what it is compared against.
+bf16 tolerance: per slice max abs <= 2e-2 x max |ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check_close, dev, flat, host
+from hierarchical_sparse_attention_mean_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_sparse_attention_mean_amd import llsa
+    return llsa
+
+
+def _dense_ref(ex):
+    q, k, v = (torch.from_numpy(ex[nm]) for nm in ("q", "k", "v"))  # fp64 [bh, n, d], CPU
+    s = q @ k.transpose(1, 2) / np.sqrt(q.shape[-1])
+    return torch.softmax(s, dim=-1) @ v
+
+
+def test_full_coverage_no_enrichment_is_dense(L):
+    n, K = 512, 32
+    w = inputs.custom(1, 3, n, 64, "bf16", seed=31, topk=K, levels=1)
+    x = inputs.make_inputs(w)
+    ex = {nm: flat(t.exact) for nm, t in x.items()}
+    dense = _dense_ref(ex).numpy()
+    ref = oracle.run(ex["q"], ex["k"], ex["v"], w.block, K, levels=1, enrich_levels=0)
+    assert np.abs(ref["o"] - dense).max() < 1e-12
+    b = L.Buffers(L.problem(1, 3, n, 64, 16, K, 1, 0), backward=False)
+    b.forward(dev(x["q"]), dev(x["k"]), dev(x["v"]))
+    torch.cuda.synchronize()
+    assert np.all(b.idx.cpu().numpy() == np.arange(K))  # every block kept
+    check_close("O", flat(host(b.o)), dense, "bf16")
+
+
+def test_sdpa_comparator_is_dense_attention():
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    n = 4096
+    w = inputs.custom(1, 2, n, 64, "bf16", seed=32, topk=8, levels=2)
+    x = inputs.make_inputs(w)
+    ex = {nm: flat(t.exact) for nm, t in x.items()}
+    dense = _dense_ref(ex).numpy()
+    q, k, v = (dev(x[nm]) for nm in ("q", "k", "v"))
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([backend]):
+                o = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+        except RuntimeError:
+            continue
+        check_close("sdpa", flat(host(o)), dense, "bf16")
+        return
+    pytest.skip("no flash / memory-efficient SDPA backend on this device")
