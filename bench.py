@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--exhaustive", action="store_true",
+                    help="also time the single-level exhaustive Top-K and report the hierarchy's routing recall")
     ap.add_argument("--dense", action="store_true",
                     help="also time dense PyTorch SDPA (flash / memory-efficient backend) at the same shapes")
     ap.add_argument("--copy-probe", action="store_true",
@@ -236,6 +238,26 @@ def main():
     sel_gbs = kernels["select"]["alg_GBps"]
     pool_gbs = kernels["pool"]["alg_GBps"]
 
+    exhaustive = None
+    if args.exhaustive:
+        n1 = w.n // w.block
+        idx1 = torch.empty((w.bh, n1, w.topk), dtype=torch.int32, device="cuda")
+        llsa.select_exhaustive(p, b.pq, b.pk, idx1, stream)
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            llsa.select_exhaustive(p, b.pq, b.pk, idx1, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hier = b.idx[:, :n1]
+        hit = (hier[..., :, None] == idx1[..., None, :]).any(-1).sum(-1).float()
+        exhaustive = {"exhaustive_select_ms": round(e0.elapsed_time(e1) / reps, 4),
+                      "hierarchical_select_ms": kernels["select"]["ms_per_step"],
+                      "routing_recall": round(float(hit.mean()) / w.topk, 4),
+                      "units_fully_recalled": round(float((hit == w.topk).float().mean()), 4)}
+
     dense = None
     if args.dense:
         fwd_chain = sum(kernels[nm]["ms_per_step"] for nm in ("pool", "select", "attn_fwd"))
@@ -261,6 +283,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_sdpa": dense,
+        "exhaustive_selection": exhaustive,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec))

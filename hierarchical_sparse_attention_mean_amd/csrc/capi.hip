@@ -203,6 +203,15 @@ int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int3
   return launched(llsa::launch_select(r.g, pq, pk, idx, (hipStream_t)stream));
 }
 
+int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({pq, pk, idx1}));
+  LLSA_TRY(check_device());
+  return launched(llsa::launch_select_exhaustive(r.g, pq, pk, idx1, (hipStream_t)stream));
+}
+
 int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
                   const float* pv, const int32_t* idx, void* o, float* lse, void* stream) {
   Resolved r;

@@ -172,6 +172,138 @@ __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq
   topk_dispatch(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, picks, coarsest);
 }
 
+// ------------------------------------------------------------------------------------------------
+// Exhaustive single-level Top-K (the quadratic baseline of the hierarchy; "general Top-K" of Figure 1):
+// every level-1 unit scores all n_1 level-1 key blocks.  grid.x = slices x 16-unit tiles (remapped),
+// 256 threads.  Candidates stream by in chunks of 64 (one 16x16 fp32 MFMA tile per wave); each row keeps a
+// buffer of at most kBuf (score, block) pairs in LDS: a candidate enters only if its score beats the row's
+// current K-th best (candidates arrive in ascending block order, so an equal score loses the tie), and the
+// buffer is cut back to its best K whenever it passes kBuf - 64 entries.
+// ------------------------------------------------------------------------------------------------
+constexpr int kBuf = 128;
+
+// Best K of the first `cnt` entries of one row buffer, ties to the lower slot (= lower block), moved to slots
+// 0..K-1 in slot order; returns the order-preserving key of the K-th best.
+__device__ __forceinline__ uint32_t row_cut(float* bs, int* bi, int cnt, int K, int lane) {
+  uint32_t key[2];
+  float sv[2];
+  int iv[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int s = lane + 64 * m;
+    sv[m] = s < cnt ? bs[s] : 0.f;
+    iv[m] = s < cnt ? bi[s] : 0;
+    key[m] = s < cnt ? ord_key(sv[m]) : 0u;
+  }
+  uint32_t T = 0;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    const int c = popc64(__ballot(key[0] >= cand)) + popc64(__ballot(key[1] >= cand));
+    T = c >= K ? cand : T;
+  }
+  const int need = K - popc64(__ballot(key[0] > T)) - popc64(__ballot(key[1] > T));
+  int eq_before = 0, sel_before = 0;
+  int dst[2];
+  bool sel[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint64_t eqm = __ballot(key[m] == T);
+    sel[m] = key[m] > T || (key[m] == T && eq_before + lanes_below(eqm) < need);
+    const uint64_t selm = __ballot(sel[m]);
+    dst[m] = sel_before + lanes_below(selm);
+    eq_before += popc64(eqm);
+    sel_before += popc64(selm);
+  }
+  // every read above is done before any slot is overwritten (values are held in registers)
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (sel[m]) {
+      bs[dst[m]] = sv[m];
+      bi[dst[m]] = iv[m];
+    }
+  }
+  return T;
+}
+
+__global__ __launch_bounds__(256) void select_exhaustive(const float* __restrict__ pq, const float* __restrict__ pk,
+                                                         int32_t* __restrict__ out, Geom g) {
+  __shared__ float sc[16][64 + 4];
+  __shared__ float bs[16][kBuf];
+  __shared__ int bi[16][kBuf];
+  __shared__ uint32_t thr[16];
+  __shared__ int bcnt[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, gg = lane >> 4;
+  const int n1 = g.rows[1];
+  const int tiles = (n1 + 15) / 16;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = wg / tiles, q0 = 16 * (wg - slice * tiles);
+  const int nq = min(16, n1 - q0);
+  const float* PQ = pq + ((size_t)slice * g.R + g.off[1]) * kD;
+  const float* PK = pk + ((size_t)slice * g.R + g.off[1]) * kD;
+  float qf[16];
+  {
+    const float4* src = reinterpret_cast<const float4*>(PQ + (size_t)(q0 + min(c, nq - 1)) * kD + 16 * gg);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 x = src[m];
+      qf[4 * m] = x.x; qf[4 * m + 1] = x.y; qf[4 * m + 2] = x.z; qf[4 * m + 3] = x.w;
+    }
+  }
+  if (threadIdx.x < 16) {
+    thr[threadIdx.x] = 0u;
+    bcnt[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < n1; c0 += 64) {
+    {
+      const int j = c0 + 16 * w + c;
+      const bool valid = j < n1;
+      const float4* src = reinterpret_cast<const float4*>(PK + (size_t)(valid ? j : 0) * kD + 16 * gg);
+      float kf[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 x = src[m];
+        kf[4 * m] = x.x; kf[4 * m + 1] = x.y; kf[4 * m + 2] = x.z; kf[4 * m + 3] = x.w;
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) acc = mfma_f32_k4(qf[s2], kf[s2], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[4 * gg + r][16 * w + c] = valid ? acc[r] : -INFINITY;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 4 * w + rr;
+      if (row >= nq) break;
+      const float s = sc[row][lane];
+      const bool take = c0 + lane < n1 && ord_key(s) > thr[row];
+      const uint64_t mask = __ballot(take);
+      int cnt = bcnt[row];
+      if (take) {
+        const int pos = cnt + lanes_below(mask);
+        bs[row][pos] = s;
+        bi[row][pos] = c0 + lane;
+      }
+      cnt += popc64(mask);
+      if (cnt > kBuf - 64) {
+        const uint32_t T = row_cut(bs[row], bi[row], cnt, g.K, lane);
+        cnt = g.K;
+        if (lane == 0) thr[row] = T;
+      }
+      if (lane == 0) bcnt[row] = cnt;
+    }
+    __syncthreads();
+  }
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = 4 * w + rr;
+    if (row >= nq) break;
+    const int cnt = bcnt[row];
+    if (cnt > g.K) row_cut(bs[row], bi[row], cnt, g.K, lane);
+    if (lane < g.K) out[((size_t)slice * n1 + q0 + row) * g.K + lane] = bi[row][lane];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream) {
@@ -192,6 +324,14 @@ hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_
     LaunchTimer timer(kSelect, stream);
     select_level<<<grid, 256, 16 * ldc * sizeof(float), stream>>>(pq, pk, idx, g, l, 0, ncand, ldc);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_exhaustive(const Geom& g, const float* pq, const float* pk, int32_t* idx1,
+                                    hipStream_t stream) {
+  const int grid = ((g.rows[1] + 15) / 16) * g.bh;
+  LaunchTimer timer(kSelectExhaustive, stream);
+  select_exhaustive<<<grid, 256, 0, stream>>>(pq, pk, idx1, g);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd"} <= set(names)
+    assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd",
+            "llsa_select_exhaustive"} <= set(names)
     for n in names:
         assert hasattr(L.lib(), n), n
 
