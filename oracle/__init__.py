@@ -62,6 +62,10 @@ def _load():
     lib.llsa_ref_attn_bwd.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _i32, _dbl,
                                       _pd, _pd, _pd, _pd, _pd, _pd, _pd, _pd, _pi,
                                       _pd, _pd, _pd, _pd, _pd]
+    lib.llsa_ref_reorder_index.restype = _i32
+    lib.llsa_ref_reorder_index.argtypes = [_i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.llsa_ref_reorder.restype = None
+    lib.llsa_ref_reorder.argtypes = [_i64, _i64, _i32, ctypes.POINTER(ctypes.c_int64), _i32, _pd, _pd]
     lib.llsa_ref_num_threads.restype = _i32
     lib.llsa_ref_num_threads.argtypes = []
     _lib = lib
@@ -194,3 +198,23 @@ def run(q, k, v, block, topk, levels=None, enrich_levels=None, scale=None, dout=
                                         want_pooled=True)
         out.update(col_ptr=cp, perm=pm, dq=dq, dk=dk, dv=dv, dpk=dpk, dpv=dpv)
     return out
+
+
+def reorder_index(H: int, W: int, block: int, levels: int) -> np.ndarray:
+    """local_of[t]: position in the 2-D-local order of row-major pixel t (recursive sqrt(B) x sqrt(B) tiles)."""
+    out = np.empty(H * W, np.int64)
+    rc = _load().llsa_ref_reorder_index(H, W, block, levels, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    if rc != 0:
+        raise ValueError("block must be a square and sqrt(block)^levels must divide the grid")
+    return out
+
+
+def reorder(x: np.ndarray, local_of: np.ndarray, to_local: bool) -> np.ndarray:
+    """Rows of x [bh, n, d] moved to the 2-D-local order (to_local) or back to row-major."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    bh, n, d = x.shape
+    lo = np.ascontiguousarray(local_of, dtype=np.int64)
+    y = np.empty_like(x)
+    _load().llsa_ref_reorder(bh, n, d, lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(to_local), _d(x),
+                             _d(y))
+    return y

@@ -449,6 +449,56 @@ void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
   free(acc_v);
 }
 
+/*
+ * Index reordering [LLSA review, domain-assumption ledger: after index reordering spatially adjacent pixels
+ * are adjacent in the flattened sequence (paper Sec. 5.1, ablation Table 5d); Figure 2 caption, truncated].
+ * The page does not give the order.  Reading: recursive s x s tiles with s*s = B, so that every level-l unit
+ * (B^l consecutive tokens) is an s^l x s^l square patch for l <= L.  For an H x W grid with S = s^L dividing H
+ * and W, pixel (y, x) of the row-major sequence (position y*W + x) goes to
+ *   local = (row-major index of its S x S top tile) * B^L
+ *         + sum_{k < L} (s * digit_k(y mod S) + digit_k(x mod S)) * B^k,
+ * digit_k = k-th base-s digit.  With B = 4 this is the Morton (Z-order) curve inside each top tile; with L = 0
+ * it is the identity.  Returns 0, or -1 if B is not a square or S does not divide H and W.
+ */
+int llsa_ref_reorder_index(int64_t H, int64_t W, int B, int L, int64_t* local_of) {
+  int s = 1;
+  while ((int64_t)(s + 1) * (s + 1) <= B) ++s;
+  if ((int64_t)s * s != B) return -1;
+  int64_t S = 1, BL = 1;
+  for (int l = 0; l < L; ++l) {
+    S *= s;
+    BL *= B;
+  }
+  if (H % S != 0 || W % S != 0) return -1;
+  for (int64_t y = 0; y < H; ++y) {
+    for (int64_t x = 0; x < W; ++x) {
+      const int64_t tile = (y / S) * (W / S) + (x / S);
+      int64_t yy = y % S, xx = x % S, inner = 0, mult = 1;
+      for (int k = 0; k < L; ++k) {
+        inner += ((yy % s) * s + (xx % s)) * mult;
+        mult *= B;
+        yy /= s;
+        xx /= s;
+      }
+      local_of[y * W + x] = tile * BL + inner;
+    }
+  }
+  return 0;
+}
+
+/* Apply the reordering to the rows of x [bh][n][d]: to_local != 0 moves row t to row local_of[t]; otherwise
+ * row local_of[t] of x goes back to row t. */
+void llsa_ref_reorder(int64_t bh, int64_t n, int d, const int64_t* local_of, int to_local, const double* x,
+                      double* y) {
+  for (int64_t b = 0; b < bh; ++b) {
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t src = to_local ? t : local_of[t];
+      const int64_t dst = to_local ? local_of[t] : t;
+      for (int e = 0; e < d; ++e) y[(b * n + dst) * d + e] = x[(b * n + src) * d + e];
+    }
+  }
+}
+
 int llsa_ref_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
