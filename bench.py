@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--reorder", action="store_true",
+                    help="also time the chain on 2-D-locally reordered inputs (reorder Q, K, V, dO in; O, dQ, dK, "
+                         "dV back out)")
     ap.add_argument("--exhaustive", action="store_true",
                     help="also time the single-level exhaustive Top-K and report the hierarchy's routing recall")
     ap.add_argument("--dense", action="store_true",
@@ -258,6 +261,48 @@ def main():
                       "routing_recall": round(float(hit.mean()) / w.topk, 4),
                       "units_fully_recalled": round(float((hit == w.topk).float().mean()), 4)}
 
+    reordered = None
+    if args.reorder:
+        H, W = w.grid
+        qr, kr, vr, dr = (torch.empty_like(t) for t in (q, k, v, do))
+        o2, dq2, dk2, dv2 = (torch.empty_like(t) for t in (q, q, q, q))
+
+        def step_reordered():
+            for a, z in ((q, qr), (k, kr), (v, vr), (do, dr)):
+                llsa.reorder(p, H, W, True, a, z, stream)
+            llsa.build_pyramid(p, qr, kr, vr, b.pq, b.pk, b.pv, stream)
+            llsa.select(p, b.pq, b.pk, b.idx, stream)
+            llsa.attn_fwd(p, qr, kr, vr, b.pk, b.pv, b.idx, b.o, b.lse, stream)
+            llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
+            llsa.attn_bwd(p, qr, kr, vr, b.o, b.lse, dr, b.pk, b.pv, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv,
+                          b.ws_b, stream)
+            for a, z in ((b.o, o2), (b.dq, dq2), (b.dk, dk2), (b.dv, dv2)):
+                llsa.reorder(p, H, W, False, a, z, stream)
+
+        for _ in range(args.warmup):
+            step_reordered()
+        torch.cuda.synchronize()
+        llsa.timing_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step_reordered()
+        torch.cuda.synchronize()
+        ms_r = (time.perf_counter() - t0) * 1e3 / args.steps
+        fam_r = llsa.timing_read()
+        llsa.timing_enable(False)
+        if args.exhaustive:  # routing recall of the hierarchy on the reordered sequence
+            n1 = w.n // w.block
+            idx1 = torch.empty((w.bh, n1, w.topk), dtype=torch.int32, device="cuda")
+            llsa.select_exhaustive(p, b.pq, b.pk, idx1, stream)
+            torch.cuda.synchronize()
+            hit = (b.idx[:, :n1][..., :, None] == idx1[..., None, :]).any(-1).sum(-1).float()
+            recall_r = round(float(hit.mean()) / w.topk, 4)
+        else:
+            recall_r = None
+        reordered = {"grid": [H, W], "ms_per_step": round(ms_r, 4), "routing_recall": recall_r,
+                     "reorder_ms_per_step": round(fam_r["reorder"][0] / args.steps, 4),
+                     "kernels_ms_per_step": {nm: round(tc[0] / args.steps, 4) for nm, tc in fam_r.items() if tc[1]}}
+
     dense = None
     if args.dense:
         fwd_chain = sum(kernels[nm]["ms_per_step"] for nm in ("pool", "select", "attn_fwd"))
@@ -284,6 +329,7 @@ def main():
         "cpu_baseline": cpu,
         "dense_sdpa": dense,
         "exhaustive_selection": exhaustive,
+        "reordered_chain": reordered,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec))

@@ -212,6 +212,21 @@ int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const floa
   return launched(llsa::launch_select_exhaustive(r.g, pq, pk, idx1, (hipStream_t)stream));
 }
 
+int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32_t to_local, const void* x, void* y,
+                 void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  const int64_t S = (int64_t)1 << (2 * r.g.L);  // 4^L
+  if (grid_h < 1 || grid_w < 1 || (int64_t)grid_h * grid_w != r.p.n || grid_h % S != 0 || grid_w % S != 0)
+    return LLSA_ERR_SHAPE;
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({x, y}));
+  if (x == y) return LLSA_ERR_PARAM;
+  LLSA_TRY(check_device());
+  return launched(llsa::launch_reorder(r.g, r.p.dtype == LLSA_BF16 ? 2 : 4, grid_w, to_local != 0, x, y,
+                                       (hipStream_t)stream));
+}
+
 int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
                   const float* pv, const int32_t* idx, void* o, float* lse, void* stream) {
   Resolved r;

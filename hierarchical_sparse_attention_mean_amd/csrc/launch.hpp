@@ -9,7 +9,7 @@
 namespace llsa {
 
 // Kernel-family ids (same values as LLSA_KERNEL_* in llsa.h).
-enum KernelFamily { kPool = 0, kSelect, kAttnFwd, kTranspose, kBwdDq, kBwdReduce, kBwdDkdv, kSelectExhaustive, kFamilies };
+enum KernelFamily { kPool = 0, kSelect, kAttnFwd, kTranspose, kBwdDq, kBwdReduce, kBwdDkdv, kSelectExhaustive, kReorder, kFamilies };
 
 // Brackets one kernel launch with hipEvents on its stream while timing is enabled (llsa_timing_enable).
 class LaunchTimer {
@@ -43,6 +43,8 @@ int persistent_grid(const void* kernel, int threads, int64_t wanted);
 hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
                           float* pk, float* pv, hipStream_t stream);
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream);
+hipError_t launch_reorder(const Geom& g, int elem_bytes, int grid_w, int to_local, const void* x, void* y,
+                          hipStream_t stream);
 hipError_t launch_select_exhaustive(const Geom& g, const float* pq, const float* pk, int32_t* idx1,
                                     hipStream_t stream);
 hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v,

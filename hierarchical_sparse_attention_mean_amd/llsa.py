@@ -25,7 +25,7 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_L
     -1, -2, -3, -4, -5, -6, -7, -8, -9
 OP_INDEX_TRANSPOSE, OP_ATTN_BWD = 1, 2
 KERNELS = ("pool", "select", "attn_fwd", "transpose", "bwd_dq", "bwd_reduce", "bwd_dkdv",
-           "select_exhaustive")  # LLSA_KERNEL_* order
+           "select_exhaustive", "reorder")  # LLSA_KERNEL_* order
 
 
 class Problem(ctypes.Structure):
@@ -56,11 +56,12 @@ _sz = ctypes.c_size_t
 _lib.llsa_build_pyramid.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.llsa_select.argtypes = [_P, _vp, _vp, _vp, _vp]
 _lib.llsa_select_exhaustive.argtypes = [_P, _vp, _vp, _vp, _vp]
+_lib.llsa_reorder.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]
 _lib.llsa_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.llsa_index_transpose.argtypes = [_P, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.llsa_attn_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
-for _f in ("llsa_build_pyramid", "llsa_select", "llsa_select_exhaustive", "llsa_attn_fwd", "llsa_index_transpose",
-           "llsa_attn_bwd"):
+for _f in ("llsa_build_pyramid", "llsa_select", "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd",
+           "llsa_index_transpose", "llsa_attn_bwd"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.llsa_resolve.argtypes = [_P, _P]
 _lib.llsa_resolve.restype = ctypes.c_int
@@ -153,6 +154,12 @@ def select_exhaustive(prob, pq, pk, idx1, stream=None):
     """Single-level exhaustive Top-K over all level-1 blocks (idx1: int32 [batch*heads, n_1, K])."""
     _check(_lib.llsa_select_exhaustive(ctypes.byref(prob), _ptr(pq), _ptr(pk), _ptr(idx1), _stream(stream)),
            "llsa_select_exhaustive")
+
+
+def reorder(prob, grid_h, grid_w, to_local, x, y, stream=None):
+    """Rows of x moved to the 2-D-local order (to_local) or back to row-major, into y."""
+    _check(_lib.llsa_reorder(ctypes.byref(prob), grid_h, grid_w, int(bool(to_local)), _ptr(x), _ptr(y),
+                             _stream(stream)), "llsa_reorder")
 
 
 def attn_fwd(prob, q, k, v, pk, pv, idx, o, lse, stream=None):

@@ -102,6 +102,21 @@ int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int3
 int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, void* stream);
 
 /*
+ * llsa_reorder -- 2-D-local index reordering of the token rows [LLSA review, domain-assumption ledger: after
+ * index reordering spatially adjacent pixels are adjacent in the sequence (paper Sec. 5.1, ablation Table 5d);
+ * Figure 2 caption].  The page does not give the order; this one takes recursive 4 x 4 tiles, so that every
+ * level-l unit (16^l consecutive tokens) is a 4^l x 4^l pixel patch for l <= L: pixel (y, x) of the row-major
+ * grid goes to (row-major index of its 4^L x 4^L top tile) * 16^L + sum_{k<L} (4 digit_k(y) + digit_k(x)) 16^k,
+ * digit_k the k-th base-4 digit of the coordinate inside the top tile.  Applied before the path to Q, K, V
+ * (and dO), and with to_local = 0 after it to O (and dQ, dK, dV).
+ *   grid_h, grid_w: the pixel grid, grid_h * grid_w = n, both divisible by 4^L (LLSA_ERR_SHAPE otherwise).
+ *   to_local: non-zero: row-major -> local order; zero: local -> row-major.
+ *   x in, y out: raw tensors [batch][heads][n][d] (dtype), distinct buffers (LLSA_ERR_PARAM if x == y).
+ */
+int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32_t to_local, const void* x, void* y,
+                 void* stream);
+
+/*
  * llsa_attn_fwd -- sparse block attention with hierarchical KV enrichment [LLSA review, "Core
  * claim"; "What carries the argument"; abstract]: raw query t in fine block i = t/B attends the B
  * raw tokens of every level-1 block in idx row i (logit sigma*q.k) and, for l = 1..L_e, the level-l
@@ -173,7 +188,8 @@ enum {
   LLSA_KERNEL_BWD_REDUCE = 5, /* backward: pooled-token gradient reduction         */
   LLSA_KERNEL_BWD_DKDV = 6,   /* backward: dK, dV through the CSC                  */
   LLSA_KERNEL_SELECT_EXHAUSTIVE = 7, /* single-level exhaustive Top-K (not on the hot path) */
-  LLSA_KERNEL_COUNT = 8
+  LLSA_KERNEL_REORDER = 8,    /* 2-D-local index reordering                        */
+  LLSA_KERNEL_COUNT = 9
 };
 /* While enabled, every kernel this library launches is bracketed by two hipEvents recorded on its
  * launch stream (process-wide switch; off by default).  Enabling clears earlier records.  The events

@@ -25,7 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol(L):
     names = _declared()
     assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_select_exhaustive"} <= set(names)
+            "llsa_select_exhaustive", "llsa_reorder"} <= set(names)
     for n in names:
         assert hasattr(L.lib(), n), n
 
@@ -119,3 +119,13 @@ def test_timing_api_without_launches(L):
     t, c = ctypes.c_double(), ctypes.c_int64()
     assert L.lib().llsa_timing_read(99, ctypes.byref(t), ctypes.byref(c)) == L.ERR_PARAM
     assert L.lib().llsa_timing_read(0, None, None) == L.ERR_NULL
+
+
+def test_reorder_validation(L):
+    p = L.problem(1, 2, 65536)  # L = 3: the grid sides must be multiples of 4^3 = 64
+    f = L.lib()
+    assert f.llsa_reorder(ctypes.byref(p), 256, 256, 1, None, None, None) == L.ERR_NULL
+    assert f.llsa_reorder(ctypes.byref(p), 256, 128, 1, 16, 32, None) == L.ERR_SHAPE   # 256 * 128 != n
+    assert f.llsa_reorder(ctypes.byref(p), 32, 2048, 1, 16, 32, None) == L.ERR_SHAPE   # 64 does not divide 32
+    assert f.llsa_reorder(ctypes.byref(p), 256, 256, 1, 16, 16, None) == L.ERR_PARAM   # in place
+    assert f.llsa_reorder(ctypes.byref(p), 256, 256, 1, 16, 40, None) == L.ERR_ALIGN
