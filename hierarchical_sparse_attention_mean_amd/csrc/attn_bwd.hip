@@ -494,6 +494,70 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
   }
 }
 
+constexpr int kGroup = 4;       // key blocks per wavefront
+constexpr int kMaxShares = 4;   // levels 2..L_e with L_e <= 5 (implied by the size limit n * d < 2^31)
+
+// ------------------------------------------------------------------------------------------------
+// 3a. Work order of the dK/dV kernel: for each slice, its key-block groups (4 consecutive key blocks) with more
+// than 8K query blocks in their columns first, then the rest, each part in group order (a stable partition
+// by block-wide prefix sums, deterministic).  The dK/dV kernel takes groups in that order, so the longest
+// columns -- up to 20x the mean on smooth or reordered inputs -- start first instead of ending the kernel.
+// grid.x = slices, 1024 threads.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ col_ptr, int32_t* __restrict__ order,
+                                                   Geom g, CscGeom cg) {
+  __shared__ int wave_tot[16];
+  __shared__ int carry_s, nlong_s;
+  const int slice = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int n1 = g.rows[1], gps = (n1 + kGroup - 1) / kGroup;
+  const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
+  int32_t* out = order + (size_t)slice * gps;
+  const int thresh = 2 * kGroup * g.K;  // twice the mean group length
+  auto is_long = [&](int gi) { return gi < gps && cp[min(kGroup * gi + kGroup, n1)] - cp[kGroup * gi] > thresh; };
+  // block-wide exclusive prefix of a 0/1 flag, with the running carry across chunks
+  auto scan = [&](int f, int* excl, int* total) {
+    int inc = f;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const int u = __shfl_up(inc, s, 64);
+      if (lane >= s) inc += u;
+    }
+    if (lane == 63) wave_tot[w] = inc;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int i = 0; i < 16; ++i) {
+      before += i < w ? wave_tot[i] : 0;
+      tot += wave_tot[i];
+    }
+    *excl = before + inc - f;
+    *total = tot;
+    __syncthreads();
+  };
+  if (t == 0) {
+    carry_s = 0;
+    nlong_s = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < gps; base += 1024) {  // number of long groups
+    int e, tot;
+    scan(is_long(base + t), &e, &tot);
+    if (t == 0) nlong_s += tot;
+    __syncthreads();
+  }
+  const int nlong = nlong_s;
+  for (int base = 0; base < gps; base += 1024) {
+    const int gi = base + t;
+    const int f = is_long(gi);
+    int e, tot;
+    scan(f, &e, &tot);
+    const int long_before = carry_s + e;
+    if (gi < gps) out[f ? long_before : nlong + gi - long_before] = gi;
+    __syncthreads();
+    if (t == 0) carry_s += tot;
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // 3. dK, dV over the level-1 CSC, four consecutive key blocks per wavefront.
 // grid.x = ceil(bh * ceil(n_1 / 4) / 4) (remapped), 256 threads; wave w takes key-block group 4 * id + w,
@@ -504,8 +568,6 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
 // -- are copied once.  One wavefront per group (not persistent) keeps the hardware's dynamic scheduling over
 // the very uneven column lengths.
 // ------------------------------------------------------------------------------------------------
-constexpr int kGroup = 4;       // key blocks per wavefront
-constexpr int kMaxShares = 4;   // levels 2..L_e with L_e <= 5 (implied by the size limit n * d < 2^31)
 
 __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
@@ -513,7 +575,8 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
                                                      const float* __restrict__ pk, const float* __restrict__ pv,
                                                      const int32_t* __restrict__ col_ptr,
                                                      const int32_t* __restrict__ perm, const float* __restrict__ gk,
-                                                     const float* __restrict__ gv, bf16_t* __restrict__ dk,
+                                                     const float* __restrict__ gv,
+                                                     const int32_t* __restrict__ order, bf16_t* __restrict__ dk,
                                                      bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
   __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];          // Q rows of the query block (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];         // dO rows (swizzled)
@@ -525,9 +588,22 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
   const int gps = (n1 + kGroup - 1) / kGroup;
-  const int gid = xcd_remap(blockIdx.x, gridDim.x) * 4 + w;
-  if (gid >= g.bh * gps) return;  // no workgroup barrier below
-  const int slice = gid / gps, j0 = kGroup * (gid - slice * gps);
+  // Work item: the order list puts each slice's long groups first.  With bh a multiple of 8, XCD x (= block % 8,
+  // round-robin dispatch) owns slices [x bh/8, (x+1) bh/8) and walks their lists position-major, so every XCD
+  // starts on its longest groups and keeps its slices in its L2; otherwise all slices go position-major.
+  int slice, pos;
+  if (g.bh % 8 == 0) {
+    const int nsl = g.bh / 8, it = 4 * (blockIdx.x / 8) + w;
+    if (it >= nsl * gps) return;  // no workgroup barrier below
+    slice = (blockIdx.x % 8) * nsl + it % nsl;
+    pos = it / nsl;
+  } else {
+    const int it = 4 * blockIdx.x + w;
+    if (it >= g.bh * gps) return;
+    slice = it % g.bh;
+    pos = it / g.bh;
+  }
+  const int j0 = kGroup * order[(size_t)slice * gps + pos];
   const int nkb = min(kGroup, n1 - j0);
   const size_t base = (size_t)slice * g.n * kD;
   const bf16_t* Q = q + base;
@@ -772,6 +848,7 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
   const size_t n_delta = align256((size_t)g.bh * g.n * sizeof(float));
   const size_t n_part = nhigh ? align256((size_t)g.bh * g.rows[2] * nhigh * kD * sizeof(float)) : 0;
   const size_t n_g = nhigh ? align256((size_t)g.bh * (g.R - g.rows[1]) * kD * sizeof(float)) : 0;
+  const size_t n_order = align256((size_t)g.bh * ((g.rows[1] + kGroup - 1) / kGroup) * sizeof(int32_t));
   if (out) {
     char* p = static_cast<char*>(base);
     out->delta = reinterpret_cast<float*>(p);
@@ -783,8 +860,10 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
     out->gk = nhigh ? reinterpret_cast<float*>(p) : nullptr;
     p += n_g;
     out->gv = nhigh ? reinterpret_cast<float*>(p) : nullptr;
+    p += n_g;
+    out->order = reinterpret_cast<int32_t*>(p);
   }
-  return n_delta + 2 * n_part + 2 * n_g;
+  return n_delta + 2 * n_part + 2 * n_g + n_order;
 }
 
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
@@ -810,10 +889,12 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    const int groups = g.bh * ((n1 + kGroup - 1) / kGroup);
-    bwd_dkdv_bf16<<<(groups + 3) / 4, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                                                         (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm,
-                                                         ws.gk, ws.gv, (bf16_t*)dk, (bf16_t*)dv, g, cg);
+    const int gps = (n1 + kGroup - 1) / kGroup;
+    const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * gps + 3) / 4) : (g.bh * gps + 3) / 4;
+    dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.order, g, cg);
+    bwd_dkdv_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                            (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm, ws.gk, ws.gv,
+                                            ws.order, (bf16_t*)dk, (bf16_t*)dv, g, cg);
   }
   return hipGetLastError();
 }

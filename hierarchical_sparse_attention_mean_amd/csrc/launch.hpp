@@ -53,14 +53,16 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
 hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_t* idx, int32_t* col_ptr,
                                   int32_t* perm, int32_t* ws_cnt, int32_t* ws_tmp, hipStream_t stream);
 
-// Backward workspace carve-up (all fp32): delta [bh][n]; partials of pooled-token gradients for levels
-// >= 2 [bh][n_2][K*(Le-1)][d] (K and V); reduced pooled gradients of levels >= 2 [bh][R - n_1][d] (K, V).
+// Backward workspace carve-up: fp32 delta [bh][n]; partials of pooled-token gradients for levels >= 2
+// [bh][n_2][K*(Le-1)][d] (K and V); reduced pooled gradients of levels >= 2 [bh][R - n_1][d] (K, V); int32
+// dK/dV work order [bh][ceil(n_1 / 4)].
 struct BwdWs {
   float* delta;
   float* part_k;
   float* part_v;
   float* gk;
   float* gv;
+  int32_t* order;  // [bh][ceil(n_1 / 4)]: key-block groups of each slice, long columns first
 };
 size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base);
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
