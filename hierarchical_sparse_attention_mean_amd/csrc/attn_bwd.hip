@@ -32,12 +32,6 @@ namespace {
 
 constexpr int kLd = kD + 8;   // bf16 row stride of K / Q / dO tiles in LDS
 
-// Pyramid row of enrichment entry e for fine block i, and its level.
-__device__ __forceinline__ int coarse_row(const Geom& g, const int32_t* I, int i, int e, int* level) {
-  *level = coarse_level(g, e);
-  return coarse_row(g, I, i, e);
-}
-
 __device__ __forceinline__ float dot16_bf16(uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
   const uint32_t x[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
   const uint32_t y[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
@@ -66,7 +60,6 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
 // Q, dO, O rows, LSE and indices are copied to LDS a whole block ahead (LDS DMA).  Gathered K / V / pyramid
 // rows are loaded coalesced (issue_stage_coalesced) and reordered through swizzled LDS tiles.
 // ------------------------------------------------------------------------------------------------
-constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a limit of the GPU path)
 constexpr int kSt = 16 + 8;      // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
 
 // kT: 16-entry tiles of level >= 2 enrichment entries whose partials are held in registers (K*(L_e-1) <= 16 kT).
@@ -86,8 +79,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float lsl[4][2][16];         // LSE of the block's queries
   __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row
   __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
+  __shared__ __attribute__((aligned(16))) EntryTab tab;                // per-entry constants (shared)
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  fill_entry_tab(g, tab);
   const int n1 = g.rows[1];
   const int gps = (n1 + 15) / 16;
   const Sweep su = xcd_sweep(g.bh * gps, blockIdx.x / 8, gridDim.x / 8);
@@ -134,12 +129,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
       if (64 * jj < plan.ncoarse) {
         const int e = min(lane + 64 * jj, plan.ncoarse - 1);
-        lds_dma4(I + coarse_sel_pos(g, b.i, e), &es[w][p][64 * jj]);
+        lds_dma4(I + tab.pos0[e] + (b.i >> tab.shift[e]) * g.K, &es[w][p][64 * jj]);
       }
     }
   };
   auto issue = [&](int p, int slice, int s, Stage& st) {
-    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], k + slice * slice_elems, v + slice * slice_elems,
+    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems, v + slice * slice_elems,
                           pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
   };
 
@@ -291,11 +286,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     sx = mfma_bf16_k32(k1, qa1, sx);
     dpv = mfma_bf16_k32(v0, da0, dpv);
     dpv = mfma_bf16_k32(v1, da1, dpv);
+    // logit bias 4l (level-l weight B^l, log2 domain), -inf past the end of the list (P = 0)
+    const float4 bias = *reinterpret_cast<const float4*>(&tab.bias[e0 + 4 * gq]);
+    const float bb[4] = {bias.x - lse2, bias.y - lse2, bias.z - lse2, bias.w - lse2};
     float ds[4], pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = e0 + 4 * gq + r;
-      const float p = e < plan.ncoarse ? fast_exp2(sx[r] * sl2 + 4.0f * (float)coarse_level(g, e) - lse2) : 0.f;
+      const float p = fast_exp2(fmaf(sx[r], sl2, bb[r]));
       pr[r] = p;
       ds[r] = p * (dpv[r] - dlt);
     }

@@ -32,7 +32,6 @@ namespace llsa {
 namespace {
 
 constexpr int kLd = kD + 8;  // LDS row stride (bf16 elements): 144 bytes, 16-byte aligned rows
-constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a limit of the GPU path)
 
 struct Softmax {
   float m = -INFINITY;  // reference max (log2 domain), identical in the 4 lanes of a query
@@ -124,8 +123,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];       // Q rows of the next block
   __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row, two slots
   __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
+  __shared__ __attribute__((aligned(16))) EntryTab tab;                // per-entry constants (shared)
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  fill_entry_tab(g, tab);
   const Sweep wb = xcd_sweep(g.bh * g.rows[1], 4 * (blockIdx.x / 8) + w, 4 * (gridDim.x / 8));
   if (wb.count == 0) return;  // no workgroup barrier is used below
   bf16_t* vt = vs[w];
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
       if (64 * jj < plan.ncoarse) {
         const int e = min(lane + 64 * jj, plan.ncoarse - 1);
-        lds_dma4(I + (coarse_sel_pos(g, i, e)), &es[w][p][64 * jj]);
+        lds_dma4(I + tab.pos0[e] + (i >> tab.shift[e]) * g.K, &es[w][p][64 * jj]);
       }
     }
   };
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
 
   // stage s of the block in slot p (slice `slice`), coalesced (see issue_stage_coalesced)
   auto issue = [&](int p, int slice, int s, Stage& st) {
-    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], k + slice * slice_elems, v + slice * slice_elems,
+    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems, v + slice * slice_elems,
                           pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
   };
 
@@ -273,13 +274,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
     s0 = mfma_bf16_k32(a0, as_bf16x8(q0), s0);
     s0 = mfma_bf16_k32(a1, as_bf16x8(q1), s0);
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = e0 + 4 * gq + r;
-      // level-l weight B^l = 16^l -> + 4l in the log2 domain
-      x[r] = e < plan.ncoarse ? s0[r] * sl2 + 4.0f * (float)coarse_level(g, e) : -INFINITY;
-    }
+    // level-l weight B^l = 16^l -> + 4l in the log2 domain; -inf past the end of the list
+    const float4 bias = *reinterpret_cast<const float4*>(&tab.bias[e0 + 4 * gq]);
+    const float x[4] = {fmaf(s0[0], sl2, bias.x), fmaf(s0[1], sl2, bias.y), fmaf(s0[2], sl2, bias.z),
+                        fmaf(s0[3], sl2, bias.w)};
     sm.step16(x, vt, c, gq);
   };
 

@@ -60,9 +60,11 @@ __device__ __forceinline__ int swz_dma_src(int lane) { return (lane >> 3) * kD +
 //           of block b1 = sel[2s+1]), lane l row 8m + l/8, bytes 16 (l%8) -- K into r[m], V into r[4+m];
 //   coarse: instruction m reads the fp32 rows of enrichment entries 16(s - nfine) + 4m + l/16 (clamped to
 //           the list), bytes 16 (l%16) -- K into r[m], V into r[4+m].
-// sel: the block's level-1 selection row; esel: its enrichment entries' selection values (LDS).
+// sel: the block's level-1 selection row; esel: its enrichment entries' selection values; row0: the first
+// pyramid row of each entry's level (EntryTab::row0) -- all in LDS.
 __device__ __forceinline__ void issue_stage_coalesced(const Geom& g, const Plan& plan, int s, const int* sel,
-                                                      const int* esel, const bf16_t* kslice, const bf16_t* vslice,
+                                                      const int* esel, const int* row0, const bf16_t* kslice,
+                                                      const bf16_t* vslice,
                                                       const float* pkslice, const float* pvslice, int lane,
                                                       Stage& st) {
   const char* kb;
@@ -83,7 +85,7 @@ __device__ __forceinline__ void issue_stage_coalesced(const Geom& g, const Plan&
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = min(e0 + 4 * m, plan.ncoarse - 1);
-      off[m] = (uint32_t)(esel[e] + coarse_off(g, e)) * (4 * kD) + 16u * (lane & 15);
+      off[m] = (uint32_t)(esel[e] + row0[e]) * (4 * kD) + 16u * (lane & 15);
     }
   }
 #pragma unroll
