@@ -31,7 +31,7 @@ COPY_PROBE_BYTES = 256 << 20
 WORKLOAD = "fwdbwd_bf16_n65536"
 
 
-KERNEL_SYMBOL = {"pool": "pool_levels123", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
+KERNEL_SYMBOL = {"pool": "pool_levels12", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
                  "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "coarse_reduce",
                  "bwd_dkdv": "bwd_dkdv_bf16"}
 
@@ -48,10 +48,10 @@ def algorithmic(w, levels, enrich):
     fine = K * B                                       # raw keys per query
     coarse = K * enrich                                # enrichment tokens per query
     nhigh = K * max(0, enrich - 1)                     # enrichment tokens of levels >= 2 per query
-    pooled_kv = 2 * bh * R * d * 4                     # both fp32 pyramids of K and V
+    pooled_kv = 2 * bh * R * d * s                     # the bf16 copies of the K and V pyramids
     out = {}
-    # pyramid: read Q, K, V once, write three fp32 pyramids
-    out["pool"] = dict(bytes=tokens * (3 * d * s + 3 * d * 4 * pooled_frac), flops=0.0)
+    # pyramid: read Q, K, V once, write three fp32 pyramids and the bf16 copies of two
+    out["pool"] = dict(bytes=tokens * (3 * d * s + (3 * d * 4 + 2 * d * s) * pooled_frac), flops=0.0)
     # selection: per pooled query unit read its pooled query and key rows (fp32), its parent row and write
     # K indices; flops of the scored (unit, block) pairs
     out["select"] = dict(bytes=bh * R * (2 * d * 4 + 2 * K * 4),
@@ -72,7 +72,7 @@ def algorithmic(w, levels, enrich):
     out["bwd_reduce"] = dict(bytes=part + 2 * bh * (R - rows[0]) * d * 4, flops=0.0)
     # backward dK/dV kernel: read K, V, Q, dO, LSE, Delta, level-1 pooled K/V and reduced gradients; write dK, dV;
     # products S, dP, dV, dK over the fine entries plus the level-1 pooled token
-    out["bwd_dkdv"] = dict(bytes=tokens * (6 * d * s + 8) + 2 * bh * rows[0] * d * 4 + 2 * bh * (R - rows[0]) * d * 4,
+    out["bwd_dkdv"] = dict(bytes=tokens * (6 * d * s + 8) + 2 * bh * rows[0] * d * s + 2 * bh * (R - rows[0]) * d * 4,
                            flops=8.0 * d * fine * tokens + 6.0 * d * K * tokens)
     return out
 
@@ -177,11 +177,11 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        llsa.build_pyramid(p, q, k, v, b.pq, b.pk, b.pv, stream)
+        b.pyramid(q, k, v, stream)
         llsa.select(p, b.pq, b.pk, b.idx, stream)
-        llsa.attn_fwd(p, q, k, v, b.pk, b.pv, b.idx, b.o, b.lse, stream)
+        llsa.attn_fwd(p, q, k, v, b.pka, b.pva, b.idx, b.o, b.lse, stream)
         llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
-        llsa.attn_bwd(p, q, k, v, b.o, b.lse, do, b.pk, b.pv, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv, b.ws_b,
+        llsa.attn_bwd(p, q, k, v, b.o, b.lse, do, b.pka, b.pva, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv, b.ws_b,
                       stream)
 
     for _ in range(args.warmup):
@@ -270,11 +270,11 @@ def main():
         def step_reordered():
             for a, z in ((q, qr), (k, kr), (v, vr), (do, dr)):
                 llsa.reorder(p, H, W, True, a, z, stream)
-            llsa.build_pyramid(p, qr, kr, vr, b.pq, b.pk, b.pv, stream)
+            b.pyramid(qr, kr, vr, stream)
             llsa.select(p, b.pq, b.pk, b.idx, stream)
-            llsa.attn_fwd(p, qr, kr, vr, b.pk, b.pv, b.idx, b.o, b.lse, stream)
+            llsa.attn_fwd(p, qr, kr, vr, b.pka, b.pva, b.idx, b.o, b.lse, stream)
             llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
-            llsa.attn_bwd(p, qr, kr, vr, b.o, b.lse, dr, b.pk, b.pv, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv,
+            llsa.attn_bwd(p, qr, kr, vr, b.o, b.lse, dr, b.pka, b.pva, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv,
                           b.ws_b, stream)
             for a, z in ((b.o, o2), (b.dq, dq2), (b.dk, dk2), (b.dv, dv2)):
                 llsa.reorder(p, H, W, False, a, z, stream)

@@ -67,7 +67,7 @@ template <int kT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
                                                       const float* __restrict__ lse, const bf16_t* __restrict__ dout,
-                                                      const float* __restrict__ pk, const float* __restrict__ pv,
+                                                      const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
                                                       const int32_t* __restrict__ idx, bf16_t* __restrict__ dq,
                                                       float* __restrict__ delta, float* __restrict__ part_k,
                                                       float* __restrict__ part_v, Geom g) {
@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     }
   };
   auto issue = [&](int p, int slice, int s, Stage& st) {
-    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems, v + slice * slice_elems,
-                          pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
+    issue_stage_coalesced(plan, s, g.K, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems,
+                          v + slice * slice_elems, pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
   };
 
   int par = 0;   // slot of the block being consumed
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     }
   };
 
-  // dQ^T += K^T dS^T over 32 keys (k32; key order of the S tiles) or 16 entries (k16), K^T read transposed
+  // dQ^T += K^T dS^T over the stage's 32 keys (key order of the S tiles), K^T read transposed
   auto dq_32 = [&](const float ds[8]) {
     uint4 u;
     u.x = pack_bf16x2(ds[0], ds[1]);
@@ -216,15 +216,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
       dq_acc[t] = mfma_bf16_k32(ka, db, dq_acc[t]);
     }
   };
-  auto dq_16 = [&](const float ds[4]) {
-    const bf16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
-    const int r = 4 * gq + (c >> 2);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dq_acc[t] = mfma_bf16_k16(lds_read_tr16(kt + swz(r, 16 * t + 4 * (c & 3))), db, dq_acc[t]);
-  };
 
-  auto consume_fine = [&](int s, const Stage& st) {
-    const bool has1 = 2 * s + 1 < g.K;
+  // One stage of 32 keys (two fine blocks, or 32 enrichment entries): K and V rows into the swizzled tiles,
+  // S^T = K Q^T and dP^T = V dO^T per 16-key half, P = 2^(S sigma log2e + bias - LSE) with the stage's bias (fine:
+  // 0, or -inf for a missing second block; enrichment: 4l per entry, -inf past the end of the list),
+  // dS = P (dP - Delta), then dQ.  The first enrichment stage also holds the level >= 2 entries (at most 32).
+  auto consume_stage = [&](const Stage& st) {
     {
       const int r = lane >> 3, ch = lane & 7;
 #pragma unroll
@@ -234,11 +231,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
         *reinterpret_cast<uint4*>(vt + o2) = st.r[4 + m];
       }
     }
+    const bool coarse = cs >= plan.nfine;
+    float bb[8];
+    if (!coarse) {
+      const float h1 = 2 * cs + 1 < g.K ? -lse2 : -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bb[r] = -lse2;
+        bb[4 + r] = h1;
+      }
+    } else {
+      const int e0 = 32 * (cs - plan.nfine) + 4 * gq;
+      const float4 b0 = *reinterpret_cast<const float4*>(&tab.bias[e0]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&tab.bias[e0 + 16]);
+      bb[0] = b0.x - lse2; bb[1] = b0.y - lse2; bb[2] = b0.z - lse2; bb[3] = b0.w - lse2;
+      bb[4] = b1.x - lse2; bb[5] = b1.y - lse2; bb[6] = b1.z - lse2; bb[7] = b1.w - lse2;
+    }
     const int c7 = c & 7;
     const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
     bf16x8 qa0, qa1, da0, da1;
     qd_ops(qa0, qa1, da0, da1);
-    float ds[8];
+    float ds[8], pr[8];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int ro = 16 * kD * t2;
@@ -249,73 +262,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
       sx = mfma_bf16_k32(k1, qa1, sx);
       dpv = mfma_bf16_k32(v0, da0, dpv);
       dpv = mfma_bf16_k32(v1, da1, dpv);
-      const bool ok = t2 == 0 || has1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = ok ? fast_exp2(sx[r] * sl2 - lse2) : 0.f;
+        const float p = fast_exp2(fmaf(sx[r], sl2, bb[4 * t2 + r]));
+        pr[4 * t2 + r] = p;
         ds[4 * t2 + r] = p * (dpv[r] - dlt);
       }
     }
     dq_32(ds);
-  };
-
-  auto consume_coarse = [&](int sc, const Stage& st) {
-    const int e0 = 16 * sc;
-    {
-      // fp32 rows of entries 4m + lane/16, dims 4 (lane%16) .. +3 -> bf16 tile rows
-      const int r = lane >> 4, ch = (lane & 15) >> 1, hh = 4 * (lane & 1);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = 4 * m + r;
-        const int o2 = row * kD + (((ch ^ row) & 7) << 3) + hh;
-        float4 fk, fv;
-        __builtin_memcpy(&fk, &st.r[m], 16);
-        __builtin_memcpy(&fv, &st.r[4 + m], 16);
-        *reinterpret_cast<uint2*>(kt + o2) = make_uint2(pack_bf16x2(fk.x, fk.y), pack_bf16x2(fk.z, fk.w));
-        *reinterpret_cast<uint2*>(vt + o2) = make_uint2(pack_bf16x2(fv.x, fv.y), pack_bf16x2(fv.z, fv.w));
-      }
-    }
-    const int c7 = c & 7;
-    const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
-    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + a0), k1 = *reinterpret_cast<const bf16x8*>(kt + a1);
-    const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vt + a0), v1 = *reinterpret_cast<const bf16x8*>(vt + a1);
-    bf16x8 qa0, qa1, da0, da1;
-    qd_ops(qa0, qa1, da0, da1);
-    f32x4 sx = {0.f, 0.f, 0.f, 0.f}, dpv = {0.f, 0.f, 0.f, 0.f};
-    sx = mfma_bf16_k32(k0, qa0, sx);
-    sx = mfma_bf16_k32(k1, qa1, sx);
-    dpv = mfma_bf16_k32(v0, da0, dpv);
-    dpv = mfma_bf16_k32(v1, da1, dpv);
-    // logit bias 4l (level-l weight B^l, log2 domain), -inf past the end of the list (P = 0)
-    const float4 bias = *reinterpret_cast<const float4*>(&tab.bias[e0 + 4 * gq]);
-    const float bb[4] = {bias.x - lse2, bias.y - lse2, bias.z - lse2, bias.w - lse2};
-    float ds[4], pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(fmaf(sx[r], sl2, bb[r]));
-      pr[r] = p;
-      ds[r] = p * (dpv[r] - dlt);
-    }
-    dq_16(ds);
-    if (e0 < nhigh && cur.valid) {
-      // entries of levels >= 2 (shared by the unit's 256 queries): dK^(l)[e] += sum_q dS^T[e][q] q and
-      // dV^(l)[e] += sum_q P^T[e][q] dO over this block's 16 queries (16x16x16, k = query); dS^T and P^T go
-      // through a small tile in the V tile's space, whose operand reads are complete
+    if (coarse && cs == plan.nfine && nhigh > 0 && cur.valid) {
+      // entries of levels >= 2 (shared by the unit's 256 queries), 16-entry tile T = entries 16T .. 16T+15:
+      // dK^(l)[e] += sum_q dS^T[e][q] q and dV^(l)[e] += sum_q P^T[e][q] dO over this block's 16 queries
+      // (16x16x16, k = query); dS^T and P^T go through a small tile in the V tile's space, whose operand reads
+      // are complete
       bf16_t* sttile = vt;
       bf16_t* pttile = vt + 16 * kSt;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sttile[(4 * gq + r) * kSt + c] = f32_to_bf16(ds[r]);
-        pttile[(4 * gq + r) * kSt + c] = f32_to_bf16(pr[r]);
-      }
-      const bf16x4 as = *reinterpret_cast<const bf16x4*>(sttile + c * kSt + 4 * gq);
-      const bf16x4 ap = *reinterpret_cast<const bf16x4*>(pttile + c * kSt + 4 * gq);
       const bf16_t* qtile = qsl[w][par];
       const bf16_t* dtile = dsl[w][par];
       const int r = 4 * gq + (c >> 2);
 #pragma unroll
       for (int T = 0; T < kT; ++T) {
-        if (sc == T) {
+        if (16 * T < nhigh) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            sttile[(4 * gq + rr) * kSt + c] = f32_to_bf16(ds[4 * T + rr]);
+            pttile[(4 * gq + rr) * kSt + c] = f32_to_bf16(pr[4 * T + rr]);
+          }
+          const bf16x4 as = *reinterpret_cast<const bf16x4*>(sttile + c * kSt + 4 * gq);
+          const bf16x4 ap = *reinterpret_cast<const bf16x4*>(pttile + c * kSt + 4 * gq);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int x = swz(r, 16 * t + 4 * (c & 3));
@@ -395,10 +369,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   };
 
   auto consume = [&](const Stage& st) {
-    if (cs < plan.nfine)
-      consume_fine(cs, st);
-    else
-      consume_coarse(cs - plan.nfine, st);
+    consume_stage(st);
     if (++cs == nst) {
       finish_block();
       cs = 0;
@@ -569,7 +540,7 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
 __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
-                                                     const float* __restrict__ pk, const float* __restrict__ pv,
+                                                     const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
                                                      const int32_t* __restrict__ col_ptr,
                                                      const int32_t* __restrict__ perm, const float* __restrict__ gk,
                                                      const float* __restrict__ gv,
@@ -579,7 +550,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];         // dO rows (swizzled)
   __shared__ __attribute__((aligned(16))) float lds_ld[4][64];            // LSE (0..15) and Delta (16..31)
   __shared__ __attribute__((aligned(16))) bf16_t kvs[4][2][16 * kD];      // K, V rows of the next key block
-  __shared__ __attribute__((aligned(16))) float p1s[4][2][kD];            // its level-1 pooled K, V rows
+  __shared__ __attribute__((aligned(16))) bf16_t p1s[4][2][kD];           // its level-1 pooled K, V rows (bf16)
   __shared__ __attribute__((aligned(16))) float shs[4][kMaxShares][2][kD];  // ancestors' pooled K, V gradients
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -636,8 +607,8 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
     lds_dma16(k + r + 8 * kD, &kvs[w][0][8 * kD]);
     lds_dma16(v + r, &kvs[w][1][0]);
     lds_dma16(v + r + 8 * kD, &kvs[w][1][8 * kD]);
-    if (lane < 32)
-      lds_dma16((lane < 16 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 4 * (lane & 15), &p1s[w][0][0]);
+    if (lane < 16)
+      lds_dma16((lane < 8 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 8 * (lane & 7), &p1s[w][0][0]);
   };
   if (lane < 32) {
     for (int s = 0; s < nsh; ++s) {
@@ -647,20 +618,18 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
     }
   }
 
-  // B operands (natural order) of the current key block: its K and V rows, and its level-1 pooled token as a
-  // broadcast operand (every column holds it), rounded to bf16 as in the forward products
+  // B operands (natural order) of the current key block: its K and V rows, and its level-1 pooled token (bf16,
+  // as in the forward products) as a broadcast operand (every column holds it)
   bf16x8 kb0, kb1, vb0, vb1, k1b0, k1b1, v1b0, v1b1;
   auto read_block = [&]() {
     kb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a0]);
     kb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a1]);
     vb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a0]);
     vb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a1]);
-    const float* kp = &p1s[w][0][8 * gq];
-    const float* vp = &p1s[w][1][8 * gq];
-    k1b0 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(kp), *reinterpret_cast<const float4*>(kp + 4));
-    k1b1 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(kp + 32), *reinterpret_cast<const float4*>(kp + 36));
-    v1b0 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(vp), *reinterpret_cast<const float4*>(vp + 4));
-    v1b1 = f32x8_to_bf16x8(*reinterpret_cast<const float4*>(vp + 32), *reinterpret_cast<const float4*>(vp + 36));
+    k1b0 = *reinterpret_cast<const bf16x8*>(&p1s[w][0][8 * gq]);
+    k1b1 = *reinterpret_cast<const bf16x8*>(&p1s[w][0][8 * gq + 32]);
+    v1b0 = *reinterpret_cast<const bf16x8*>(&p1s[w][1][8 * gq]);
+    v1b1 = *reinterpret_cast<const bf16x8*>(&p1s[w][1][8 * gq + 32]);
     wait_lds();  // the slot is refilled next
   };
 
@@ -864,7 +833,7 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
 }
 
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
-                           const void* o, const float* lse, const void* dout, const float* pk, const float* pv,
+                           const void* o, const float* lse, const void* dout, const void* pk, const void* pv,
                            const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk,
                            void* dv, const BwdWs& ws, hipStream_t stream) {
   const int n1 = g.rows[1];
@@ -874,7 +843,8 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
     const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
     auto kernel = nhigh <= 16 ? bwd_dq_bf16<1> : bwd_dq_bf16<2>;
     kernel<<<persistent_grid((const void*)kernel, 256, groups), 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, lse, (const bf16_t*)dout, pk, pv,
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, lse, (const bf16_t*)dout,
+        (const bf16_t*)pk, (const bf16_t*)pv,
         idx, (bf16_t*)dq, ws.delta, ws.part_k, ws.part_v, g);
   }
   if (g.Le >= 2) {
@@ -890,7 +860,8 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
     const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * gps + 3) / 4) : (g.bh * gps + 3) / 4;
     dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.order, g, cg);
     bwd_dkdv_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                                            (const bf16_t*)dout, lse, ws.delta, pk, pv, col_ptr, perm, ws.gk, ws.gv,
+                                            (const bf16_t*)dout, lse, ws.delta, (const bf16_t*)pk,
+                                            (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv,
                                             ws.order, (bf16_t*)dk, (bf16_t*)dv, g, cg);
   }
   return hipGetLastError();

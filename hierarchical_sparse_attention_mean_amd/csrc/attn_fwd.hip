@@ -13,8 +13,8 @@
 //     lines) and put into operand order through wave-private LDS tiles: K read back as the MFMA A operand,
 //     V^T read with ds_read_b64_tr_b16 (transposed 4x16 reads).  Loading the operands directly in MFMA
 //     order would make each quarter-wave touch 16 rows, and the vector L1 is bound by such accesses.
-//   * Keys go two fine blocks (32 keys) per stage; enrichment tokens (fp32 pyramid rows, rounded to bf16
-//     for the products) go 16 per stage with a per-entry logit bias and a validity mask.
+//   * Keys go 32 per stage: two fine blocks, or 32 enrichment tokens (rows of the bf16 copy of the pooled
+//     pyramid) with a per-entry logit bias that is -inf past the end of the list.
 //   * Online softmax in the log2 domain with fp32 running max / sum; O rounded to bf16 at the end,
 //     natural-log LSE stored for the backward pass.
 //   * Persistent waves: each XCD sweeps a contiguous range of fine blocks with all its resident waves, and
@@ -94,18 +94,6 @@ struct Softmax {
       acc[t] = mfma_bf16_k32(va, pb, acc[t]);
     }
   }
-
-  // 16 keys: x[r] = key 4g+r; V rows 0..15 in the LDS tile (16x16x16 product over the keys).
-  __device__ void step16(const float x[4], const bf16_t* vt, int c, int gq) {
-    float p[4];
-    update<4>(x, p);
-    const uint2 pu = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    bf16x4 pb;
-    __builtin_memcpy(&pb, &pu, 8);
-    const bf16_t* r0 = vt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = mfma_bf16_k16(lds_read_tr16(r0 + 16 * t), pb, acc[t]);
-  }
 };
 
 // Persistent kernel: grid = 8 * (workgroups resident per XCD), 256 threads; each wave runs the fine blocks
@@ -115,8 +103,8 @@ struct Softmax {
 // block ahead, with DMA loads that hold no registers.  So the latency chain index -> gather -> product of
 // one block hides behind the work of the previous one.
 __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                     const bf16_t* __restrict__ v, const float* __restrict__ pk,
-                                                     const float* __restrict__ pv, const int32_t* __restrict__ idx,
+                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ pk,
+                                                     const bf16_t* __restrict__ pv, const int32_t* __restrict__ idx,
                                                      bf16_t* __restrict__ o, float* __restrict__ lse, Geom g) {
   __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];      // V tile (read transposed)
   __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];      // K tile (read as MFMA A operand)
@@ -157,8 +145,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
 
   // stage s of the block in slot p (slice `slice`), coalesced (see issue_stage_coalesced)
   auto issue = [&](int p, int slice, int s, Stage& st) {
-    issue_stage_coalesced(g, plan, s, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems, v + slice * slice_elems,
-                          pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
+    issue_stage_coalesced(plan, s, g.K, is1[w][p], es[w][p], tab.row0, k + slice * slice_elems,
+                          v + slice * slice_elems, pk + slice * slice_rows, pv + slice * slice_rows, lane, st);
   };
 
   int par = 0;                       // slot of the block being consumed
@@ -225,8 +213,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     if (gq == 0) lse[(size_t)cslice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
   };
 
-  auto consume_fine = [&](int s, const Stage& st) {
-    const bool has1 = 2 * s + 1 < g.K;
+  // One stage: the 32 key rows go to the K and V tiles; S^T = K Q^T for keys 0..15 (s0) and 16..31 (s1); the
+  // logits take the stage's bias (fine stages: 0, or -inf for a missing second block when K is odd; enrichment
+  // stages: 4l per entry -- level-l weight B^l = 16^l in the log2 domain -- and -inf past the end of the list).
+  auto consume = [&](const Stage& st) {
     {
       // key rows 8m + lane/8 of the 32 keys, 16 bytes at column 8*(lane%8), into the K and V tiles
       const int o = (lane >> 3) * kLd + 8 * (lane & 7);
@@ -236,7 +226,17 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
         *reinterpret_cast<uint4*>(vt + o + 8 * m * kLd) = st.r[4 + m];
       }
     }
-    // A operands: key row c (block b0) and 16 + c (block b1), dims 8g..8g+7 and 32+8g..32+8g+7
+    float4 b0, b1;
+    if (cs < plan.nfine) {
+      b0 = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float h1 = 2 * cs + 1 < g.K ? 0.f : -INFINITY;
+      b1 = make_float4(h1, h1, h1, h1);
+    } else {
+      const int e0 = 32 * (cs - plan.nfine) + 4 * gq;
+      b0 = *reinterpret_cast<const float4*>(&tab.bias[e0]);
+      b1 = *reinterpret_cast<const float4*>(&tab.bias[e0 + 16]);
+    }
+    // A operands: key row c and 16 + c, dims 8g..8g+7 and 32+8g..32+8g+7
     const bf16_t* kr = kt + c * kLd + 8 * gq;
     const bf16x8 k00 = *reinterpret_cast<const bf16x8*>(kr), k01 = *reinterpret_cast<const bf16x8*>(kr + 32);
     const bf16x8 k10 = *reinterpret_cast<const bf16x8*>(kr + 16 * kLd);
@@ -247,45 +247,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     s0 = mfma_bf16_k32(k01, qa1, s0);
     s1 = mfma_bf16_k32(k10, qa0, s1);
     s1 = mfma_bf16_k32(k11, qa1, s1);
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = s0[r] * sl2;
-      x[4 + r] = has1 ? s1[r] * sl2 : -INFINITY;
-    }
+    const float x[8] = {fmaf(s0[0], sl2, b0.x), fmaf(s0[1], sl2, b0.y), fmaf(s0[2], sl2, b0.z), fmaf(s0[3], sl2, b0.w),
+                        fmaf(s1[0], sl2, b1.x), fmaf(s1[1], sl2, b1.y), fmaf(s1[2], sl2, b1.z), fmaf(s1[3], sl2, b1.w)};
     sm.step32(x, vt, c, gq);
-  };
-  auto consume_coarse = [&](int e0, const Stage& st) {
-    {
-      // fp32 rows of entries 4m + lane/16, dims 4 (lane%16) .. +3 -> bf16 K and V tile rows; rows past the end
-      // of the list hold a valid duplicate whose probability is exactly 0
-      const int o = (lane >> 4) * kLd + 4 * (lane & 15);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float4 fk, fv;
-        __builtin_memcpy(&fk, &st.r[m], 16);
-        __builtin_memcpy(&fv, &st.r[4 + m], 16);
-        *reinterpret_cast<uint2*>(kt + o + 4 * m * kLd) = make_uint2(pack_bf16x2(fk.x, fk.y), pack_bf16x2(fk.z, fk.w));
-        *reinterpret_cast<uint2*>(vt + o + 4 * m * kLd) = make_uint2(pack_bf16x2(fv.x, fv.y), pack_bf16x2(fv.z, fv.w));
-      }
-    }
-    const bf16_t* kr = kt + c * kLd + 8 * gq;
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr), a1 = *reinterpret_cast<const bf16x8*>(kr + 32);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-    s0 = mfma_bf16_k32(a0, as_bf16x8(q0), s0);
-    s0 = mfma_bf16_k32(a1, as_bf16x8(q1), s0);
-    // level-l weight B^l = 16^l -> + 4l in the log2 domain; -inf past the end of the list
-    const float4 bias = *reinterpret_cast<const float4*>(&tab.bias[e0 + 4 * gq]);
-    const float x[4] = {fmaf(s0[0], sl2, bias.x), fmaf(s0[1], sl2, bias.y), fmaf(s0[2], sl2, bias.z),
-                        fmaf(s0[3], sl2, bias.w)};
-    sm.step16(x, vt, c, gq);
-  };
-
-  auto consume = [&](const Stage& st) {
-    if (cs < plan.nfine)
-      consume_fine(cs, st);
-    else
-      consume_coarse(16 * (cs - plan.nfine), st);
     if (++cs == nst) {
       finish_block();
       cs = 0;
@@ -388,17 +352,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
 }  // namespace
 
 hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v,
-                           const float* pk, const float* pv, const int32_t* idx, void* o, float* lse,
+                           const void* pk, const void* pv, const int32_t* idx, void* o, float* lse,
                            hipStream_t stream) {
   const int nb = g.bh * g.rows[1];
   const int grid = (nb + 3) / 4;
   LaunchTimer timer(kAttnFwd, stream);
   if (dtype_bf16)
-    attn_fwd_bf16<<<persistent_grid((const void*)attn_fwd_bf16, 256, grid), 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pk, pv, idx,
-                                            (bf16_t*)o, lse, g);
+    attn_fwd_bf16<<<persistent_grid((const void*)attn_fwd_bf16, 256, grid), 256, 0, stream>>>(
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx, (bf16_t*)o,
+        lse, g);
   else
-    attn_fwd_f32<<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pk, pv, idx,
-                                           (float*)o, lse, g);
+    attn_fwd_f32<<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, (const float*)pk,
+                                           (const float*)pv, idx, (float*)o, lse, g);
   return hipGetLastError();
 }
 

@@ -185,13 +185,16 @@ const char* llsa_status_string(int status) {
 }
 
 int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq, float* pk,
-                       float* pv, void* stream) {
+                       float* pv, void* pk_bf16, void* pv_bf16, void* stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
+  const bool bf16 = r.p.dtype == LLSA_BF16;
   LLSA_TRY(check_ptrs({q, k, v, pq, pk, pv}));
+  if (bf16) LLSA_TRY(check_ptrs({pk_bf16, pv_bf16}));
   LLSA_TRY(check_device());
-  return launched(llsa::launch_pyramid(r.g, r.p.dtype == LLSA_BF16, q, k, v, pq, pk, pv, (hipStream_t)stream));
+  return launched(llsa::launch_pyramid(r.g, bf16, q, k, v, pq, pk, pv, bf16 ? pk_bf16 : nullptr,
+                                       bf16 ? pv_bf16 : nullptr, (hipStream_t)stream));
 }
 
 int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, void* stream) {
@@ -227,8 +230,8 @@ int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32
                                        (hipStream_t)stream));
 }
 
-int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
-                  const float* pv, const int32_t* idx, void* o, float* lse, void* stream) {
+int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
+                  const void* pv, const int32_t* idx, void* o, float* lse, void* stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
@@ -254,7 +257,7 @@ int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* 
 }
 
 int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
-                  const float* lse, const void* dout, const float* pk, const float* pv, const int32_t* idx,
+                  const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
                   const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
                   size_t ws_bytes, void* stream) {
   Resolved r;

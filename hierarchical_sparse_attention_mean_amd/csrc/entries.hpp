@@ -5,9 +5,9 @@
 // l = 1..L_e the K level-l pooled tokens kept by its level-l ancestor unit i / B^(l-1), with logit bias
 // l*ln B.  Enrichment entry e (0 <= e < K*L_e) is ordered levels 2..L_e first, then level 1.
 //
-// The kernels walk this list in *stages* of equal register cost (8 x 16 bytes per lane):
-//   fine stage s   : raw key blocks I1[2s], I1[2s+1] (32 keys);
-//   coarse stage s : 16 enrichment tokens (fp32 pyramid rows).
+// The kernels walk this list in *stages* of 32 bf16 key rows (K and V, 8 x 16 bytes per lane):
+//   fine stage s   : raw key blocks I1[2s], I1[2s+1];
+//   coarse stage s : enrichment entries 32s .. 32s+31 (rows of the bf16 copy of the pooled pyramid).
 // Stage s+1's loads are issued before stage s is consumed, so one stage of loads is always in flight.
 #pragma once
 #include "common.hpp"
@@ -58,14 +58,14 @@ struct Stage {
 struct Plan {
   int nfine;     // ceil(K / 2) stages of raw key blocks
   int ncoarse;   // enrichment entries K * L_e
-  int nstages;   // nfine + ceil(ncoarse / 16)
+  int nstages;   // nfine + ceil(ncoarse / 32)
 };
 
 __device__ __forceinline__ Plan make_plan(const Geom& g) {
   Plan p;
   p.nfine = (g.K + 1) / 2;
   p.ncoarse = g.K * g.Le;
-  p.nstages = p.nfine + (p.ncoarse + 15) / 16;
+  p.nstages = p.nfine + (p.ncoarse + 31) / 32;
   return p;
 }
 
@@ -76,29 +76,27 @@ constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a
 //   row0[e]  first pyramid row of entry e's level;
 //   pos0[e], shift[e]  the entry's position in the slice's selection array for fine block i is
 //            pos0[e] + (i >> shift[e]) * K  (its ancestor unit of level l is i / B^(l-1));
-//   bias[e]  the logit bias l * log2(B) = 4l in the log2 domain, -inf past the end of the list (up to 16
+//   bias[e]  the logit bias l * log2(B) = 4l in the log2 domain, -inf past the end of the list (up to 31
 //            padding entries), so that the padded rows of a stage get probability exactly 0.
 // Entries past the end repeat the last entry's row and position (in-bounds duplicates).
 struct EntryTab {
   int row0[kMaxCoarse];
   int pos0[kMaxCoarse];
   int shift[kMaxCoarse];
-  float bias[kMaxCoarse + 16];
+  float bias[kMaxCoarse];
 };
 
 // All threads of the workgroup take part; ends with a workgroup barrier.
 __device__ __forceinline__ void fill_entry_tab(const Geom& g, EntryTab& t) {
   const int ncoarse = g.K * g.Le;
-  for (int e = threadIdx.x; e < kMaxCoarse + 16; e += blockDim.x) {
+  for (int e = threadIdx.x; e < kMaxCoarse; e += blockDim.x) {
     const int ec = min(e, max(ncoarse - 1, 0));
     int l, slot;
     coarse_entry(g, ec, &l, &slot);
-    if (e < kMaxCoarse) {
-      const int off = level_off(g, l);
-      t.row0[e] = off;
-      t.pos0[e] = off * g.K + slot;
-      t.shift[e] = 4 * (l - 1);
-    }
+    const int off = level_off(g, l);
+    t.row0[e] = off;
+    t.pos0[e] = off * g.K + slot;
+    t.shift[e] = 4 * (l - 1);
     t.bias[e] = e < ncoarse ? 4.0f * (float)l : -INFINITY;
   }
   __syncthreads();

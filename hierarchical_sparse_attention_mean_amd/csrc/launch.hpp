@@ -41,14 +41,14 @@ int resident_workgroups(const void* kernel, int threads);
 int persistent_grid(const void* kernel, int threads, int64_t wanted);
 
 hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
-                          float* pk, float* pv, hipStream_t stream);
+                          float* pk, float* pv, void* pk_bf16, void* pv_bf16, hipStream_t stream);
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream);
 hipError_t launch_reorder(const Geom& g, int elem_bytes, int grid_w, int to_local, const void* x, void* y,
                           hipStream_t stream);
 hipError_t launch_select_exhaustive(const Geom& g, const float* pq, const float* pk, int32_t* idx1,
                                     hipStream_t stream);
 hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v,
-                           const float* pk, const float* pv, const int32_t* idx, void* o, float* lse,
+                           const void* pk, const void* pv, const int32_t* idx, void* o, float* lse,
                            hipStream_t stream);
 hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_t* idx, int32_t* col_ptr,
                                   int32_t* perm, int32_t* ws_cnt, int32_t* ws_tmp, hipStream_t stream);
@@ -66,7 +66,7 @@ struct BwdWs {
 };
 size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base);
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
-                           const void* o, const float* lse, const void* dout, const float* pk, const float* pv,
+                           const void* o, const float* lse, const void* dout, const void* pk, const void* pv,
                            const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk,
                            void* dv, const BwdWs& ws, hipStream_t stream);
 

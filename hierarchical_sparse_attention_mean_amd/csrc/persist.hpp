@@ -52,40 +52,39 @@ __device__ __forceinline__ int swz(int row, int col) { return row * kD + ((((col
 __device__ __forceinline__ int swz_dma_src(int lane) { return (lane >> 3) * kD + (((lane & 7) ^ (lane >> 3)) << 3); }
 
 // Loads of stage s of a block's plan, coalesced: a quarter-wave (16 lanes) reads whole 128-byte lines (two
-// bf16 rows, or half an fp32 row), and the consumer puts rows into MFMA operand order through LDS tiles.
-// The branch only forms two uniform base pointers and eight per-lane byte offsets; the eight loads then
+// bf16 rows), and the consumer puts rows into MFMA operand order through LDS tiles.  Instruction m reads
+// rows 8m .. 8m+7 of the stage's 32 keys (lane l: row 8m + l/8, bytes 16 (l%8)) -- K into r[m], V into
+// r[4+m]:
+//   fine:   rows 0..15 are key block b0 = sel[2s], rows 16..31 block b1 = sel[2s+1] (raw K, V);
+//   coarse: row j is enrichment entry 32(s - nfine) + j (clamped to the list) of the bf16 pooled pyramid.
+// The branch only forms two uniform base pointers and four per-lane byte offsets; the eight loads then
 // follow on one straight path, so every stage leaves the same loads in flight in the same registers and
 // the compiler's waits stay exact.
-//   fine:   instruction m reads key rows 8m .. 8m+7 of the 32 keys (rows 0..15 of block b0 = sel[2s], 16..31
-//           of block b1 = sel[2s+1]), lane l row 8m + l/8, bytes 16 (l%8) -- K into r[m], V into r[4+m];
-//   coarse: instruction m reads the fp32 rows of enrichment entries 16(s - nfine) + 4m + l/16 (clamped to
-//           the list), bytes 16 (l%16) -- K into r[m], V into r[4+m].
 // sel: the block's level-1 selection row; esel: its enrichment entries' selection values; row0: the first
 // pyramid row of each entry's level (EntryTab::row0) -- all in LDS.
-__device__ __forceinline__ void issue_stage_coalesced(const Geom& g, const Plan& plan, int s, const int* sel,
+__device__ __forceinline__ void issue_stage_coalesced(const Plan& plan, int s, int K, const int* sel,
                                                       const int* esel, const int* row0, const bf16_t* kslice,
-                                                      const bf16_t* vslice,
-                                                      const float* pkslice, const float* pvslice, int lane,
-                                                      Stage& st) {
+                                                      const bf16_t* vslice, const bf16_t* pkslice,
+                                                      const bf16_t* pvslice, int lane, Stage& st) {
   const char* kb;
   const char* vb;
   uint32_t off[4];
+  const uint32_t sub = (uint32_t)lane >> 3, col = 16u * (lane & 7);
   if (s < plan.nfine) {
     const int b0 = __builtin_amdgcn_readfirstlane(sel[2 * s]);
-    const int b1 = __builtin_amdgcn_readfirstlane(sel[min(2 * s + 1, g.K - 1)]);
+    const int b1 = __builtin_amdgcn_readfirstlane(sel[min(2 * s + 1, K - 1)]);
     kb = reinterpret_cast<const char*>(kslice);
     vb = reinterpret_cast<const char*>(vslice);
-    const uint32_t sub = (uint32_t)lane >> 3, col = 16u * (lane & 7);
 #pragma unroll
     for (int m = 0; m < 4; ++m) off[m] = (16u * (m < 2 ? b0 : b1) + 8u * (m & 1) + sub) * (2 * kD) + col;
   } else {
-    const int e0 = 16 * (s - plan.nfine) + (lane >> 4);
+    const int e0 = 32 * (s - plan.nfine) + (int)sub;
     kb = reinterpret_cast<const char*>(pkslice);
     vb = reinterpret_cast<const char*>(pvslice);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int e = min(e0 + 4 * m, plan.ncoarse - 1);
-      off[m] = (uint32_t)(esel[e] + row0[e]) * (4 * kD) + 16u * (lane & 15);
+      const int e = min(e0 + 8 * m, plan.ncoarse - 1);
+      off[m] = (uint32_t)(esel[e] + row0[e]) * (2 * kD) + col;
     }
   }
 #pragma unroll

@@ -3,13 +3,15 @@
 // Method: X^(l)[j] = (1/B) * sum_{t<B} X^(l-1)[jB + t], X^(0) = X, l = 1..L
 // [LLSA review (pith.science, arXiv 2512.16615), "Core claim" and "What carries the argument"].
 //
-// Design (HBM-bound streaming reduction, read once, all levels in one pass):
-//   * One 256-thread workgroup owns one level-3 unit (16 chunks of 256 raw tokens) of one tensor of
-//     one slice when L >= 3, else one level-2 unit (or one 256-token chunk when L = 1).
-//   * Per chunk each thread sums 8 rows x 8 dims (16-byte loads), pairs with its partner lane for the
-//     16-row level-1 mean, writes it, and the level-2 mean is formed from LDS; level 3 accumulates
-//     in registers across the 16 chunks.  The next chunk is loaded before the current one is reduced.
-//   * Levels >= 4 (n >= B^5) are pooled by a small follow-up kernel from level 3.
+// Design (HBM-bound streaming reduction, raw tensors read once):
+//   * pool_levels12: one 256-thread workgroup per 256-token chunk (one level-2 unit) of one tensor of one
+//     slice -- bh * n / 256 * 3 independent workgroups, enough to keep every CU's loads in flight.  Each
+//     thread loads 8 rows x 8 dims (8 x 16 bytes, all issued at once), pairs with its partner lane for the
+//     16-row level-1 mean, and the level-2 mean is formed from LDS.
+//   * pool_up: level l >= 3 from level l - 1 (1/256 of the raw bytes and less).
+//   * For bf16 problems the pooled K and V rows are also stored rounded to bf16 (the attention kernels'
+//     operands -- their products round pooled tokens to bf16 anyway), so that the attention gathers read
+//     128 bytes per pooled row instead of 256.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -65,104 +67,103 @@ struct ChunkRegs<float> {
   }
 };
 
-// grid.x = units per slice, grid.y = slice, grid.z = tensor (0 = Q, 1 = K, 2 = V)
+// Outputs of one tensor: the fp32 pyramid and, for K and V of bf16 problems, its bf16 copy (else null).
+struct PoolDst {
+  float* f;
+  bf16_t* h;
+};
+
+// grid.x = 256-token chunks per slice, grid.y = slice, grid.z = tensor (0 = Q, 1 = K, 2 = V)
 template <typename T>
-__global__ __launch_bounds__(256) void pool_levels123(const T* __restrict__ q, const T* __restrict__ k,
-                                                      const T* __restrict__ v, float* __restrict__ pq,
-                                                      float* __restrict__ pk, float* __restrict__ pv, Geom g,
-                                                      int chunks_per_wg) {
+__global__ __launch_bounds__(256) void pool_levels12(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, float* __restrict__ pq,
+                                                     float* __restrict__ pk, float* __restrict__ pv,
+                                                     bf16_t* __restrict__ pkh, bf16_t* __restrict__ pvh, Geom g) {
   __shared__ float l1s[16][kD];
-  const int tensor = blockIdx.z, slice = blockIdx.y, wg = blockIdx.x;
+  const int tensor = blockIdx.z, slice = blockIdx.y, gc = blockIdx.x;
   const T* src = (tensor == 0 ? q : tensor == 1 ? k : v) + (size_t)slice * g.n * kD;
-  float* dst = (tensor == 0 ? pq : tensor == 1 ? pk : pv) + (size_t)slice * g.R * kD;
+  const size_t pbase = (size_t)slice * g.R * kD;
+  float* dst = (tensor == 0 ? pq : tensor == 1 ? pk : pv) + pbase;
+  bf16_t* dsth = tensor == 0 ? nullptr : (tensor == 1 ? pkh : pvh);
+  if (dsth) dsth += pbase;
   const int t = threadIdx.x;
   const int dim0 = 8 * (t & 7), half = (t >> 3) & 1, u1 = t >> 4;
-  const int n1 = g.rows[1];
+  const int row1 = 16 * gc + u1;
   const float inv = 1.0f / (float)kB;
 
-  float acc3 = 0.f;
-  ChunkRegs<T> cur, nxt;
-  {
-    const int gc = wg * chunks_per_wg;
-    const int valid = (16 * gc + u1) < n1;
-    cur.load(src + ((size_t)256 * gc + u1 * 16 + half * 8) * kD + dim0, valid);
+  ChunkRegs<T> cur;
+  cur.load(src + ((size_t)256 * gc + u1 * 16 + half * 8) * kD + dim0, row1 < g.rows[1]);
+  float s[8];
+  cur.sum(s);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] += shfl_xor_f(s[e], 8);
+  float m[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m[e] = s[4 * half + e] * inv;
+  const int col = dim0 + 4 * half;
+  if (row1 < g.rows[1]) {
+    const size_t o = (size_t)(g.off[1] + row1) * kD + col;
+    *reinterpret_cast<float4*>(dst + o) = make_float4(m[0], m[1], m[2], m[3]);
+    if (dsth) *reinterpret_cast<uint2*>(dsth + o) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
   }
-  for (int c = 0; c < chunks_per_wg; ++c) {
-    const int gc = wg * chunks_per_wg + c;
-    const int row1 = 16 * gc + u1;
-    if (c + 1 < chunks_per_wg) {
-      const int valid = (row1 + 16) < n1;
-      nxt.load(src + ((size_t)256 * (gc + 1) + u1 * 16 + half * 8) * kD + dim0, valid);
-    }
-    float s[8];
-    cur.sum(s);
+  if (g.L >= 2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += shfl_xor_f(s[e], 8);
-    float m[4];
+    for (int e = 0; e < 4; ++e) l1s[u1][col + e] = m[e];
+    __syncthreads();
+    if (t < kD / 2) {
+      // two dims per thread, so that the bf16 copy is one 4-byte store
+      float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m[e] = s[4 * half + e] * inv;
-    if (row1 < n1)
-      *reinterpret_cast<float4*>(dst + (size_t)(g.off[1] + row1) * kD + dim0 + 4 * half) =
-          make_float4(m[0], m[1], m[2], m[3]);
-    if (g.L >= 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) l1s[u1][dim0 + 4 * half + e] = m[e];
-      __syncthreads();
-      if (t < kD) {
-        float x = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x += l1s[r][t];
-        x *= inv;
-        dst[(size_t)(g.off[2] + gc) * kD + t] = x;
-        acc3 += x;
+      for (int r = 0; r < 16; ++r) {
+        x0 += l1s[r][2 * t];
+        x1 += l1s[r][2 * t + 1];
       }
-      __syncthreads();
+      x0 *= inv;
+      x1 *= inv;
+      const size_t o = (size_t)(g.off[2] + gc) * kD + 2 * t;
+      *reinterpret_cast<float2*>(dst + o) = make_float2(x0, x1);
+      if (dsth) *reinterpret_cast<uint32_t*>(dsth + o) = pack_bf16x2(x0, x1);
     }
-    if (c + 1 < chunks_per_wg) cur = nxt;
   }
-  if (g.L >= 3 && t < kD) dst[(size_t)(g.off[3] + wg) * kD + t] = acc3 * inv;
 }
 
-// Level l >= 4 from level l-1: grid.x = rows of level l, grid.y = slice, grid.z = tensor; 64 threads.
+// Level l >= 3 from level l-1: grid.x = rows of level l, grid.y = slice, grid.z = tensor; 64 threads.
 __global__ __launch_bounds__(64) void pool_up(float* __restrict__ pq, float* __restrict__ pk,
-                                              float* __restrict__ pv, Geom g, int level) {
+                                              float* __restrict__ pv, bf16_t* __restrict__ pkh,
+                                              bf16_t* __restrict__ pvh, Geom g, int level) {
   const int tensor = blockIdx.z, slice = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
-  float* base = (tensor == 0 ? pq : tensor == 1 ? pk : pv) + (size_t)slice * g.R * kD;
+  const size_t pbase = (size_t)slice * g.R * kD;
+  float* base = (tensor == 0 ? pq : tensor == 1 ? pk : pv) + pbase;
+  bf16_t* baseh = tensor == 0 ? nullptr : (tensor == 1 ? pkh : pvh);
   const float* src = base + (size_t)(g.off[level - 1] + j * kB) * kD + t;
   float x = 0.f;
 #pragma unroll
   for (int r = 0; r < kB; ++r) x += src[r * kD];
-  base[(size_t)(g.off[level] + j) * kD + t] = x * (1.0f / (float)kB);
+  x *= 1.0f / (float)kB;
+  const size_t o = (size_t)(g.off[level] + j) * kD + t;
+  base[o] = x;
+  if (baseh) baseh[pbase + o] = f32_to_bf16(x);
 }
 
 }  // namespace
 
 hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
-                          float* pk, float* pv, hipStream_t stream) {
-  int chunks, units;
-  if (g.L >= 3) {
-    chunks = 16;
-    units = g.rows[3];
-  } else if (g.L == 2) {
-    chunks = 1;
-    units = g.rows[2];
-  } else {
-    chunks = 1;
-    units = (g.rows[1] + 15) / 16;
-  }
-  dim3 grid(units, g.bh, 3);
+                          float* pk, float* pv, void* pkh, void* pvh, hipStream_t stream) {
+  bf16_t* kh = dtype_bf16 ? static_cast<bf16_t*>(pkh) : nullptr;
+  bf16_t* vh = dtype_bf16 ? static_cast<bf16_t*>(pvh) : nullptr;
+  const dim3 grid((g.rows[1] + 15) / 16, g.bh, 3);
   {
     LaunchTimer timer(kPool, stream);
     if (dtype_bf16)
-      pool_levels123<bf16_t><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pq,
-                                                        pk, pv, g, chunks);
+      pool_levels12<bf16_t><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, pq,
+                                                       pk, pv, kh, vh, g);
     else
-      pool_levels123<float><<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pq, pk,
-                                                       pv, g, chunks);
+      pool_levels12<float><<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, pq, pk,
+                                                      pv, kh, vh, g);
   }
-  for (int l = 4; l <= g.L; ++l) {
+  for (int l = 3; l <= g.L; ++l) {
     LaunchTimer timer(kPool, stream);
-    pool_up<<<dim3(g.rows[l], g.bh, 3), 64, 0, stream>>>(pq, pk, pv, g, l);
+    pool_up<<<dim3(g.rows[l], g.bh, 3), 64, 0, stream>>>(pq, pk, pv, kh, vh, g, l);
   }
   return hipGetLastError();
 }

@@ -53,7 +53,7 @@ _P = ctypes.POINTER(Problem)
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
 
-_lib.llsa_build_pyramid.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.llsa_build_pyramid.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.llsa_select.argtypes = [_P, _vp, _vp, _vp, _vp]
 _lib.llsa_select_exhaustive.argtypes = [_P, _vp, _vp, _vp, _vp]
 _lib.llsa_reorder.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]
@@ -141,9 +141,10 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def build_pyramid(prob, q, k, v, pq, pk, pv, stream=None):
+def build_pyramid(prob, q, k, v, pq, pk, pv, pk_bf16=None, pv_bf16=None, stream=None):
+    """fp32 pyramids pq, pk, pv; for bf16 problems also the bf16 copies of pk, pv (the attention operands)."""
     _check(_lib.llsa_build_pyramid(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(pq), _ptr(pk), _ptr(pv),
-                                   _stream(stream)), "llsa_build_pyramid")
+                                   _ptr(pk_bf16), _ptr(pv_bf16), _stream(stream)), "llsa_build_pyramid")
 
 
 def select(prob, pq, pk, idx, stream=None):
@@ -192,6 +193,13 @@ class Buffers:
         R = pyramid_rows(r)
         shape = (r.batch, r.heads, r.n, r.d)
         self.pq, self.pk, self.pv = (torch.empty((bh, R, r.d), dtype=torch.float32, device=device) for _ in range(3))
+        # pooled K, V in the raw dtype, read by the attention calls (the fp32 pyramids themselves for fp32)
+        if r.dtype == BF16:
+            self.pkb, self.pvb = (torch.empty((bh, R, r.d), dtype=torch.bfloat16, device=device) for _ in range(2))
+            self.pka, self.pva = self.pkb, self.pvb
+        else:
+            self.pkb = self.pvb = None
+            self.pka, self.pva = self.pk, self.pv
         self.idx = torch.empty((bh, R, r.topk), dtype=torch.int32, device=device)
         self.o = torch.empty(shape, dtype=tdt, device=device)
         self.lse = torch.empty((bh, r.n), dtype=torch.float32, device=device)
@@ -202,16 +210,19 @@ class Buffers:
             self.ws_b = torch.empty(max(1, workspace_bytes(r, OP_ATTN_BWD)), dtype=torch.uint8, device=device)
             self.dq, self.dk, self.dv = (torch.empty(shape, dtype=tdt, device=device) for _ in range(3))
 
+    def pyramid(self, q, k, v, stream=None):
+        build_pyramid(self.prob, q, k, v, self.pq, self.pk, self.pv, self.pkb, self.pvb, stream)
+
     def forward(self, q, k, v, stream=None):
         p = self.prob
-        build_pyramid(p, q, k, v, self.pq, self.pk, self.pv, stream)
+        self.pyramid(q, k, v, stream)
         select(p, self.pq, self.pk, self.idx, stream)
-        attn_fwd(p, q, k, v, self.pk, self.pv, self.idx, self.o, self.lse, stream)
+        attn_fwd(p, q, k, v, self.pka, self.pva, self.idx, self.o, self.lse, stream)
 
     def backward(self, q, k, v, dout, stream=None):
         p = self.prob
         index_transpose(p, self.idx, self.col_ptr, self.perm, self.ws_t, stream)
-        attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pk, self.pv, self.idx, self.col_ptr, self.perm,
+        attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pka, self.pva, self.idx, self.col_ptr, self.perm,
                  self.dq, self.dk, self.dv, self.ws_b, stream)
 
 

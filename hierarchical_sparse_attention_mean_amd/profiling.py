@@ -33,7 +33,7 @@ KERNEL_SOURCES = {
     "bwd_dq_bf16": ["attn_bwd.hip"] + _COMMON,
     "bwd_dkdv_bf16": ["attn_bwd.hip"] + _COMMON,
     "coarse_reduce": ["attn_bwd.hip"] + _COMMON,
-    "pool_levels123": ["pyramid.hip", "common.hpp", "launch.hpp"],
+    "pool_levels12": ["pyramid.hip", "common.hpp", "launch.hpp"],
     "select_level": ["select.hip", "common.hpp", "launch.hpp"],
 }
 

@@ -11,7 +11,8 @@
  * Tensors are device pointers into caller-owned memory.  Raw tensors Q, K, V, O, dO, dQ, dK, dV are
  * [batch][heads][n][d], contiguous, d fastest, stored as fp32 or bf16 (llsa_problem.dtype).
  * The pooled pyramid is fp32 [batch*heads][R][d] with R = sum_{l=1..L} n_l and n_l = n / B^l; level l
- * starts at row sum_{l'<l} n_l'.  Selection indices are int32 [batch*heads][R][K] (same row order),
+ * starts at row sum_{l'<l} n_l'.  The attention entry points read the pooled K and V pyramids in the raw
+ * dtype: the fp32 pyramids for fp32 problems, their bf16 copies (same layout) for bf16 problems.  Selection indices are int32 [batch*heads][R][K] (same row order),
  * each row ascending.  The CSC of level l (l = 1..T, T = max(1, L_e)) is col_ptr (n_l + 1 entries,
  * relative to the level) and perm (n_l * K entries, each a CSR position p = u*K + k, ascending within
  * a column); levels are concatenated per batch*head in level order.
@@ -74,9 +75,12 @@ enum { LLSA_OP_INDEX_TRANSPOSE = 1, LLSA_OP_ATTN_BWD = 2 };
  * {Q, K, V}.  Accumulation and storage in fp32.
  *   q, k, v   in : raw tensors (dtype).
  *   pq, pk, pv out: fp32 pyramids [batch*heads][R][d].
+ *   pk_bf16, pv_bf16 out (bf16 problems; ignored and may be NULL for fp32): the pooled K and V pyramids
+ *             rounded to bf16 (round to nearest even), bf16 [batch*heads][R][d] -- the pyramid operands of
+ *             llsa_attn_fwd / llsa_attn_bwd, whose bf16 products round pooled tokens to bf16.
  */
 int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq,
-                       float* pk, float* pv, void* stream);
+                       float* pk, float* pv, void* pk_bf16, void* pv_bf16, void* stream);
 
 /*
  * llsa_select -- hierarchical Top-K [LLSA review, "Core claim"; "What carries the argument";
@@ -122,14 +126,16 @@ int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32
  * raw tokens of every level-1 block in idx row i (logit sigma*q.k) and, for l = 1..L_e, the level-l
  * pooled tokens kept by its level-l ancestor unit i/B^(l-1) (logit sigma*q.k + l*ln B, i.e. weight
  * B^l).  Only the sparse indices are read; no dense mask exists.
- *   q, k, v in : raw tensors (dtype).  pk, pv in: fp32 pyramids.  idx in: from llsa_select.
+ *   q, k, v in : raw tensors (dtype).  idx in: from llsa_select.
+ *   pk, pv  in : pooled K and V pyramids in the raw dtype (fp32: pk, pv of llsa_build_pyramid; bf16: its
+ *                pk_bf16, pv_bf16).
  *   o   out: [batch][heads][n][d] (dtype).
  *   lse out: fp32 [batch*heads][n], natural-log log-sum-exp of each query's logits (for backward).
- * bf16 runs the products on bf16 MFMA with fp32 accumulation (pooled K/V rounded to bf16 for the
- * products, probabilities rounded to bf16 for the PV product); fp32 computes in fp32.
+ * bf16 runs the products on bf16 MFMA with fp32 accumulation (pooled K/V in bf16, probabilities rounded
+ * to bf16 for the PV product); fp32 computes in fp32.
  */
-int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const float* pk,
-                  const float* pv, const int32_t* idx, void* o, float* lse, void* stream);
+int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
+                  const void* pv, const int32_t* idx, void* o, float* lse, void* stream);
 
 /*
  * llsa_index_transpose -- CSR -> CSC of the selection of levels 1..T, T = max(1, L_e) [LLSA review,
@@ -151,13 +157,13 @@ int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* 
  * B^-l.  No gradient flows through the Top-K choice or into pooled queries.  Key-side gradients are
  * gathered per key block through the CSC (no atomics).  bf16 only in this version (LLSA_ERR_DTYPE for
  * fp32).
- *   q, k, v, o, dout in: raw tensors (dtype); lse in: from llsa_attn_fwd; pk, pv, idx: as forward;
+ *   q, k, v, o, dout in: raw tensors (dtype); lse in: from llsa_attn_fwd; pk, pv (bf16), idx: as forward;
  *   col_ptr, perm in: from llsa_index_transpose.
  *   dq, dk, dv out: raw tensors (dtype).
  *   ws scratch of llsa_workspace_bytes(prob, LLSA_OP_ATTN_BWD) bytes (caller-owned).
  */
 int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
-                  const float* lse, const void* dout, const float* pk, const float* pv, const int32_t* idx,
+                  const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
                   const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
                   size_t ws_bytes, void* stream);
 

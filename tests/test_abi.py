@@ -63,7 +63,8 @@ def test_validation_codes(L, kw, code):
     p = L.problem(**base)
     assert L.lib().llsa_resolve(ctypes.byref(p), None) == getattr(L, code)
     # the entry points return the same status and launch nothing
-    assert L.lib().llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None) == getattr(L, code)
+    assert L.lib().llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                                      None) == getattr(L, code)
     assert L.workspace_bytes(p, L.OP_ATTN_BWD) == 0
 
 
@@ -71,7 +72,10 @@ def test_null_and_alignment_checked_before_the_device(L):
     p = L.problem(1, 2, 4096)
     f = L.lib()
     assert f.llsa_attn_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None) == L.ERR_NULL
-    assert f.llsa_build_pyramid(ctypes.byref(p), 16, 32, 48, 64, 80, 88, None) == L.ERR_ALIGN
+    assert f.llsa_build_pyramid(ctypes.byref(p), 16, 32, 48, 64, 80, 88, 96, 112, None) == L.ERR_ALIGN
+    # bf16 problems need the bf16 copies of the pooled K, V pyramids
+    assert f.llsa_build_pyramid(ctypes.byref(p), 16, 32, 48, 64, 80, 96, None, 112, None) == L.ERR_NULL
+    assert f.llsa_build_pyramid(ctypes.byref(p), 16, 32, 48, 64, 80, 96, 112, 8, None) == L.ERR_ALIGN
     assert f.llsa_select(None, 16, 16, 16, None) == L.ERR_NULL
 
 
@@ -92,7 +96,7 @@ def test_workspace_checked_before_the_device(L):
 def test_empty_batch_is_a_no_op(L):
     p = L.problem(0, 4, 4096)
     f = L.lib()
-    assert f.llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None) == L.OK
+    assert f.llsa_build_pyramid(ctypes.byref(p), None, None, None, None, None, None, None, None, None) == L.OK
     assert f.llsa_attn_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None) == L.OK
 
 

@@ -50,7 +50,7 @@ def test_exhaustive_select(L, name, w):
     ref, _ = oracle.select(pq1, pk1, w.n, w.block, 1, w.topk)
     b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels, -1,
                             L.BF16 if w.dtype == "bf16" else L.F32), backward=False)
-    L.build_pyramid(b.prob, dev(x["q"]), dev(x["k"]), dev(x["v"]), b.pq, b.pk, b.pv)
+    b.pyramid(dev(x["q"]), dev(x["k"]), dev(x["v"]))
     idx1 = torch.empty((w.bh, n1, w.topk), dtype=torch.int32, device="cuda")
     L.select_exhaustive(b.prob, b.pq, b.pk, idx1)
     L.select(b.prob, b.pq, b.pk, b.idx)

@@ -54,7 +54,7 @@ def _run_sampled(L, w, samples):
         idx2 = idx.clone()
         idx2[s] = torch.from_numpy(ref["idx"][0]).cuda()
         b.idx.copy_(idx2)
-        L.attn_fwd(b.prob, q, k, v, b.pk, b.pv, b.idx, b.o, b.lse)
+        L.attn_fwd(b.prob, q, k, v, b.pka, b.pva, b.idx, b.o, b.lse)
         b.backward(q, k, v, do)
         torch.cuda.synchronize()
         assert np.array_equal(b.col_ptr[s].cpu().numpy(), ref["col_ptr"][0])
