@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     const int jc = min(j, nblk - 1);
     const int U = su.first + su.stride * (jc >> 2);
     Blk b;
-    b.slice = U / gps;
+    b.slice = uniform(U / gps);
     b.u2 = U - b.slice * gps;
     const int i = 16 * b.u2 + w + 4 * (jc & 3);
     b.valid = i < n1;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   auto unit_end = [&](int ju) {
     if (nhigh == 0) return;
     const int U = su.first + su.stride * ju;
-    const int slice = U / gps, u2 = U - slice * gps;
+    const int slice = uniform(U / gps), u2 = U - slice * gps;
     float* red = reinterpret_cast<float*>(&kts[0][0]);  // [2][32][kD] fp32 = 16 KB
     barrier_lds();
 #pragma unroll

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   // copy the inputs of the wave's j-th block (clamped to the last) into slot p (Q: the single Q slot)
   auto prefetch = [&](int j, int p) {
     const int gb = wb.first + wb.stride * min(j, wb.count - 1);
-    const int slice = gb / g.rows[1], i = gb - slice * g.rows[1];
+    const int slice = uniform(gb / g.rows[1]), i = gb - slice * g.rows[1];
     const bf16_t* qrows = q + slice * slice_elems + (size_t)16 * i * kD;  // 2 KB, contiguous
     lds_dma16(qrows + 8 * lane, &qs[w][0]);
     lds_dma16(qrows + 512 + 8 * lane, &qs[w][512]);
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
       }
     }
   };
-  auto block_slice = [&](int j) { return (wb.first + wb.stride * j) / g.rows[1]; };
+  auto block_slice = [&](int j) { return uniform((wb.first + wb.stride * j) / g.rows[1]); };
 
   // stage s of the block in slot p (slice `slice`), coalesced (see issue_stage_coalesced)
   auto issue = [&](int p, int slice, int s, Stage& st) {
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     }
   };
 
-  const int T = wb.count * nst;
+  const int T = uniform(wb.count * nst);
   Stage A, B;
   issue(0, cslice, 0, A);
   for (int t = 0; t < T; t += 2) {

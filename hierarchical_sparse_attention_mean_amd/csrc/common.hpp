@@ -82,16 +82,37 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Reduce over the four 16-lane groups (lanes c, c+16, c+32, c+48); every lane gets the result.
+// v of lane l ^ 8 (within each 16-lane row): a DPP row rotation by 8 on the VALU.
+__device__ __forceinline__ float xor8_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+}
+
+// Reduce over the four 16-lane groups (lanes c, c+16, c+32, c+48); every lane gets the same result.
+// gfx950's lane swaps stay on the VALU (a shuffle would go through the LDS unit and wait for it):
+// v_permlane32_swap(v, v) returns (v of lanes 0..31, v of lanes 32..63) in both halves, and
+// v_permlane16_swap(v, v) returns the even and the odd 16-lane rows of each half -- so combining the two
+// results combines lane l with lane l^32, then with lane l^16, in the same order in every lane.
+__device__ __forceinline__ void swap32(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float v, float& even, float& odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  even = __uint_as_float(r[0]);
+  odd = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float group_sum(float v) {
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
+  float a, b;
+  swap32(v, a, b);
+  swap16(a + b, a, b);
+  return a + b;
 }
 __device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  v = fmaxf(v, shfl_xor_f(v, 32));
-  return v;
+  float a, b;
+  swap32(v, a, b);
+  swap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs; remap so that consecutive logical ids

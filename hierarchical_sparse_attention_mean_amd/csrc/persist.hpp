@@ -32,13 +32,18 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(
 struct Sweep {
   int first, stride, count;
 };
+// Wave-uniform value in a scalar register.  Integer divisions are expanded on the vector unit, and the
+// compiler then treats their results -- and every loop bound or index derived from them -- as divergent:
+// loops turn into exec-masked loops and per-stage address arithmetic runs on the VALU.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ Sweep xcd_sweep(int n, int r, int per_xcd) {
   const int x = blockIdx.x % 8;
   const int lo = (int)(((int64_t)x * n) / 8), hi = (int)(((int64_t)(x + 1) * n) / 8);
   Sweep sw;
-  sw.first = lo + r;
-  sw.stride = per_xcd;
-  sw.count = r < hi - lo ? (hi - lo - r + per_xcd - 1) / per_xcd : 0;
+  sw.first = uniform(lo + r);
+  sw.stride = uniform(per_xcd);
+  sw.count = uniform(r < hi - lo ? (hi - lo - r + per_xcd - 1) / per_xcd : 0);
   return sw;
 }
 

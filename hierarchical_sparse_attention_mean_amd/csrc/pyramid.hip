@@ -67,12 +67,6 @@ struct ChunkRegs<float> {
   }
 };
 
-// Outputs of one tensor: the fp32 pyramid and, for K and V of bf16 problems, its bf16 copy (else null).
-struct PoolDst {
-  float* f;
-  bf16_t* h;
-};
-
 // grid.x = 256-token chunks per slice, grid.y = slice, grid.z = tensor (0 = Q, 1 = K, 2 = V)
 template <typename T>
 __global__ __launch_bounds__(256) void pool_levels12(const T* __restrict__ q, const T* __restrict__ k,
@@ -96,7 +90,7 @@ __global__ __launch_bounds__(256) void pool_levels12(const T* __restrict__ q, co
   float s[8];
   cur.sum(s);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s[e] += shfl_xor_f(s[e], 8);
+  for (int e = 0; e < 8; ++e) s[e] += xor8_f(s[e]);
   float m[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) m[e] = s[4 * half + e] * inv;

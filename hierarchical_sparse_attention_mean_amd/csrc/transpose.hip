@@ -56,12 +56,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// grid.x = T levels, grid.y = slice; 1024 threads.  cnt[cp_off + 0 .. n_l] (entry 0 is zero, entry
-// j+1 the count of column j) is scanned inclusively into col_ptr, and the cursor of column j
-// (= col_ptr[j]) is left in cnt[cp_off + j].
-__global__ __launch_bounds__(1024) void csc_scan(int32_t* __restrict__ cnt, int32_t* __restrict__ col_ptr, Geom g,
-                                                 CscGeom cg) {
-  __shared__ int wave_tot[16];
+// grid.x = T levels, grid.y = slice; 256 threads, 4 consecutive counters per thread (a small workgroup, so
+// that it can run beside a resident attention kernel).  cnt[cp_off + 0 .. n_l] (entry 0 is zero, entry j+1
+// the count of column j) is scanned inclusively into col_ptr, and the cursor of column j (= col_ptr[j]) is
+// left in cnt[cp_off + j].
+constexpr int kScanThreads = 256, kScanPer = 4;
+__global__ __launch_bounds__(kScanThreads) void csc_scan(int32_t* __restrict__ cnt, int32_t* __restrict__ col_ptr,
+                                                         Geom g, CscGeom cg) {
+  constexpr int kWaves = kScanThreads / 64, kChunk = kScanThreads * kScanPer;
+  __shared__ int wave_tot[kWaves];
   __shared__ int carry_s;
   const int l = blockIdx.x + 1, slice = blockIdx.y;
   const int len = g.rows[l] + 1;
@@ -70,24 +73,33 @@ __global__ __launch_bounds__(1024) void csc_scan(int32_t* __restrict__ cnt, int3
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   if (t == 0) carry_s = 0;
   __syncthreads();
-  for (int base = 0; base < len; base += 1024) {
-    const int x = base + t;
-    const int v = x < len ? a[x] : 0;
-    const int inc = wave_inclusive_scan(v, lane);
+  for (int base = 0; base < len; base += kChunk) {
+    const int x0 = base + kScanPer * t;
+    int v[kScanPer], run = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      v[i] = x0 + i < len ? a[x0 + i] : 0;
+      run += v[i];
+      v[i] = run;  // inclusive within the thread
+    }
+    const int inc = wave_inclusive_scan(run, lane);
     if (lane == 63) wave_tot[w] = inc;
     __syncthreads();
     if (w == 0) {
-      const int tv = lane < 16 ? wave_tot[lane] : 0;
+      const int tv = lane < kWaves ? wave_tot[lane] : 0;
       const int ti = wave_inclusive_scan(tv, lane);
-      if (lane < 16) wave_tot[lane] = ti - tv;  // exclusive prefix of wave totals
+      if (lane < kWaves) wave_tot[lane] = ti - tv;  // exclusive prefix of wave totals
     }
     __syncthreads();
-    const int carry = carry_s;
-    const int out = carry + wave_tot[w] + inc;
-    if (x < len) cp[x] = out;
-    if (x < len - 1) a[x] = out;  // cursor of column x = col_ptr[x]; a[x] was already read into v
+    const int before = carry_s + wave_tot[w] + inc - run;  // exclusive prefix of this thread's first counter
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int x = x0 + i, out = before + v[i];
+      if (x < len) cp[x] = out;
+      if (x < len - 1) a[x] = out;  // cursor of column x = col_ptr[x]; a[x] was already read
+    }
     __syncthreads();
-    if (t == 1023) carry_s = out;
+    if (t == kScanThreads - 1) carry_s = before + run;
     __syncthreads();
   }
 }
@@ -139,7 +151,7 @@ hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_
   }
   {
     LaunchTimer timer(kTranspose, stream);
-    csc_scan<<<dim3(cg.T, g.bh), 1024, 0, stream>>>(ws_cnt, col_ptr, g, cg);
+    csc_scan<<<dim3(cg.T, g.bh), kScanThreads, 0, stream>>>(ws_cnt, col_ptr, g, cg);
   }
   {
     LaunchTimer timer(kTranspose, stream);
