@@ -121,8 +121,12 @@ int launched(hipError_t e) { return e == hipSuccess ? LLSA_OK : LLSA_ERR_LAUNCH;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// transpose workspace: per-column counters (cursors) of every slice and level, then the unordered CSC staging
+size_t transpose_cnt_bytes(const Resolved& r) {
+  return align256((size_t)r.bh * r.cg.cp_len * sizeof(int32_t));
+}
 size_t transpose_ws(const Resolved& r) {
-  return align256((size_t)r.bh * r.cg.cp_len * sizeof(int32_t)) + align256((size_t)r.bh * r.cg.pm_len * sizeof(int32_t));
+  return transpose_cnt_bytes(r) + align256((size_t)r.bh * r.cg.pm_len * sizeof(int32_t));
 }
 
 #define LLSA_TRY(x)          \
@@ -252,7 +256,7 @@ int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* 
   LLSA_TRY(check_ptrs({ws}));
   LLSA_TRY(check_device());
   int32_t* cnt = static_cast<int32_t*>(ws);
-  int32_t* tmp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256((size_t)r.bh * r.cg.cp_len * sizeof(int32_t)));
+  int32_t* tmp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + transpose_cnt_bytes(r));
   return launched(llsa::launch_index_transpose(r.g, r.cg, idx, col_ptr, perm, cnt, tmp, (hipStream_t)stream));
 }
 

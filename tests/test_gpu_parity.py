@@ -127,6 +127,27 @@ def test_transpose_bit_exact(L, name, w, levels, Le):
     assert np.array_equal(b.perm.cpu().numpy(), ref["perm"])
 
 
+@pytest.mark.parametrize("n,K,levels,Le", [(4096, 8, 2, 2), (65536, 8, 3, 3), (4096, 5, 2, 1)])
+def test_transpose_non_hierarchical(L, n, K, levels, Le):
+    """Rows that are not children of their parent's picks (random ascending rows at every level): the
+    hierarchical fill misses entries, raises its flag and the general path must give the oracle's CSC."""
+    rng = np.random.default_rng(7 + n + K)
+    bh = 2
+    R = oracle.pyramid_rows(n, 16, levels)
+    idx = np.empty((bh, R, K), dtype=np.int32)
+    for l in range(1, levels + 1):
+        nl, off = n // 16 ** l, oracle.level_offset(n, 16, l)
+        for b in range(bh):
+            for u in range(nl):
+                idx[b, off + u] = np.sort(rng.choice(nl, size=K, replace=False))
+    cp_ref, pm_ref = oracle.index_transpose(idx, n, 16, levels, K, Le)
+    b = L.Buffers(L.problem(1, bh, n, topk=K, levels=levels, enrich_levels=Le))
+    L.index_transpose(b.prob, torch.from_numpy(idx).cuda(), b.col_ptr, b.perm, b.ws_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.col_ptr.cpu().numpy(), cp_ref)
+    assert np.array_equal(b.perm.cpu().numpy(), pm_ref)
+
+
 @pytest.mark.parametrize("name,w,levels,Le", _backward_cases(), ids=[c[0] for c in _backward_cases()])
 def test_backward_with_oracle_selection(L, name, w, levels, Le):
     x, ex, ref = _prepare(name, w, levels, Le)
