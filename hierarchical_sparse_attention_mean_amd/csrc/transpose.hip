@@ -214,8 +214,10 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ idx, 
     // this lane's candidates r0 + 64 i + lane: the rows' entries, all loads issued before any is used
     int vals[kFillPer][KM];
     int unit[kFillPer];
+    const int nsub = min(kFillPer, (ncand - r0 + 63) / 64);  // sub-chunks of this round that hold candidates
 #pragma unroll
     for (int i = 0; i < kFillPer; ++i) {
+      if (i >= nsub) break;  // uniform
       const int cl = min(r0 + 64 * i + lane, ncand - 1) - r0;  // in-bounds duplicate past the end, never used
       unit[i] = top ? r0 + cl : 16 * __shfl(par, cl >> 4, 64) + (cl & 15);
       const int32_t* row = I + (size_t)unit[i] * K;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ idx, 
     }
 #pragma unroll
     for (int i = 0; i < kFillPer; ++i) {
-      if (r0 + 64 * i >= ncand) break;  // uniform
+      if (i >= nsub) break;  // uniform
       uint32_t mask = 0;  // columns 16J + c this candidate picked (at most one entry each; a row ascends)
       int k0 = 0;
       if (r0 + 64 * i + lane < ncand) {
