@@ -2,7 +2,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input already resident in HBM:
 pyramid -> hierarchical selection -> enriched attention forward -> CSR->CSC transpose -> backward,
-each through the C ABI of libllsa.so on torch's current stream.  The workload is the N = 65536
+each through the C ABI of libllsa.so on torch's current stream, except the transpose, which needs only the
+selection and runs on a second stream beside the forward (the backward waits for it).  The workload is the N = 65536
 forward+backward configuration (batch 1, 16 heads, head dim 64, bf16, B = 16, K = 8, L = 3, smooth
 2-D Gaussian-random-field inputs on a 256x256 grid plus 0.1 noise, dO ~ N(0, 1)).
 
@@ -175,14 +176,11 @@ def main():
     b = llsa.Buffers(llsa.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
     p = b.prob
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority, like every stream here
 
     def step():
-        b.pyramid(q, k, v, stream)
-        llsa.select(p, b.pq, b.pk, b.idx, stream)
-        llsa.attn_fwd(p, q, k, v, b.pka, b.pva, b.idx, b.o, b.lse, stream)
-        llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
-        llsa.attn_bwd(p, q, k, v, b.o, b.lse, do, b.pka, b.pva, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv, b.ws_b,
-                      stream)
+        # pyramid -> selection -> forward, the index transpose on the second stream beside the forward -> backward
+        b.forward_backward(q, k, v, do, stream, side)
 
     for _ in range(args.warmup):
         step()
@@ -270,12 +268,7 @@ def main():
         def step_reordered():
             for a, z in ((q, qr), (k, kr), (v, vr), (do, dr)):
                 llsa.reorder(p, H, W, True, a, z, stream)
-            b.pyramid(qr, kr, vr, stream)
-            llsa.select(p, b.pq, b.pk, b.idx, stream)
-            llsa.attn_fwd(p, qr, kr, vr, b.pka, b.pva, b.idx, b.o, b.lse, stream)
-            llsa.index_transpose(p, b.idx, b.col_ptr, b.perm, b.ws_t, stream)
-            llsa.attn_bwd(p, qr, kr, vr, b.o, b.lse, dr, b.pka, b.pva, b.idx, b.col_ptr, b.perm, b.dq, b.dk, b.dv,
-                          b.ws_b, stream)
+            b.forward_backward(qr, kr, vr, dr, stream, side)
             for a, z in ((b.o, o2), (b.dq, dq2), (b.dk, dk2), (b.dv, dv2)):
                 llsa.reorder(p, H, W, False, a, z, stream)
 

@@ -358,7 +358,10 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
   const int grid = (nb + 3) / 4;
   LaunchTimer timer(kAttnFwd, stream);
   if (dtype_bf16)
-    attn_fwd_bf16<<<persistent_grid((const void*)attn_fwd_bf16, 256, grid), 256, 0, stream>>>(
+    // two thirds of the resident workgroups: as fast as a full load (the gathers are bound by the CU's vector
+    // memory path, not by the number of waves), and it leaves room for a kernel on another stream -- the index
+    // transpose, which needs only the selection, can run beside the forward
+    attn_fwd_bf16<<<max(8, persistent_grid((const void*)attn_fwd_bf16, 256, grid) * 2 / 3 / 8 * 8), 256, 0, stream>>>(
         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx, (bf16_t*)o,
         lse, g);
   else

@@ -225,6 +225,24 @@ class Buffers:
         attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pka, self.pva, self.idx, self.col_ptr, self.perm,
                  self.dq, self.dk, self.dv, self.ws_b, stream)
 
+    def forward_backward(self, q, k, v, dout, stream, side):
+        """The whole chain with the index transpose on the second stream `side`, beside the forward: it needs
+        only the selection, and the backward waits for it (events; both streams at default priority)."""
+        import torch
+        p = self.prob
+        if not hasattr(self, "_ev"):
+            self._ev = (torch.cuda.Event(), torch.cuda.Event())
+        self.pyramid(q, k, v, stream)
+        select(p, self.pq, self.pk, self.idx, stream)
+        self._ev[0].record(stream)
+        side.wait_event(self._ev[0])
+        index_transpose(p, self.idx, self.col_ptr, self.perm, self.ws_t, side)
+        self._ev[1].record(side)
+        attn_fwd(p, q, k, v, self.pka, self.pva, self.idx, self.o, self.lse, stream)
+        stream.wait_event(self._ev[1])
+        attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pka, self.pva, self.idx, self.col_ptr, self.perm,
+                 self.dq, self.dk, self.dv, self.ws_b, stream)
+
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
