@@ -56,6 +56,10 @@ def _load():
     lib.llsa_ref_attn_fwd.restype = None
     lib.llsa_ref_attn_fwd.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _i32, _dbl,
                                       _pd, _pd, _pd, _pd, _pd, _pi, _pd, _pd]
+    lib.llsa_ref_attn_fwd_complement.restype = None
+    lib.llsa_ref_attn_fwd_complement.argtypes = lib.llsa_ref_attn_fwd.argtypes
+    lib.llsa_ref_entry_weight.restype = _i32
+    lib.llsa_ref_entry_weight.argtypes = [_i64, _i32, _i32, _i32, _i32, _pi, _i64, _i32, ctypes.POINTER(ctypes.c_double)]
     lib.llsa_ref_index_transpose.restype = None
     lib.llsa_ref_index_transpose.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _pi, _pi, _pi]
     lib.llsa_ref_attn_bwd.restype = None
@@ -122,16 +126,27 @@ def select(pq: np.ndarray, pk: np.ndarray, n: int, block: int, levels: int, topk
     return idx, int(pairs)
 
 
-def attn_fwd(q, k, v, pk, pv, idx, block, levels, topk, enrich_levels, scale):
-    """Enriched sparse attention forward.  Returns (o [bh, n, d], lse [bh, n])."""
+def attn_fwd(q, k, v, pk, pv, idx, block, levels, topk, enrich_levels, scale, complement: bool = False):
+    """Enriched sparse attention forward.  Returns (o [bh, n, d], lse [bh, n]).  complement=True takes the
+    complement-partition reading of the enrichment (the unkept candidates of every level)."""
     q, k, v, pk, pv = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, pk, pv))
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     bh, n, d = q.shape
     o = np.empty_like(q)
     lse = np.empty((bh, n), np.float64)
-    _load().llsa_ref_attn_fwd(bh, n, d, block, levels, topk, enrich_levels, scale,
-                              _d(q), _d(k), _d(v), _d(pk), _d(pv), _i(idx), _d(o), _d(lse))
+    fn = _load().llsa_ref_attn_fwd_complement if complement else _load().llsa_ref_attn_fwd
+    fn(bh, n, d, block, levels, topk, enrich_levels, scale,
+       _d(q), _d(k), _d(v), _d(pk), _d(pv), _i(idx), _d(o), _d(lse))
     return o, lse
+
+
+def entry_weight(idx_slice, n, block, levels, topk, enrich_levels, query, complement):
+    """(number of entries, sum of their weights B^level) of one query of one slice's selection."""
+    idx_slice = np.ascontiguousarray(idx_slice, dtype=np.int32)
+    w = ctypes.c_double()
+    ne = _load().llsa_ref_entry_weight(n, block, levels, topk, enrich_levels, _i(idx_slice), query,
+                                       int(bool(complement)), ctypes.byref(w))
+    return int(ne), w.value
 
 
 def transposed_levels(levels: int, enrich_levels: int) -> int:

@@ -256,15 +256,76 @@ static int build_entries(int64_t n, int B, int L, int K, int Le, const int32_t* 
 static int max_entries(int B, int L, int K, int Le) { return K * B + K * (Le > L ? L : Le); }
 
 /* ------------------------------------------------------------------------------------------------ */
+/* The complement-partition reading of enrichment (called E2 in the design notes): the page says the */
+/* enrichment appends the *selected* coarse tokens (E1 above), but its O(K log N) accounting also    */
+/* fits the set of candidates each level scored and did not keep.  E(n): the fine tokens of the kept */
+/* level-1 blocks (bias 0), then for l = 1..Le the level-l blocks that the query's level-l unit      */
+/* scored but did not keep -- the B children of the parent unit's picks, or every block at the      */
+/* coarsest level -- as pooled tokens with bias l*ln B (weight B^l).  With Le = L every raw key is   */
+/* represented exactly once: as itself, or through its finest ancestor that was scored and not kept. */
+/* [LLSA review, "Core claim" (enrichment, weights B^l); "What carries the argument"]               */
+/* ------------------------------------------------------------------------------------------------ */
+static int build_entries_complement(int64_t n, int B, int L, int K, int Le, const int32_t* I, int64_t query,
+                                    entry_t* E) {
+  int ne = 0;
+  const int64_t i = query / B; /* fine query block = level-1 unit */
+  const int k1 = level_k(n, B, 1, K);
+  const int64_t off1 = level_off(n, B, 1);
+  for (int k = 0; k < k1; ++k) {
+    const int64_t c = I[(off1 + i) * K + k];
+    for (int t = 0; t < B; ++t) {
+      E[ne].level = 0;
+      E[ne].row = c * B + t;
+      E[ne].bias = 0.0;
+      ++ne;
+    }
+  }
+  for (int l = 1; l <= Le && l <= L; ++l) {
+    const int64_t a = i / ipow(B, l - 1); /* level-l unit containing fine block i */
+    const int64_t offl = level_off(n, B, l);
+    const int kl = level_k(n, B, l, K);
+    const int32_t* picks = I + (offl + a) * K;
+    /* the unit's candidates, in the order they were scored */
+    int64_t ncand;
+    const int32_t* parent_picks = NULL;
+    int kp = 0;
+    if (l == L) {
+      ncand = level_rows(n, B, L);
+    } else {
+      kp = level_k(n, B, l + 1, K);
+      parent_picks = I + (level_off(n, B, l + 1) + a / B) * K;
+      ncand = (int64_t)kp * B;
+    }
+    for (int64_t x = 0; x < ncand; ++x) {
+      const int64_t c = l == L ? x : (int64_t)parent_picks[x / B] * B + x % B;
+      int kept = 0;
+      for (int k = 0; k < kl; ++k) kept |= picks[k] == c;
+      if (kept) continue;
+      E[ne].level = l;
+      E[ne].row = c;
+      E[ne].bias = (double)l * log((double)B);
+      ++ne;
+    }
+  }
+  return ne;
+}
+
+static int max_entries_complement(int64_t n, int B, int L, int K, int Le) {
+  int64_t m = (int64_t)K * B;
+  for (int l = 1; l <= Le && l <= L; ++l) m += l == L ? level_rows(n, B, L) : (int64_t)K * B;
+  return (int)m;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
 /* O4 -- enriched sparse attention forward: z_e = sigma * q.k_e + bias_e; lse = ln sum exp z;        */
 /* O = sum_e exp(z_e - lse) v_e.                                                                     */
 /* [LLSA review, "Core claim"; "What carries the argument"; abstract (sparse indices, no dense mask)] */
 /* ------------------------------------------------------------------------------------------------ */
-void llsa_ref_attn_fwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
-                       const double* q, const double* k, const double* v, const double* pk,
-                       const double* pv, const int32_t* idx, double* o, double* lse) {
+static void attn_fwd_entries(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                             const double* q, const double* k, const double* v, const double* pk,
+                             const double* pv, const int32_t* idx, double* o, double* lse, int complement) {
   const int64_t R = llsa_ref_pyramid_rows(n, B, L);
-  const int me = max_entries(B, L, K, Le);
+  const int me = complement ? max_entries_complement(n, B, L, K, Le) : max_entries(B, L, K, Le);
 #pragma omp parallel
   {
     entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
@@ -274,7 +335,8 @@ void llsa_ref_attn_fwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
       const int64_t s = sq / n, qi = sq % n;
       const double* qv = q + (s * n + qi) * d;
       const int32_t* I = idx + s * R * K;
-      const int ne = build_entries(n, B, L, K, Le, I, qi, E);
+      const int ne = complement ? build_entries_complement(n, B, L, K, Le, I, qi, E)
+                                : build_entries(n, B, L, K, Le, I, qi, E);
       double zmax = -INFINITY;
       for (int e = 0; e < ne; ++e) {
         const double* kv = E[e].level == 0 ? k + (s * n + E[e].row) * d
@@ -300,6 +362,35 @@ void llsa_ref_attn_fwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
     free(E);
     free(z);
   }
+}
+
+void llsa_ref_attn_fwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                       const double* q, const double* k, const double* v, const double* pk,
+                       const double* pv, const int32_t* idx, double* o, double* lse) {
+  attn_fwd_entries(bh, n, d, B, L, K, Le, sigma, q, k, v, pk, pv, idx, o, lse, 0);
+}
+
+/* The forward over the complement-partition entry set (build_entries_complement). */
+void llsa_ref_attn_fwd_complement(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                                  const double* q, const double* k, const double* v, const double* pk,
+                                  const double* pv, const int32_t* idx, double* o, double* lse) {
+  attn_fwd_entries(bh, n, d, B, L, K, Le, sigma, q, k, v, pk, pv, idx, o, lse, 1);
+}
+
+/* Number of entries of query `query` of slice 0 under either reading, and the sum of their weights
+ * (1 per raw token, B^l per level-l pooled token): with the complement reading and Le = L the weights add
+ * up to n. */
+int llsa_ref_entry_weight(int64_t n, int B, int L, int K, int Le, const int32_t* idx, int64_t query,
+                          int complement, double* weight) {
+  const int me = complement ? max_entries_complement(n, B, L, K, Le) : max_entries(B, L, K, Le);
+  entry_t* E = (entry_t*)malloc(sizeof(entry_t) * (size_t)me);
+  const int ne = complement ? build_entries_complement(n, B, L, K, Le, idx, query, E)
+                            : build_entries(n, B, L, K, Le, idx, query, E);
+  double w = 0.0;
+  for (int e = 0; e < ne; ++e) w += (double)ipow(B, E[e].level);
+  *weight = w;
+  free(E);
+  return ne;
 }
 
 /* ------------------------------------------------------------------------------------------------ */
