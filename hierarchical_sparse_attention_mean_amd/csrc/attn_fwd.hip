@@ -102,26 +102,34 @@ struct Softmax {
 // block's Q rows, selection row and enrichment entries are copied into a second set of LDS buffers a whole
 // block ahead, with DMA loads that hold no registers.  So the latency chain index -> gather -> product of
 // one block hides behind the work of the previous one.
+// kMaxC: enrichment entries per fine block the LDS holds; kComp: the complement reading (entries from the
+// complement lists `esrc`, laid out by `cm`) instead of the selected tokens (entries from the selection `idx`).
+template <int kMaxC, bool kComp>
 __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ pk,
                                                      const bf16_t* __restrict__ pv, const int32_t* __restrict__ idx,
-                                                     bf16_t* __restrict__ o, float* __restrict__ lse, Geom g) {
+                                                     const int32_t* __restrict__ esrc, bf16_t* __restrict__ o,
+                                                     float* __restrict__ lse, Geom g, CompGeom cm) {
   __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];      // V tile (read transposed)
   __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];      // K tile (read as MFMA A operand)
   __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];       // Q rows of the next block
   __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row, two slots
-  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
-  __shared__ __attribute__((aligned(16))) EntryTab tab;                // per-entry constants (shared)
+  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxC];         // enrichment entries' block indices
+  __shared__ __attribute__((aligned(16))) EntryTabT<kMaxC> tab;        // per-entry constants (shared)
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  fill_entry_tab(g, tab);
+  if (kComp)
+    fill_entry_tab_complement(g, cm, tab);
+  else
+    fill_entry_tab(g, tab);
   const Sweep wb = xcd_sweep(g.bh * g.rows[1], 4 * (blockIdx.x / 8) + w, 4 * (gridDim.x / 8));
   if (wb.count == 0) return;  // no workgroup barrier is used below
   bf16_t* vt = vs[w];
   bf16_t* kt = ks[w];
-  const Plan plan = make_plan(g);
+  const Plan plan = make_plan(g, kComp ? cm.total : g.K * g.Le);
   const int nst = plan.nstages;
   const size_t slice_elems = (size_t)g.n * kD, slice_rows = (size_t)g.R * kD;
+  const size_t esrc_slice = kComp ? (size_t)cm.slice : (size_t)g.R * g.K;
   const float sl2 = g.scale_log2;
 
   // copy the inputs of the wave's j-th block (clamped to the last) into slot p (Q: the single Q slot)
@@ -133,11 +141,12 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     lds_dma16(qrows + 512 + 8 * lane, &qs[w][512]);
     const int32_t* I = idx + (size_t)slice * g.R * g.K;
     if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + i) * g.K + lane, &is1[w][p][0]);
+    const int32_t* E = esrc + slice * esrc_slice;
 #pragma unroll
-    for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
+    for (int jj = 0; jj < kMaxC / 64; ++jj) {
       if (64 * jj < plan.ncoarse) {
         const int e = min(lane + 64 * jj, plan.ncoarse - 1);
-        lds_dma4(I + tab.pos0[e] + (i >> tab.shift[e]) * g.K, &es[w][p][64 * jj]);
+        lds_dma4(E + tab.pos0[e] + (i >> tab.shift[e]) * tab.stride[e], &es[w][p][64 * jj]);
       }
     }
   };
@@ -357,16 +366,30 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
   const int nb = g.bh * g.rows[1];
   const int grid = (nb + 3) / 4;
   LaunchTimer timer(kAttnFwd, stream);
-  if (dtype_bf16)
+  if (dtype_bf16) {
     // two thirds of the resident workgroups: as fast as a full load (the gathers are bound by the CU's vector
     // memory path, not by the number of waves), and it leaves room for a kernel on another stream -- the index
     // transpose, which needs only the selection, can run beside the forward
-    attn_fwd_bf16<<<max(8, persistent_grid((const void*)attn_fwd_bf16, 256, grid) * 2 / 3 / 8 * 8), 256, 0, stream>>>(
-        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx, (bf16_t*)o,
-        lse, g);
-  else
+    auto kernel = attn_fwd_bf16<kMaxCoarse, false>;
+    kernel<<<max(8, persistent_grid((const void*)kernel, 256, grid) * 2 / 3 / 8 * 8), 256, 0, stream>>>(
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx, idx,
+        (bf16_t*)o, lse, g, CompGeom{});
+  } else {
     attn_fwd_f32<<<grid, 256, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, (const float*)pk,
                                            (const float*)pv, idx, (float*)o, lse, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_complement(const Geom& g, const CompGeom& cm, const void* q, const void* k,
+                                      const void* v, const void* pk, const void* pv, const int32_t* idx,
+                                      const int32_t* comp, void* o, float* lse, hipStream_t stream) {
+  const int nb = g.bh * g.rows[1];
+  LaunchTimer timer(kAttnFwd, stream);
+  auto kernel = attn_fwd_bf16<kMaxComplement, true>;
+  kernel<<<persistent_grid((const void*)kernel, 256, (nb + 3) / 4), 256, 0, stream>>>(
+      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx, comp,
+      (bf16_t*)o, lse, g, cm);
   return hipGetLastError();
 }
 

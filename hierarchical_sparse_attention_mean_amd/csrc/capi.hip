@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "entries.hpp"
 #include "launch.hpp"
 #include "llsa.h"
 
@@ -129,6 +130,24 @@ size_t transpose_ws(const Resolved& r) {
   return transpose_cnt_bytes(r) + align256((size_t)r.bh * r.cg.pm_len * sizeof(int32_t));
 }
 
+// Complement lists: level l = 1..L_e, m_l = (B-1) K candidates scored and not kept per unit (n_L - K at the
+// coarsest level), n_l units.
+llsa::CompGeom comp_geom(const Resolved& r) {
+  llsa::CompGeom cm;
+  memset(&cm, 0, sizeof(cm));
+  const llsa::Geom& g = r.g;
+  int off = 0;
+  for (int l = 1; l <= g.Le; ++l) {
+    cm.m[l] = l == g.L ? g.rows[l] - g.K : (llsa::kB - 1) * g.K;
+    cm.off[l] = off;
+    off += g.rows[l] * cm.m[l];
+    cm.total += cm.m[l];
+  }
+  cm.slice = off;
+  return cm;
+}
+size_t complement_ws(const Resolved& r) { return align256((size_t)r.bh * comp_geom(r).slice * sizeof(int32_t)); }
+
 #define LLSA_TRY(x)          \
   do {                       \
     const int _s = (x);      \
@@ -169,6 +188,7 @@ size_t llsa_workspace_bytes(const llsa_problem* prob, int op) {
   if (resolve(prob, &r) != LLSA_OK) return 0;
   if (op == LLSA_OP_INDEX_TRANSPOSE) return transpose_ws(r);
   if (op == LLSA_OP_ATTN_BWD) return llsa::bwd_ws_layout(r.g, nullptr, nullptr);
+  if (op == LLSA_OP_ATTN_FWD_COMPLEMENT) return complement_ws(r);
   return 0;
 }
 
@@ -243,6 +263,27 @@ int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const 
   LLSA_TRY(check_device());
   return launched(
       llsa::launch_attn_fwd(r.g, r.p.dtype == LLSA_BF16, q, k, v, pk, pv, idx, o, lse, (hipStream_t)stream));
+}
+
+int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
+                             const void* pv, const int32_t* idx, void* o, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
+  const llsa::CompGeom cm = comp_geom(r);
+  if (cm.total > llsa::kMaxComplement) return LLSA_ERR_UNSUPPORTED;
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({q, k, v, pk, pv, idx, o, lse}));
+  const size_t need = complement_ws(r);
+  if (need > 0 && (!ws || ws_bytes < need)) return LLSA_ERR_WORKSPACE;
+  if (need > 0) LLSA_TRY(check_ptrs({ws}));
+  LLSA_TRY(check_device());
+  int32_t* comp = static_cast<int32_t*>(ws);
+  hipError_t e = llsa::launch_complement_lists(r.g, cm, idx, comp, (hipStream_t)stream);
+  if (e != hipSuccess) return LLSA_ERR_LAUNCH;
+  return launched(llsa::launch_attn_fwd_complement(r.g, cm, q, k, v, pk, pv, idx, comp ? comp : idx, o, lse,
+                                                   (hipStream_t)stream));
 }
 
 int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm, void* ws,

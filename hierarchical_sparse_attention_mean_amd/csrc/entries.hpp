@@ -61,35 +61,43 @@ struct Plan {
   int nstages;   // nfine + ceil(ncoarse / 32)
 };
 
-__device__ __forceinline__ Plan make_plan(const Geom& g) {
+__device__ __forceinline__ Plan make_plan(const Geom& g, int ncoarse) {
   Plan p;
   p.nfine = (g.K + 1) / 2;
-  p.ncoarse = g.K * g.Le;
+  p.ncoarse = ncoarse;
   p.nstages = p.nfine + (p.ncoarse + 31) / 32;
   return p;
 }
+__device__ __forceinline__ Plan make_plan(const Geom& g) { return make_plan(g, g.K * g.Le); }
 
-constexpr int kMaxCoarse = 128;  // K * L_e enrichment entries per fine block (a limit of the GPU path)
+constexpr int kMaxCoarse = 128;      // K * L_e selected enrichment entries per fine block (a GPU-path limit)
+constexpr int kMaxComplement = 576;  // entries of the complement reading per fine block (a GPU-path limit)
 
 // Per-entry constants of the enrichment list -- the same for every fine block, so a workgroup computes them
-// once (fill_entry_tab) and the stage loop reads them from LDS instead of re-deriving level and offsets:
+// once (fill_entry_tab*) and the stage loop reads them from LDS instead of re-deriving level and offsets:
 //   row0[e]  first pyramid row of entry e's level;
-//   pos0[e], shift[e]  the entry's position in the slice's selection array for fine block i is
-//            pos0[e] + (i >> shift[e]) * K  (its ancestor unit of level l is i / B^(l-1));
+//   pos0[e], shift[e], stride[e]  the position of the entry's block index in its source array (the
+//            selection, or the complement lists) for fine block i is pos0[e] + (i >> shift[e]) * stride[e]
+//            (its ancestor unit of level l is i / B^(l-1));
 //   bias[e]  the logit bias l * log2(B) = 4l in the log2 domain, -inf past the end of the list (up to 31
 //            padding entries), so that the padded rows of a stage get probability exactly 0.
 // Entries past the end repeat the last entry's row and position (in-bounds duplicates).
-struct EntryTab {
-  int row0[kMaxCoarse];
-  int pos0[kMaxCoarse];
-  int shift[kMaxCoarse];
-  float bias[kMaxCoarse];
+template <int kN>
+struct EntryTabT {
+  int row0[kN];
+  int pos0[kN];
+  int shift[kN];
+  int stride[kN];
+  float bias[kN];
 };
+using EntryTab = EntryTabT<kMaxCoarse>;
 
-// All threads of the workgroup take part; ends with a workgroup barrier.
-__device__ __forceinline__ void fill_entry_tab(const Geom& g, EntryTab& t) {
+// Selected-token reading: entry e is slot s of level l's row of the ancestor (levels 2..L_e first, then level
+// 1).  All threads of the workgroup take part; ends with a workgroup barrier.
+template <int kN>
+__device__ __forceinline__ void fill_entry_tab(const Geom& g, EntryTabT<kN>& t) {
   const int ncoarse = g.K * g.Le;
-  for (int e = threadIdx.x; e < kMaxCoarse; e += blockDim.x) {
+  for (int e = threadIdx.x; e < kN; e += blockDim.x) {
     const int ec = min(e, max(ncoarse - 1, 0));
     int l, slot;
     coarse_entry(g, ec, &l, &slot);
@@ -97,7 +105,33 @@ __device__ __forceinline__ void fill_entry_tab(const Geom& g, EntryTab& t) {
     t.row0[e] = off;
     t.pos0[e] = off * g.K + slot;
     t.shift[e] = 4 * (l - 1);
+    t.stride[e] = g.K;
     t.bias[e] = e < ncoarse ? 4.0f * (float)l : -INFINITY;
+  }
+  __syncthreads();
+}
+
+// Layout of the complement lists (one slice): level l = 1..L_e holds, for each of its n_l units, the m_l
+// candidates the unit scored and did not keep, at off[l] + unit * m_l.
+struct CompGeom {
+  int total;                 // sum_l m_l: entries per fine block
+  int slice;                 // ints per slice
+  int m[kMaxLevels + 1];     // m_l
+  int off[kMaxLevels + 1];   // first int of level l
+};
+
+// Complement reading: entry e is item x of level l's list of the ancestor, levels 1..L_e in order.
+template <int kN>
+__device__ __forceinline__ void fill_entry_tab_complement(const Geom& g, const CompGeom& cm, EntryTabT<kN>& t) {
+  for (int e = threadIdx.x; e < kN; e += blockDim.x) {
+    const int ec = min(e, max(cm.total - 1, 0));
+    int l = 1, start = 0;
+    while (l < g.Le && ec >= start + cm.m[l]) start += cm.m[l++];
+    t.row0[e] = level_off(g, l);
+    t.pos0[e] = cm.off[l] + (ec - start);
+    t.shift[e] = 4 * (l - 1);
+    t.stride[e] = cm.m[l];
+    t.bias[e] = e < cm.total ? 4.0f * (float)l : -INFINITY;
   }
   __syncthreads();
 }

@@ -9,7 +9,8 @@
 namespace llsa {
 
 // Kernel-family ids (same values as LLSA_KERNEL_* in llsa.h).
-enum KernelFamily { kPool = 0, kSelect, kAttnFwd, kTranspose, kBwdDq, kBwdReduce, kBwdDkdv, kSelectExhaustive, kReorder, kFamilies };
+enum KernelFamily { kPool = 0, kSelect, kAttnFwd, kTranspose, kBwdDq, kBwdReduce, kBwdDkdv, kSelectExhaustive, kReorder,
+                    kComplement, kFamilies };
 
 // Brackets one kernel launch with hipEvents on its stream while timing is enabled (llsa_timing_enable).
 class LaunchTimer {
@@ -50,6 +51,12 @@ hipError_t launch_select_exhaustive(const Geom& g, const float* pq, const float*
 hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v,
                            const void* pk, const void* pv, const int32_t* idx, void* o, float* lse,
                            hipStream_t stream);
+struct CompGeom;
+hipError_t launch_complement_lists(const Geom& g, const CompGeom& cm, const int32_t* idx, int32_t* comp,
+                                   hipStream_t stream);
+hipError_t launch_attn_fwd_complement(const Geom& g, const CompGeom& cm, const void* q, const void* k,
+                                      const void* v, const void* pk, const void* pv, const int32_t* idx,
+                                      const int32_t* comp, void* o, float* lse, hipStream_t stream);
 hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_t* idx, int32_t* col_ptr,
                                   int32_t* perm, int32_t* ws_cnt, int32_t* ws_tmp, hipStream_t stream);
 

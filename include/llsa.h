@@ -67,7 +67,7 @@ typedef struct {
 } llsa_problem;
 
 /* Operation ids for llsa_workspace_bytes. */
-enum { LLSA_OP_INDEX_TRANSPOSE = 1, LLSA_OP_ATTN_BWD = 2 };
+enum { LLSA_OP_INDEX_TRANSPOSE = 1, LLSA_OP_ATTN_BWD = 2, LLSA_OP_ATTN_FWD_COMPLEMENT = 3 };
 
 /*
  * llsa_build_pyramid -- hierarchical compression [LLSA review, "Core claim"; "What carries the
@@ -138,6 +138,25 @@ int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const 
                   const void* pv, const int32_t* idx, void* o, float* lse, void* stream);
 
 /*
+ * llsa_attn_fwd_complement -- the forward under the complement-partition reading of the enrichment, the
+ * alternative the pages leave open [LLSA review, "Core claim" (enrichment appends coarse tokens, weight
+ * B^l) and "What carries the argument" (O(K log N) tokens per query)]: raw query t in fine block i attends
+ * the B raw tokens of every level-1 block in idx row i and, for l = 1..L_e, the level-l pooled tokens of the
+ * blocks its level-l ancestor unit i/B^(l-1) scored but did not keep -- the B children of each block kept by
+ * the unit's parent, or every block at the coarsest level -- with logit sigma*q.k + l*ln B.  With L_e = L
+ * every raw key enters exactly once, as itself or through its finest scored-and-unkept ancestor.
+ *   q, k, v, pk, pv, idx, o, lse: as llsa_attn_fwd (bf16 only: LLSA_ERR_DTYPE for fp32).
+ *   idx must come from llsa_select (a hierarchical selection).
+ *   ws scratch of llsa_workspace_bytes(prob, LLSA_OP_ATTN_FWD_COMPLEMENT) bytes (caller-owned): the
+ *      complement lists, int32.
+ * Limit: at most 576 entries per fine block, sum_{l<L} (B-1) K + (n_L - K) over l <= L_e
+ * (LLSA_ERR_UNSUPPORTED otherwise); N = 262144, K = 16, L = 3 has 528.
+ */
+int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v,
+                             const void* pk, const void* pv, const int32_t* idx, void* o, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * llsa_index_transpose -- CSR -> CSC of the selection of levels 1..T, T = max(1, L_e) [LLSA review,
  * "What carries the argument": a CSR-to-CSC scan gives each key block its query blocks without a
  * dense N x N mask].  Column j of level l lists the CSR positions p = u*K + k with idx = j, ascending.
@@ -189,13 +208,14 @@ enum {
   LLSA_KERNEL_POOL = 0,       /* pyramid pooling                                   */
   LLSA_KERNEL_SELECT = 1,     /* hierarchical Top-K, one launch per level          */
   LLSA_KERNEL_ATTN_FWD = 2,   /* enriched attention forward                        */
-  LLSA_KERNEL_TRANSPOSE = 3,  /* CSR -> CSC: zero, count, scan, scatter, order     */
+  LLSA_KERNEL_TRANSPOSE = 3,  /* CSR -> CSC: counts and scan, fill (or scatter, order) */
   LLSA_KERNEL_BWD_DQ = 4,     /* backward: dQ, Delta, pooled-token partials        */
   LLSA_KERNEL_BWD_REDUCE = 5, /* backward: pooled-token gradient reduction         */
   LLSA_KERNEL_BWD_DKDV = 6,   /* backward: dK, dV through the CSC                  */
   LLSA_KERNEL_SELECT_EXHAUSTIVE = 7, /* single-level exhaustive Top-K (not on the hot path) */
   LLSA_KERNEL_REORDER = 8,    /* 2-D-local index reordering                        */
-  LLSA_KERNEL_COUNT = 9
+  LLSA_KERNEL_COMPLEMENT = 9, /* complement lists of the complement reading        */
+  LLSA_KERNEL_COUNT = 10
 };
 /* While enabled, every kernel this library launches is bracketed by two hipEvents recorded on its
  * launch stream (process-wide switch; off by default).  Enabling clears earlier records.  The events

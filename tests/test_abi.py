@@ -25,7 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol(L):
     names = _declared()
     assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_select_exhaustive", "llsa_reorder"} <= set(names)
+            "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd_complement"} <= set(names)
     for n in names:
         assert hasattr(L.lib(), n), n
 
@@ -91,6 +91,24 @@ def test_workspace_checked_before_the_device(L):
     assert f.llsa_attn_bwd(ctypes.byref(p), *args, 64, nb - 1, None) == L.ERR_WORKSPACE
     pf = L.problem(1, 2, 4096, dtype=L.F32)
     assert f.llsa_attn_bwd(ctypes.byref(pf), *args, 64, nb, None) == L.ERR_DTYPE
+
+
+def test_complement_forward_host_checks(L):
+    f = L.lib()
+    p = L.problem(1, 2, 65536)  # K = 8, L = 3: 120 + 120 + 8 = 248 entries per fine block
+    need = L.workspace_bytes(p, L.OP_ATTN_FWD_COMPLEMENT)
+    ints = 4096 * 120 + 256 * 120 + 16 * 8
+    assert need == -(-2 * ints * 4 // 256) * 256
+    args = [16] * 8
+    assert f.llsa_attn_fwd_complement(ctypes.byref(p), *args, 64, need - 1, None) == L.ERR_WORKSPACE
+    assert f.llsa_attn_fwd_complement(ctypes.byref(p), *args, None, need, None) == L.ERR_WORKSPACE
+    assert f.llsa_attn_fwd_complement(ctypes.byref(p), *([None] * 8), 64, need, None) == L.ERR_NULL
+    pf = L.problem(1, 2, 65536, dtype=L.F32)
+    assert f.llsa_attn_fwd_complement(ctypes.byref(pf), *args, 64, need, None) == L.ERR_DTYPE
+    big = L.problem(1, 1, 65536, topk=32, levels=2)  # 480 + 224 = 704 > 576
+    assert f.llsa_attn_fwd_complement(ctypes.byref(big), *args, 64, 1 << 30, None) == L.ERR_UNSUPPORTED
+    empty = L.problem(0, 4, 65536)
+    assert f.llsa_attn_fwd_complement(ctypes.byref(empty), *([None] * 8), None, 0, None) == L.OK
 
 
 def test_empty_batch_is_a_no_op(L):
