@@ -78,6 +78,20 @@ def algorithmic(w, levels, enrich):
     return out
 
 
+def complement_algorithmic(w, levels, enrich):
+    """Complement-partition reading of the enrichment: entries per fine block, list ints per slice, and the
+    algorithmic bytes / flops of the list kernel and of its forward (each tensor counted once)."""
+    bh, n, d, B, K = w.bh, w.n, w.d, w.block, w.topk
+    rows = [n // B ** l for l in range(1, levels + 1)]
+    m = [rows[-1] - K if l == levels else (B - 1) * K for l in range(1, enrich + 1)]
+    total, ints = sum(m), sum(rows[l - 1] * m[l - 1] for l in range(1, enrich + 1))
+    tokens, R = bh * n, sum(rows)
+    lists = dict(bytes=bh * (R * K * 4 + ints * 4), flops=0.0)
+    fwd = dict(bytes=tokens * (4 * d * 2 + 4) + 2 * bh * R * d * 2 + bh * ints * 4,
+               flops=4.0 * d * (K * B + total) * tokens)
+    return total, ints, lists, fwd
+
+
 def oracle_baseline(w, x, budget_s=20.0):
     """Oracle chain timed on whole (batch, head) slices until ~budget_s of CPU work; scaled to one step."""
     import oracle
@@ -151,6 +165,8 @@ def main():
                     help="also time the single-level exhaustive Top-K and report the hierarchy's routing recall")
     ap.add_argument("--dense", action="store_true",
                     help="also time dense PyTorch SDPA (flash / memory-efficient backend) at the same shapes")
+    ap.add_argument("--complement", action="store_true",
+                    help="also time the forward under the complement-partition reading of the enrichment")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of COPY_PROBE_BYTES after the warm-up (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE; see hierarchical_sparse_attention_mean_amd/profiling.py)")
@@ -296,6 +312,30 @@ def main():
                      "reorder_ms_per_step": round(fam_r["reorder"][0] / args.steps, 4),
                      "kernels_ms_per_step": {nm: round(tc[0] / args.steps, 4) for nm, tc in fam_r.items() if tc[1]}}
 
+    complement = None
+    if args.complement:
+        total, ints, a_lists, a_fwd = complement_algorithmic(w, p.levels, p.enrich_levels)
+        ws_c = torch.empty(max(1, llsa.workspace_bytes(p, llsa.OP_ATTN_FWD_COMPLEMENT)), dtype=torch.uint8,
+                           device="cuda")
+        o_c, lse_c = torch.empty_like(b.o), torch.empty_like(b.lse)
+        for _ in range(2):
+            llsa.attn_fwd_complement(p, q, k, v, b.pka, b.pva, b.idx, o_c, lse_c, ws_c, stream)
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 2)
+        llsa.timing_enable(True)
+        for _ in range(reps):
+            llsa.attn_fwd_complement(p, q, k, v, b.pka, b.pva, b.idx, o_c, lse_c, ws_c, stream)
+        torch.cuda.synchronize()
+        fam_c = llsa.timing_read()
+        llsa.timing_enable(False)
+        lists_ms, fwd_ms = fam_c["complement"][0] / reps, fam_c["attn_fwd"][0] / reps
+        complement = {"entries_per_fine_block": total, "selected_entries_per_fine_block": p.topk * p.enrich_levels,
+                      "lists_ms": round(lists_ms, 4), "attn_fwd_ms": round(fwd_ms, 4),
+                      "attn_fwd_alg_GBps": round(a_fwd["bytes"] / (fwd_ms * 1e-3) / 1e9, 1),
+                      "attn_fwd_alg_TFLOPs": round(a_fwd["flops"] / (fwd_ms * 1e-3) / 1e12, 2),
+                      "selected_reading_attn_fwd_ms": kernels["attn_fwd"]["ms_per_step"]}
+        del ws_c, o_c, lse_c
+
     dense = None
     if args.dense:
         fwd_chain = sum(kernels[nm]["ms_per_step"] for nm in ("pool", "select", "attn_fwd"))
@@ -323,6 +363,7 @@ def main():
         "dense_sdpa": dense,
         "exhaustive_selection": exhaustive,
         "reordered_chain": reordered,
+        "complement_forward": complement,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec))
