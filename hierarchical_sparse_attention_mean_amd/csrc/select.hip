@@ -42,56 +42,66 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 // Top-K of each of the workgroup's query rows from the scores in LDS (16 rows x ldc floats, slot order =
 // candidate order): a 32-step bitwise search for the K-th largest order-preserving key (one compare and one
-// ballot per step), ties at the threshold taken in ascending slot order, kept slots compacted in ascending
-// order with ballot prefix counts.  Candidate slots ascend with block index, so this realises the tie rule
-// and the ascending row order directly.  Wave w handles rows 4w .. 4w+3.
+// ballot per slot group and step), ties at the threshold taken in ascending slot order, kept slots compacted in
+// ascending order with ballot prefix counts.  Candidate slots ascend with block index, so this realises the
+// tie rule and the ascending row order directly.  Wave w handles rows 4w .. 4w+3, their four searches
+// interleaved step by step (independent compare -> count -> select chains that hide each other's latency).
 // kM = ceil(ncand / 64) slot groups per lane, a compile-time constant so that the 32 search steps carry no
 // per-group branches.
 template <int kM>
 __device__ __forceinline__ void topk_rows(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
                                           int32_t* out_rows, const int32_t* picks, int coarsest) {
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * w + rr;
-    if (row >= nq) break;
-    uint32_t key[kM];
+  constexpr int kR = 4;
+  uint32_t key[kR][kM];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int row = 4 * w + r;
 #pragma unroll
     for (int m = 0; m < kM; ++m) {
       const int s = lane + 64 * m;
-      // invalid slots (beyond the candidate count or past the last level-L block) get key 0, below
-      // every real score's key (the smallest, -inf, maps to 0x007FFFFF)
-      key[m] = s < ncand ? ord_key(sc[row * ldc + s]) : 0u;
+      // invalid slots (beyond the candidate count or past the last level-L block) and rows past nq get key
+      // 0, below every real score's key (the smallest, -inf, maps to 0x007FFFFF)
+      key[r][m] = (row < nq && s < ncand) ? ord_key(sc[row * ldc + s]) : 0u;
     }
-    // K-th largest key by bitwise search: largest T with #{key >= T} >= K
-    uint32_t T = 0;
-#pragma unroll 4
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
+  }
+  // K-th largest key of each row by bitwise search: largest T with #{key >= T} >= K
+  uint32_t T[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) T[r] = 0;
+#pragma unroll 2
+  for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const uint32_t cand = T[r] | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int m = 0; m < kM; ++m) cnt += popc64(__ballot(key[m] >= cand));
-      T = cnt >= K ? cand : T;
+      for (int m = 0; m < kM; ++m) cnt += popc64(__ballot(key[r][m] >= cand));
+      T[r] = cnt >= K ? cand : T[r];
     }
+  }
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int row = 4 * w + r;
+    if (row >= nq) break;
     int greater = 0;
 #pragma unroll
-    for (int m = 0; m < kM; ++m) greater += popc64(__ballot(key[m] > T));
+    for (int m = 0; m < kM; ++m) greater += popc64(__ballot(key[r][m] > T[r]));
     const int need = K - greater;  // ties at T to take, lowest slots first
     int eq_before = 0, sel_before = 0;
     int32_t* out = out_rows + (size_t)row * K;
 #pragma unroll
     for (int m = 0; m < kM; ++m) {
-      {
-        const uint64_t eqm = __ballot(key[m] == T);
-        const bool sel_eq = (key[m] == T) && (eq_before + lanes_below(eqm) < need);
-        const bool sel = (key[m] > T) || sel_eq;
-        const uint64_t selm = __ballot(sel);
-        if (sel) {
-          const int s = lane + 64 * m;
-          const int blk = coarsest ? s : picks[s >> 4] * kB + (s & 15);
-          out[sel_before + lanes_below(selm)] = blk;
-        }
-        eq_before += popc64(eqm);
-        sel_before += popc64(selm);
+      const uint64_t eqm = __ballot(key[r][m] == T[r]);
+      const bool sel_eq = (key[r][m] == T[r]) && (eq_before + lanes_below(eqm) < need);
+      const bool sel = (key[r][m] > T[r]) || sel_eq;
+      const uint64_t selm = __ballot(sel);
+      if (sel) {
+        const int s = lane + 64 * m;
+        const int blk = coarsest ? s : picks[s >> 4] * kB + (s & 15);
+        out[sel_before + lanes_below(selm)] = blk;
       }
+      eq_before += popc64(eqm);
+      sel_before += popc64(selm);
     }
   }
 }
@@ -131,45 +141,69 @@ __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq
   const int nq = coarsest ? min(16, nl - q0) : 16;
   const int32_t* picks = coarsest ? nullptr : I + (size_t)(g.off[level + 1] + bx) * g.K;
   const int ntiles = (ncand + 15) / 16;
+  // the parent's picks also in LDS, for the block numbers of the kept slots (a global read there would wait
+  // behind the row's stores, which may alias it)
+  __shared__ int pks[32];
+  if (!coarsest && threadIdx.x < g.K) pks[threadIdx.x] = picks[threadIdx.x];
 
-  // A operand: this lane's query row (q0 + c), dims 16*gg .. 16*gg+15 (step s uses dim 16*gg + s).
+  // A operand: this lane's query row (q0 + c); step s = 4m + e uses dim 16m + 4gg + e, so that the four lanes
+  // of a row read 64 contiguous bytes per load (the same dim order for both operands).
   float qf[16];
   {
     const bool ok = c < nq;
-    const float4* src = reinterpret_cast<const float4*>(PQ + (size_t)(g.off[level] + q0 + (ok ? c : 0)) * kD + 16 * gg);
+    const float4* src = reinterpret_cast<const float4*>(PQ + (size_t)(g.off[level] + q0 + (ok ? c : 0)) * kD + 4 * gg);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      float4 x = ok ? src[m] : make_float4(0, 0, 0, 0);
+      float4 x = ok ? src[4 * m] : make_float4(0, 0, 0, 0);
       qf[4 * m] = x.x; qf[4 * m + 1] = x.y; qf[4 * m + 2] = x.z; qf[4 * m + 3] = x.w;
     }
   }
-  for (int t = w; t < ntiles; t += 4) {
-    int j;  // candidate block index (row within the level) for this lane's column c
-    bool valid;
+  // candidate row of tile t for this lane's column c (row 0 where the slot is empty), scores -inf there
+  auto cand_row = [&](int t, bool* valid) {
+    int j;
     if (coarsest) {
       j = 16 * t + c;
-      valid = j < nl;
+      *valid = j < nl;
     } else {
       j = picks[t] * kB + c;
-      valid = true;
+      *valid = true;
     }
-    float kf[16];
-    const float4* src = reinterpret_cast<const float4*>(PK + (size_t)(g.off[level] + (valid ? j : 0)) * kD + 16 * gg);
+    return g.off[level] + (*valid ? j : 0);
+  };
+  auto load_row = [&](int row, float kf[16]) {
+    const float4* src = reinterpret_cast<const float4*>(PK + (size_t)row * kD + 4 * gg);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      float4 x = src[m];
+      const float4 x = src[4 * m];
       kf[4 * m] = x.x; kf[4 * m + 1] = x.y; kf[4 * m + 2] = x.z; kf[4 * m + 3] = x.w;
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  };
+  // tiles two at a time (t and t + 4): both tiles' rows in flight together, their MFMA chains interleaved
+  for (int t = w; t < ntiles; t += 8) {
+    const bool two = t + 4 < ntiles;
+    bool v0, v1 = false;
+    const int r0 = cand_row(t, &v0);
+    const int r1 = two ? cand_row(t + 4, &v1) : r0;
+    float k0[16], k1[16];
+    load_row(r0, k0);
+    load_row(r1, k1);
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = mfma_f32_k4(qf[s], kf[s], acc);
-    // acc[r] = score(query row 4*gg + r, candidate slot 16*t + c)
+    for (int s = 0; s < 16; ++s) {
+      a0 = mfma_f32_k4(qf[s], k0[s], a0);
+      a1 = mfma_f32_k4(qf[s], k1[s], a1);
+    }
+    // a*[r] = score(query row 4*gg + r, candidate slot 16*t + c)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[(4 * gg + r) * ldc + 16 * t + c] = valid ? acc[r] : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[(4 * gg + r) * ldc + 16 * t + c] = v0 ? a0[r] : -INFINITY;
+    if (two) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[(4 * gg + r) * ldc + 16 * (t + 4) + c] = v1 ? a1[r] : -INFINITY;
+    }
   }
   __syncthreads();
 
-  topk_dispatch(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, picks, coarsest);
+  topk_dispatch(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, pks, coarsest);
 }
 
 // ------------------------------------------------------------------------------------------------
