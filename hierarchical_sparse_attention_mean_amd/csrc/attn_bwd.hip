@@ -463,73 +463,127 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
 }
 
 constexpr int kGroup = 4;       // key blocks per wavefront
+constexpr int kSplitMul = 4;    // groups longer than kSplitMul x the mean group length are split into chunks
 constexpr int kMaxShares = 4;   // levels 2..L_e with L_e <= 5 (implied by the size limit n * d < 2^31)
 
+}  // namespace
+
+// Per-slice capacities of the dK/dV work lists (see dkdv_order).
+DkdvBounds dkdv_bounds(const Geom& g) {
+  const int n1 = g.rows[1];
+  DkdvBounds b;
+  b.items = (n1 + kGroup - 1) / kGroup + n1 / 8 + 1;
+  b.slots = n1 / 8 + 1;
+  b.splits = n1 / 16 + 1;
+  return b;
+}
+
+namespace {
+
 // ------------------------------------------------------------------------------------------------
-// 3a. Work order of the dK/dV kernel: for each slice, its key-block groups (4 consecutive key blocks) with more
-// than 8K query blocks in their columns first, then the rest, each part in group order (a stable partition
-// by block-wide prefix sums, deterministic).  The dK/dV kernel takes groups in that order, so the longest
-// columns -- up to 20x the mean on smooth or reordered inputs -- start first instead of ending the kernel.
+// 3a. Work items of the dK/dV kernel.  A group is 4 consecutive key blocks; its stages are the query blocks of
+// their level-1 CSC columns, concatenated (T_g of them).  A group with more than S stages is split into
+// ceil(T_g / S) chunks of near-equal size: on smooth or reordered inputs single columns reach 30x the mean, and
+// one wavefront walking such a group would end the kernel long after the others.  S (>= kSplitMul x the mean
+// group length 4 K) is set by the host to twice the stages per resident wavefront, so only groups that would
+// outlast the rest are split.  Each chunk writes fp32 partial dK, dV of the key blocks it touches to a slot of
+// its own; the chunk that finishes last (an integer counter per split group) sums all of them in chunk order,
+// so the result does not depend on which chunk that is.
+// Items: an unsplit group is (group, 0, T_g, -1); chunk c of split group i is (group, c, i, first slot + c),
+// the split record (group, first slot, chunks, T_g).  Item order per slice: groups with more than twice the
+// mean length first (each expanded into its chunks), then the rest, each part in group order (stable
+// partitions by block-wide prefix sums), so the longest work starts first.  Bounds per slice (n_1 K stages in
+// all), for the smallest S: items <= groups + n_1 / 8, slots <= n_1 / 8, split groups <= n_1 / 16 (each split
+// group has T_g > S and at most 2 T_g / S chunks).
 // grid.x = slices, 1024 threads.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ col_ptr, int32_t* __restrict__ order,
-                                                   Geom g, CscGeom cg) {
-  __shared__ int wave_tot[16];
-  __shared__ int carry_s, nlong_s;
+__global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ col_ptr, int4* __restrict__ items,
+                                                   int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                                   Geom g, CscGeom cg, DkdvBounds bd, int S, int walk) {
+  __shared__ long long wave_tot[16];
+  __shared__ int carry_s[4], nlong_s;
   const int slice = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n1 = g.rows[1], gps = (n1 + kGroup - 1) / kGroup;
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
-  int32_t* out = order + (size_t)slice * gps;
+  int4* it_out = items + (size_t)slice * bd.items;
+  int4* sp_out = splits + (size_t)slice * bd.splits;
   const int thresh = 2 * kGroup * g.K;  // twice the mean group length
-  auto is_long = [&](int gi) { return gi < gps && cp[min(kGroup * gi + kGroup, n1)] - cp[kGroup * gi] > thresh; };
-  // block-wide exclusive prefix of a 0/1 flag, with the running carry across chunks
-  auto scan = [&](int f, int* excl, int* total) {
-    int inc = f;
+  auto glen = [&](int gi) { return gi < gps ? cp[min(kGroup * gi + kGroup, n1)] - cp[kGroup * gi] : 0; };
+  auto chunks = [&](int T) { return T > S ? (T + S - 1) / S : 1; };
+  // block-wide exclusive prefix of two counts at once (low and high 32 bits), with the totals
+  auto scan = [&](int lo, int hi, int* elo, int* ehi, int* tlo, int* thi) {
+    const long long f = ((long long)hi << 32) + lo;
+    long long inc = f;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
-      const int u = __shfl_up(inc, s, 64);
+      const long long u = __shfl_up(inc, s, 64);
       if (lane >= s) inc += u;
     }
     if (lane == 63) wave_tot[w] = inc;
     __syncthreads();
-    int before = 0, tot = 0;
+    long long before = 0, tot = 0;
     for (int i = 0; i < 16; ++i) {
       before += i < w ? wave_tot[i] : 0;
       tot += wave_tot[i];
     }
-    *excl = before + inc - f;
-    *total = tot;
+    const long long e = before + inc - f;
+    *elo = (int)(e & 0xFFFFFFFFll);
+    *ehi = (int)(e >> 32);
+    *tlo = (int)(tot & 0xFFFFFFFFll);
+    *thi = (int)(tot >> 32);
     __syncthreads();
   };
-  if (t == 0) {
-    carry_s = 0;
-    nlong_s = 0;
-  }
+  if (t < 4) carry_s[t] = 0;
+  if (t == 0) nlong_s = 0;
   __syncthreads();
-  for (int base = 0; base < gps; base += 1024) {  // number of long groups
-    int e, tot;
-    scan(is_long(base + t), &e, &tot);
-    if (t == 0) nlong_s += tot;
-    __syncthreads();
+  if (gps > 1024) {  // items of the long groups, before the others are placed (one chunk of groups needs no pass)
+    for (int base = 0; base < gps; base += 1024) {
+      const int T = glen(base + t);
+      int e, x, tot, y;
+      scan(T > thresh ? chunks(T) : 0, 0, &e, &x, &tot, &y);
+      if (t == 0) nlong_s += tot;
+      __syncthreads();
+    }
   }
-  const int nlong = nlong_s;
   for (int base = 0; base < gps; base += 1024) {
     const int gi = base + t;
-    const int f = is_long(gi);
-    int e, tot;
-    scan(f, &e, &tot);
-    const int long_before = carry_s + e;
-    if (gi < gps) out[f ? long_before : nlong + gi - long_before] = gi;
+    const int T = glen(gi);
+    const bool in = gi < gps, lng = in && T > thresh, split = lng && T > S;
+    const int nch = split ? chunks(T) : 1;
+    int e0, e1, e2, e3, t0, t1, t2, t3;
+    scan(lng ? nch : 0, in && !lng ? 1 : 0, &e0, &e1, &t0, &t1);  // item positions: long groups, the others
+    scan(split ? nch : 0, split ? 1 : 0, &e2, &e3, &t2, &t3);      // partial slots, split-group index
+    const int nlong = gps > 1024 ? nlong_s : t0;
+    if (split) {
+      const int p0 = carry_s[0] + e0, slot0 = carry_s[2] + e2, si = carry_s[3] + e3;
+      for (int c = 0; c < nch; ++c) it_out[p0 + c] = make_int4(gi, c, si, slot0 + c);
+      sp_out[si] = make_int4(gi, slot0, nch, T);
+      counters[(size_t)slice * bd.splits + si] = 0;
+    } else if (lng) {
+      it_out[carry_s[0] + e0] = make_int4(gi, 0, T, -1);
+    } else if (in) {
+      it_out[nlong + carry_s[1] + e1] = make_int4(gi, 0, T, -1);
+    }
     __syncthreads();
-    if (t == 0) carry_s += tot;
+    if (t == 0) {
+      if (gps <= 1024) nlong_s = t0;
+      carry_s[0] += t0;
+      carry_s[1] += t1;
+      carry_s[2] += t2;
+      carry_s[3] += t3;
+    }
     __syncthreads();
   }
+  const int count = nlong_s + carry_s[1];
+  // the positions the dK/dV grid walks past the last item hold an end marker (group -1)
+  for (int p = count + t; p < walk; p += 1024) it_out[p] = make_int4(-1, 0, 0, -1);
 }
 
 // ------------------------------------------------------------------------------------------------
 // 3. dK, dV over the level-1 CSC, four consecutive key blocks per wavefront.
-// grid.x = ceil(bh * ceil(n_1 / 4) / 4) (remapped), 256 threads; wave w takes key-block group 4 * id + w,
-// i.e. key blocks 4*gi .. 4*gi+3 of one slice.  The group's columns are consecutive in perm, so the wave walks
+// grid.x = ceil(bh * walk / 4) (remapped; walk = the items-per-slice bound for the split length in use),
+// 256 threads; wave w takes work item 4 * id + w: a
+// key-block group (key blocks 4*gi .. 4*gi+3 of one slice) or a chunk of a split group's stages.  The group's columns are consecutive in perm, so the wave walks
 // one list of query blocks (its stages) across its key blocks, the next stage's loads in flight while a stage
 // is consumed.  A key block's own rows (K, V and its level-1 pooled token) are copied to LDS (DMA) while the
 // previous block is consumed; the levels >= 2 shares -- the same for the four blocks, whose ancestors coincide
@@ -537,41 +591,36 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
 // the very uneven column lengths.
 // ------------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                                                     const float* __restrict__ lse, const float* __restrict__ delta,
-                                                     const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
-                                                     const int32_t* __restrict__ col_ptr,
-                                                     const int32_t* __restrict__ perm, const float* __restrict__ gk,
-                                                     const float* __restrict__ gv,
-                                                     const int32_t* __restrict__ order, bf16_t* __restrict__ dk,
-                                                     bf16_t* __restrict__ dv, Geom g, CscGeom cg) {
-  __shared__ __attribute__((aligned(16))) bf16_t qs[4][16 * kD];          // Q rows of the query block (swizzled)
-  __shared__ __attribute__((aligned(16))) bf16_t dos[4][16 * kD];         // dO rows (swizzled)
-  __shared__ __attribute__((aligned(16))) float lds_ld[4][64];            // LSE (0..15) and Delta (16..31)
-  __shared__ __attribute__((aligned(16))) bf16_t kvs[4][2][16 * kD];      // K, V rows of the next key block
-  __shared__ __attribute__((aligned(16))) bf16_t p1s[4][2][kD];           // its level-1 pooled K, V rows (bf16)
-  __shared__ __attribute__((aligned(16))) float shs[4][kMaxShares][2][kD];  // ancestors' pooled K, V gradients
+// LDS of the dK/dV kernel (per wave w: index [w]).
+struct DkdvLds {
+  bf16_t qs[4][16 * kD];               // Q rows of the query block (swizzled)
+  bf16_t dos[4][16 * kD];              // dO rows (swizzled)
+  float lds_ld[4][64];                 // LSE (0..15) and Delta (16..31)
+  bf16_t kvs[4][2][16 * kD];           // K, V rows of the next key block
+  bf16_t p1s[4][2][kD];                // its level-1 pooled K, V rows (bf16)
+  float shs[4][kMaxShares][2][kD];     // ancestors' pooled K, V gradients
+};
+
+// One work item of wave w.  split: a chunk of a split group (partial sums; the last chunk combines).
+template <bool split>
+__device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                          const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                          const float* __restrict__ lse, const float* __restrict__ delta,
+                                          const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
+                                          const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ perm,
+                                          const float* __restrict__ gk, const float* __restrict__ gv,
+                                          const int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                          float* __restrict__ part, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+                                          const Geom& g, const CscGeom& cg, const DkdvBounds& bd, int slice,
+                                          int4 item, int w) {
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n1 = g.rows[1];
-  const int gps = (n1 + kGroup - 1) / kGroup;
-  // Work item: the order list puts each slice's long groups first.  With bh a multiple of 8, XCD x (= block % 8,
-  // round-robin dispatch) owns slices [x bh/8, (x+1) bh/8) and walks their lists position-major, so every XCD
-  // starts on its longest groups and keeps its slices in its L2; otherwise all slices go position-major.
-  int slice, pos;
-  if (g.bh % 8 == 0) {
-    const int nsl = g.bh / 8, it = 4 * (blockIdx.x / 8) + w;
-    if (it >= nsl * gps) return;  // no workgroup barrier below
-    slice = (blockIdx.x % 8) * nsl + it % nsl;
-    pos = it / nsl;
-  } else {
-    const int it = 4 * blockIdx.x + w;
-    if (it >= g.bh * gps) return;
-    slice = it % g.bh;
-    pos = it / g.bh;
-  }
-  const int j0 = kGroup * order[(size_t)slice * gps + pos];
+  const int j0 = kGroup * item.x;
+  const int slot = item.w;
+  int4 sp = make_int4(0, 0, 1, 0);
+  if (split) sp = splits[(size_t)slice * bd.splits + item.z];  // group, first slot, chunks, stages
+  const int s0 = split ? (int)((int64_t)item.y * sp.w / sp.z) : 0;
+  const int s1 = split ? (int)((int64_t)(item.y + 1) * sp.w / sp.z) : item.z;
   const int nkb = min(kGroup, n1 - j0);
   const size_t base = (size_t)slice * g.n * kD;
   const bf16_t* Q = q + base;
@@ -580,19 +629,22 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   const float* DL = delta + (size_t)slice * g.n;
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
   const int32_t* pm = perm + (size_t)slice * cg.pm_len + cg.pm_off[1];
-  bf16_t* qt = qs[w];
-  bf16_t* dt = dos[w];
-  float* ldt = lds_ld[w];
+  bf16_t* qt = sm.qs[w];
+  bf16_t* dt = sm.dos[w];
+  float* ldt = sm.lds_ld[w];
   const int c7 = c & 7;
   const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
   const int trr = 4 * gq + (c >> 2);
   const bool enrich1 = g.Le >= 1;
-  const int nsh = max(0, min(g.Le, kMaxShares + 1) - 1);
+  const int nsh = split ? 0 : max(0, min(g.Le, kMaxShares + 1) - 1);  // chunks leave the shares to the combine
 
-  // column starts of the group's key blocks (lane t: column j0 + t; lane nkb: the end of the last one)
-  const int cpl = cp[j0 + min(lane, nkb)];
-  const int y0 = __builtin_amdgcn_readfirstlane(cpl);
-  const int total = __builtin_amdgcn_readlane(cpl, nkb) - y0;
+  // column starts of the group's key blocks (lane t: column j0 + t; lane nkb: the end of the last one), as stage
+  // numbers of the item (clipped to its stages [s0, s1) of the group)
+  const int cpr = cp[j0 + min(lane, nkb)];
+  const int yg = __builtin_amdgcn_readfirstlane(cpr);
+  const int cpl = min(max(cpr - yg, s0), s1) - s0;
+  const int y0 = yg + s0;  // perm position of the item's first stage
+  const int total = __builtin_amdgcn_readlane(cpl, nkb);
   auto col_len = [&](int b) { return __builtin_amdgcn_readlane(cpl, b + 1) - __builtin_amdgcn_readlane(cpl, b); };
   auto next_nonempty = [&](int b) {  // first block after b with a non-empty column, nkb if none
     int nb = b + 1;
@@ -603,18 +655,18 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   // copies of one key block's rows into the (single) block slot, and of the shares
   auto dma_block = [&](int b) {
     const size_t r = base + (size_t)16 * (j0 + b) * kD + swz_dma_src(lane);
-    lds_dma16(k + r, &kvs[w][0][0]);
-    lds_dma16(k + r + 8 * kD, &kvs[w][0][8 * kD]);
-    lds_dma16(v + r, &kvs[w][1][0]);
-    lds_dma16(v + r + 8 * kD, &kvs[w][1][8 * kD]);
+    lds_dma16(k + r, &sm.kvs[w][0][0]);
+    lds_dma16(k + r + 8 * kD, &sm.kvs[w][0][8 * kD]);
+    lds_dma16(v + r, &sm.kvs[w][1][0]);
+    lds_dma16(v + r + 8 * kD, &sm.kvs[w][1][8 * kD]);
     if (lane < 16)
-      lds_dma16((lane < 8 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 8 * (lane & 7), &p1s[w][0][0]);
+      lds_dma16((lane < 8 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 8 * (lane & 7), &sm.p1s[w][0][0]);
   };
   if (lane < 32) {
     for (int s = 0; s < nsh; ++s) {
       const int l = s + 2, a = j0 >> (4 * (l - 1));
       const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 4 * (lane & 15);
-      lds_dma16((lane < 16 ? gk : gv) + gr, &shs[w][s][0][0]);
+      lds_dma16((lane < 16 ? gk : gv) + gr, &sm.shs[w][s][0][0]);
     }
   }
 
@@ -622,14 +674,14 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   // as in the forward products) as a broadcast operand (every column holds it)
   bf16x8 kb0, kb1, vb0, vb1, k1b0, k1b1, v1b0, v1b1;
   auto read_block = [&]() {
-    kb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a0]);
-    kb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][0][a1]);
-    vb0 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a0]);
-    vb1 = *reinterpret_cast<const bf16x8*>(&kvs[w][1][a1]);
-    k1b0 = *reinterpret_cast<const bf16x8*>(&p1s[w][0][8 * gq]);
-    k1b1 = *reinterpret_cast<const bf16x8*>(&p1s[w][0][8 * gq + 32]);
-    v1b0 = *reinterpret_cast<const bf16x8*>(&p1s[w][1][8 * gq]);
-    v1b1 = *reinterpret_cast<const bf16x8*>(&p1s[w][1][8 * gq + 32]);
+    kb0 = *reinterpret_cast<const bf16x8*>(&sm.kvs[w][0][a0]);
+    kb1 = *reinterpret_cast<const bf16x8*>(&sm.kvs[w][0][a1]);
+    vb0 = *reinterpret_cast<const bf16x8*>(&sm.kvs[w][1][a0]);
+    vb1 = *reinterpret_cast<const bf16x8*>(&sm.kvs[w][1][a1]);
+    k1b0 = *reinterpret_cast<const bf16x8*>(&sm.p1s[w][0][8 * gq]);
+    k1b1 = *reinterpret_cast<const bf16x8*>(&sm.p1s[w][0][8 * gq + 32]);
+    v1b0 = *reinterpret_cast<const bf16x8*>(&sm.p1s[w][1][8 * gq]);
+    v1b1 = *reinterpret_cast<const bf16x8*>(&sm.p1s[w][1][8 * gq + 32]);
     wait_lds();  // the slot is refilled next
   };
 
@@ -641,6 +693,17 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   // dK = sigma dK^T + shares, dV = dV^T + shares (lane holds d = 16t + 4g + r of key c; with_acc false for a key
   // block no query block kept) -> bf16 rows through the Q / dO tiles, then whole-row coalesced stores
   auto finish = [&](int b, bool with_acc) {
+    if (split) {  // fp32 partial of a touched block to the item's slot: [block][K, V][key][dim]
+      if (with_acc) {
+        float* P = part + (((size_t)slice * bd.slots + slot) * kGroup + b) * (2 * 16 * kD) + c * kD + 4 * gq;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          *reinterpret_cast<f32x4*>(P + 16 * t) = dk_acc[t];
+          *reinterpret_cast<f32x4*>(P + 16 * kD + 16 * t) = dv_acc[t];
+        }
+      }
+      return;
+    }
     float kx[4][4], vx[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -653,8 +716,8 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
       const float wgt = 1.0f / (float)(1 << (4 * (s + 2)));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float4 gk4 = *reinterpret_cast<const float4*>(&shs[w][s][0][16 * t + 4 * gq]);
-        const float4 gv4 = *reinterpret_cast<const float4*>(&shs[w][s][1][16 * t + 4 * gq]);
+        const float4 gk4 = *reinterpret_cast<const float4*>(&sm.shs[w][s][0][16 * t + 4 * gq]);
+        const float4 gv4 = *reinterpret_cast<const float4*>(&sm.shs[w][s][1][16 * t + 4 * gq]);
         kx[t][0] += gk4.x * wgt; kx[t][1] += gk4.y * wgt; kx[t][2] += gk4.z * wgt; kx[t][3] += gk4.w * wgt;
         vx[t][0] += gv4.x * wgt; vx[t][1] += gv4.y * wgt; vx[t][2] += gv4.z * wgt; vx[t][3] += gv4.w * wgt;
       }
@@ -773,7 +836,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   };
 
   int gc = 0;  // stages consumed
-  int cend = __builtin_amdgcn_readlane(cpl, cb + 1) - y0;
+  int cend = __builtin_amdgcn_readlane(cpl, cb + 1);
   auto consume = [&](const QStage& st) {
     compute(st);
     if (++gc == cend) {
@@ -787,7 +850,7 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
         cb = nb;
         nb = next_nonempty(cb);
         if (nb < nkb) dma_block(nb);
-        cend = __builtin_amdgcn_readlane(cpl, cb + 1) - y0;
+        cend = __builtin_amdgcn_readlane(cpl, cb + 1);
       }
       finish(prev, true);
       for (int b = prev + 1; b < (cb > prev ? cb : nkb); ++b) finish(b, false);  // blocks nobody kept
@@ -803,6 +866,101 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
     issue_next(A);
     if (t + 1 < total) consume(B);
   }
+  if (!split) return;
+
+  // Split group: count this chunk done (its partial stores made visible first); the last one to finish sums
+  // every chunk's partials of each key block in chunk order (a chunk's partial of block b exists iff its
+  // stages meet b's column), then scale and shares as in finish.  Lane: key lane / 4, dims 16 (lane % 4) + 0..15.
+  __threadfence();
+  int done = 0;
+  if (lane == 0) done = atomicAdd(&counters[(size_t)slice * bd.splits + item.z], 1);
+  done = __shfl(done, 0, 64);
+  if (done != sp.z - 1) return;
+  __threadfence();
+  const int key = lane >> 2, d0 = 16 * (lane & 3);
+  const int nshc = max(0, min(g.Le, kMaxShares + 1) - 1);
+  for (int b = 0; b < nkb; ++b) {
+    const int cs = __builtin_amdgcn_readlane(cpr, b) - yg, ce = __builtin_amdgcn_readlane(cpr, b + 1) - yg;
+    float kx[16], vx[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kx[e] = vx[e] = 0.f;
+    for (int ch = 0; ch < sp.z; ++ch) {
+      const int c0 = (int)((int64_t)ch * sp.w / sp.z), c1 = (int)((int64_t)(ch + 1) * sp.w / sp.z);
+      if (max(cs, c0) >= min(ce, c1)) continue;
+      const float* P = part + (((size_t)slice * bd.slots + sp.y + ch) * kGroup + b) * (2 * 16 * kD) + key * kD + d0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(P + e);
+        const float4 z = *reinterpret_cast<const float4*>(P + 16 * kD + e);
+        kx[e] += a.x; kx[e + 1] += a.y; kx[e + 2] += a.z; kx[e + 3] += a.w;
+        vx[e] += z.x; vx[e + 1] += z.y; vx[e + 2] += z.z; vx[e + 3] += z.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kx[e] *= g.scale;
+    for (int sh = 0; sh < nshc; ++sh) {
+      const int l = sh + 2, a = j0 >> (4 * (l - 1));
+      const float wgt = 1.0f / (float)(1 << (4 * l));
+      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + d0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(gk + gr + e);
+        const float4 z4 = *reinterpret_cast<const float4*>(gv + gr + e);
+        kx[e] += a4.x * wgt; kx[e + 1] += a4.y * wgt; kx[e + 2] += a4.z * wgt; kx[e + 3] += a4.w * wgt;
+        vx[e] += z4.x * wgt; vx[e + 1] += z4.y * wgt; vx[e + 2] += z4.z * wgt; vx[e + 3] += z4.w * wgt;
+      }
+    }
+    const size_t go = base + ((size_t)16 * (j0 + b) + key) * kD + d0;
+    st16(dk + go, make_uint4(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]), pack_bf16x2(kx[4], kx[5]),
+                             pack_bf16x2(kx[6], kx[7])));
+    st16(dk + go + 8, make_uint4(pack_bf16x2(kx[8], kx[9]), pack_bf16x2(kx[10], kx[11]),
+                                 pack_bf16x2(kx[12], kx[13]), pack_bf16x2(kx[14], kx[15])));
+    st16(dv + go, make_uint4(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]), pack_bf16x2(vx[4], vx[5]),
+                             pack_bf16x2(vx[6], vx[7])));
+    st16(dv + go + 8, make_uint4(pack_bf16x2(vx[8], vx[9]), pack_bf16x2(vx[10], vx[11]),
+                                 pack_bf16x2(vx[12], vx[13]), pack_bf16x2(vx[14], vx[15])));
+  }
+}
+
+__global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                                                     const float* __restrict__ lse, const float* __restrict__ delta,
+                                                     const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
+                                                     const int32_t* __restrict__ col_ptr,
+                                                     const int32_t* __restrict__ perm, const float* __restrict__ gk,
+                                                     const float* __restrict__ gv,
+                                                     const int4* __restrict__ items,
+                                                     const int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                                     float* __restrict__ part, bf16_t* __restrict__ dk,
+                                                     bf16_t* __restrict__ dv, Geom g, CscGeom cg, DkdvBounds bd,
+                                                     int walk) {
+  __shared__ __attribute__((aligned(16))) DkdvLds sm;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Work item: the item list puts each slice's long groups first.  With bh a multiple of 8, XCD x (= block % 8,
+  // round-robin dispatch) owns slices [x bh/8, (x+1) bh/8) and walks their lists position-major, so every XCD
+  // starts on its longest groups and keeps its slices in its L2; otherwise all slices go position-major.
+  int slice, pos;
+  if (g.bh % 8 == 0) {
+    const int nsl = g.bh / 8, it = 4 * (blockIdx.x / 8) + w;
+    if (it >= nsl * walk) return;  // no workgroup barrier below
+    slice = (blockIdx.x % 8) * nsl + it % nsl;
+    pos = it / nsl;
+  } else {
+    const int it = 4 * blockIdx.x + w;
+    if (it >= g.bh * walk) return;
+    slice = it % g.bh;
+    pos = it / g.bh;
+  }
+  int4 item = items[(size_t)slice * bd.items + pos];  // pos < walk <= capacity; group -1 past the last item
+  item = make_int4(uniform(item.x), uniform(item.y), uniform(item.z), uniform(item.w));
+  if (item.x < 0) return;
+  // two copies of the item code: the one for unsplit groups carries none of the split path
+  if (item.w >= 0)
+    dkdv_item<true>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv, g,
+                    cg, bd, slice, item, w);
+  else
+    dkdv_item<false>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv,
+                     g, cg, bd, slice, item, w);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -814,7 +972,11 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
   const size_t n_delta = align256((size_t)g.bh * g.n * sizeof(float));
   const size_t n_part = nhigh ? align256((size_t)g.bh * g.rows[2] * nhigh * kD * sizeof(float)) : 0;
   const size_t n_g = nhigh ? align256((size_t)g.bh * (g.R - g.rows[1]) * kD * sizeof(float)) : 0;
-  const size_t n_order = align256((size_t)g.bh * ((g.rows[1] + kGroup - 1) / kGroup) * sizeof(int32_t));
+  const DkdvBounds bd = dkdv_bounds(g);
+  const size_t n_items = align256((size_t)g.bh * bd.items * sizeof(int4));
+  const size_t n_splits = align256((size_t)g.bh * bd.splits * sizeof(int4));
+  const size_t n_ctr = align256((size_t)g.bh * bd.splits * sizeof(int32_t));
+  const size_t n_dkdv = align256((size_t)g.bh * bd.slots * kGroup * 2 * 16 * kD * sizeof(float));
   if (out) {
     char* p = static_cast<char*>(base);
     out->delta = reinterpret_cast<float*>(p);
@@ -827,9 +989,15 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
     p += n_g;
     out->gv = nhigh ? reinterpret_cast<float*>(p) : nullptr;
     p += n_g;
-    out->order = reinterpret_cast<int32_t*>(p);
+    out->items = reinterpret_cast<int4*>(p);
+    p += n_items;
+    out->splits = reinterpret_cast<int4*>(p);
+    p += n_splits;
+    out->split_done = reinterpret_cast<int32_t*>(p);
+    p += n_ctr;
+    out->dkdv_part = reinterpret_cast<float*>(p);
   }
-  return n_delta + 2 * n_part + 2 * n_g + n_order;
+  return n_delta + 2 * n_part + 2 * n_g + n_items + n_splits + n_ctr + n_dkdv;
 }
 
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
@@ -856,13 +1024,21 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    const int gps = (n1 + kGroup - 1) / kGroup;
-    const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * gps + 3) / 4) : (g.bh * gps + 3) / 4;
-    dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.order, g, cg);
+    const DkdvBounds bd = dkdv_bounds(g);
+    // split length: twice the stages per resident wavefront (all slices' n_1 K stages spread over the waves
+    // the device holds), at least kSplitMul x the mean group length
+    const int64_t waves = 4 * (int64_t)std::max(1, resident_workgroups((const void*)bwd_dkdv_bf16, 256));
+    const int64_t per_wave = ((int64_t)g.bh * n1 * g.K + waves - 1) / waves;
+    const int S = (int)std::min<int64_t>(std::max<int64_t>(kSplitMul * kGroup * g.K, 2 * per_wave), 1 << 30);
+    // items per slice with this S: groups + at most 2 n_1 K / S chunks beyond one per split group
+    const int walk = (int)std::min<int64_t>(bd.items, (n1 + kGroup - 1) / kGroup + 2 * (int64_t)n1 * g.K / S + 1);
+    const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * walk + 3) / 4) : (g.bh * walk + 3) / 4;
+    dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, S, walk);
     bwd_dkdv_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                                             (const bf16_t*)dout, lse, ws.delta, (const bf16_t*)pk,
-                                            (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv,
-                                            ws.order, (bf16_t*)dk, (bf16_t*)dv, g, cg);
+                                            (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv, ws.items,
+                                            ws.splits, ws.split_done, ws.dkdv_part, (bf16_t*)dk, (bf16_t*)dv, g,
+                                            cg, bd, walk);
   }
   return hipGetLastError();
 }

@@ -40,6 +40,7 @@ int resident_workgroups(const void* kernel, int threads);
 // Grid of a persistent kernel that wants `wanted` workgroups of work: at most one resident wave of
 // workgroups, rounded up to a multiple of 8 (one per XCD), at least 8.
 int persistent_grid(const void* kernel, int threads, int64_t wanted);
+int resident_workgroups(const void* kernel, int threads);
 
 hipError_t launch_pyramid(const Geom& g, int dtype_bf16, const void* q, const void* k, const void* v, float* pq,
                           float* pk, float* pv, void* pk_bf16, void* pv_bf16, hipStream_t stream);
@@ -69,8 +70,15 @@ struct BwdWs {
   float* part_v;
   float* gk;
   float* gv;
-  int32_t* order;  // [bh][ceil(n_1 / 4)]: key-block groups of each slice, long columns first
+  int4* items;       // [bh][DkdvBounds::items]: dK/dV work items, an end marker (group -1) after the last
+  int4* splits;      // [bh][DkdvBounds::splits]: split groups (group, first slot, chunks, stages)
+  int32_t* split_done;  // [bh][DkdvBounds::splits]: chunks of each split group finished
+  float* dkdv_part;  // [bh][DkdvBounds::slots][4 blocks][K, V][16 keys][d]: partial sums of split groups
 };
+struct DkdvBounds {
+  int items, slots, splits;  // per-slice capacities
+};
+DkdvBounds dkdv_bounds(const Geom& g);
 size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base);
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, const void* pk, const void* pv,

@@ -17,6 +17,10 @@ Recipe
   is standardised, flattened row-major to ``F`` of shape [H*W, C], projected by ``P`` [C, d] with
   entries N(0, 1/C), and Q = F P + a*eps_Q, K = F P + a*eps_K, V = F P + a*eps_V with independent
   eps ~ N(0, 1) and noise amplitude ``a``.
+* ``"hub"``: i.i.d. N(0, 1) rows plus a shared direction ``u`` (entries +-1, drawn per slice from the
+  projection stream): every query row gets ``hub_gain * u`` and so do the key rows of the first
+  ``hub_tokens`` tokens, so that every unit's selection keeps the blocks that hold them -- a few key
+  blocks whose CSC columns hold every query block (the most skewed column lengths there are).
 * ``dO`` is i.i.d. N(0, 1).
 * Values are drawn in float64, then rounded once (round-to-nearest-even) to fp32 or bf16.
 """
@@ -44,12 +48,14 @@ class Workload:
     topk: int
     levels: int
     backward: bool
-    kind: str           # "iid" or "field"
+    kind: str           # "iid", "field" or "hub"
     seed: int
     grid: tuple = field(default=(0, 0))   # (H, W) pixel grid, H * W == n
     length_scale: float = 16.0
     channels: int = 8
     noise: float = 0.1
+    hub_tokens: int = 64
+    hub_gain: float = 0.35
 
     @property
     def bh(self) -> int:
@@ -135,6 +141,12 @@ def _slice_values(w: Workload, s: int, d: int):
         X = F @ P
         return [X + w.noise * rng(w.seed, s, st).standard_normal((n, d))
                 for st in (STREAM_Q, STREAM_K, STREAM_V)]
+    if w.kind == "hub":
+        q, k, v = (rng(w.seed, s, st).standard_normal((n, d)) for st in (STREAM_Q, STREAM_K, STREAM_V))
+        u = rng(w.seed, s, STREAM_PROJ).choice(np.array([-1.0, 1.0]), d)
+        q += w.hub_gain * u
+        k[:w.hub_tokens] += w.hub_gain * u
+        return [q, k, v]
     raise ValueError(w.kind)
 
 

@@ -41,6 +41,11 @@ CASES = [
     ("f32_n4096_K7_Le1", inputs.custom(1, 2, 4096, 64, "f32", seed=18, topk=7, levels=2), 2, 1),
     ("bf16_field_n65536_L3_h1", inputs.custom(1, 1, 65536, 64, "bf16", seed=19, kind="field", topk=8, levels=3,
                                               backward=True), 3, -1),
+    # hub inputs: a few key blocks kept by every query block, so the dK/dV kernel splits their groups
+    ("bf16_hub_n4096_split", inputs.custom(1, 2, 4096, 64, "bf16", seed=21, kind="hub", topk=8, levels=2,
+                                           backward=True), 2, -1),
+    ("bf16_hub_n4096_K5_Le1", inputs.custom(1, 1, 4096, 64, "bf16", seed=22, kind="hub", topk=5, levels=2,
+                                            backward=True), 2, 1),
 ]
 _cache = {}
 
@@ -204,6 +209,30 @@ def test_deterministic(L, name, w, levels, Le):
         outs.append([t.clone() for t in (b.idx, b.o, b.lse, b.col_ptr, b.perm, b.dq, b.dk, b.dv)])
     for a, c in zip(*outs):
         assert torch.equal(a, c)
+
+
+def test_split_groups_deterministic(L):
+    """Hub inputs: the oracle's level-1 columns put more than 4x the mean group length (4 K stages) into one
+    group of 4 key blocks, so its stages run as several chunks whose partial sums dkdv_combine adds; two runs
+    give identical bits."""
+    name, w, levels, Le = next(c for c in CASES if c[0] == "bf16_hub_n4096_split")
+    x, ex, ref = _prepare(name, w, levels, Le)
+    n1 = w.n // w.block
+    cp1 = ref["col_ptr"][:, :n1 + 1]
+    groups = cp1[:, np.minimum(np.arange(0, n1, 4) + 4, n1)] - cp1[:, np.arange(0, n1, 4)]
+    assert groups.max() > 4 * 4 * w.topk, groups.max()
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    outs = []
+    for _ in range(2):
+        b = L.Buffers(_prob(L, w, levels, Le))
+        b.pyramid(q, k, v)
+        b.idx.copy_(torch.from_numpy(ref["idx"]))
+        L.attn_fwd(b.prob, q, k, v, b.pka, b.pva, b.idx, b.o, b.lse)
+        b.backward(q, k, v, do)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (b.dq, b.dk, b.dv)])
+    for a, c in zip(*outs):
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
 def test_tie_rule_on_gpu(L):
