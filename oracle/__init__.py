@@ -66,6 +66,8 @@ def _load():
     lib.llsa_ref_attn_bwd.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32, _i32, _dbl,
                                       _pd, _pd, _pd, _pd, _pd, _pd, _pd, _pd, _pi,
                                       _pd, _pd, _pd, _pd, _pd]
+    lib.llsa_ref_attn_bwd_complement.restype = None
+    lib.llsa_ref_attn_bwd_complement.argtypes = lib.llsa_ref_attn_bwd.argtypes
     lib.llsa_ref_reorder_index.restype = _i32
     lib.llsa_ref_reorder_index.argtypes = [_i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_int64)]
     lib.llsa_ref_reorder.restype = None
@@ -172,8 +174,9 @@ def index_transpose(idx, n, block, levels, topk, enrich_levels):
 
 
 def attn_bwd(q, k, v, o, lse, dout, pk, pv, idx, block, levels, topk, enrich_levels, scale,
-             want_pooled: bool = False):
-    """Backward.  Returns (dq, dk, dv) or (dq, dk, dv, dpk, dpv) with pooled-token gradients."""
+             want_pooled: bool = False, complement: bool = False):
+    """Backward.  Returns (dq, dk, dv) or (dq, dk, dv, dpk, dpv) with pooled-token gradients.
+    complement=True takes the complement-partition reading of the enrichment."""
     q, k, v, o, dout, pk, pv = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, o, dout, pk, pv))
     lse = np.ascontiguousarray(lse, dtype=np.float64)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -185,9 +188,10 @@ def attn_bwd(q, k, v, o, lse, dout, pk, pv, idx, block, levels, topk, enrich_lev
     else:
         dpk = dpv = None
         pdpk = pdpv = ctypes.cast(None, _pd)
-    _load().llsa_ref_attn_bwd(bh, n, d, block, levels, topk, enrich_levels, scale,
-                              _d(q), _d(k), _d(v), _d(o), _d(lse), _d(dout), _d(pk), _d(pv), _i(idx),
-                              _d(dq), _d(dk), _d(dv), pdpk, pdpv)
+    fn = _load().llsa_ref_attn_bwd_complement if complement else _load().llsa_ref_attn_bwd
+    fn(bh, n, d, block, levels, topk, enrich_levels, scale,
+       _d(q), _d(k), _d(v), _d(o), _d(lse), _d(dout), _d(pk), _d(pv), _i(idx),
+       _d(dq), _d(dk), _d(dv), pdpk, pdpv)
     if want_pooled:
         return dq, dk, dv, dpk, dpv
     return dq, dk, dv

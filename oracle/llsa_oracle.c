@@ -441,14 +441,15 @@ void llsa_ref_index_transpose(int64_t bh, int64_t n, int B, int L, int K, int Le
 /* No gradient through the Top-K choice or into pooled queries.                                       */
 /* [LLSA review, "If this is right" (backward uses only sparse indices); abstract; "Core claim"]     */
 /* Optional dpk/dpv (may be NULL) receive the pooled-token gradients [bh][R][d].                       */
+/* complement != 0: the complement-partition entry set (build_entries_complement) instead.             */
 /* ------------------------------------------------------------------------------------------------ */
-void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
-                       const double* q, const double* k, const double* v, const double* o,
-                       const double* lse, const double* dout, const double* pk, const double* pv,
-                       const int32_t* idx, double* dq, double* dk, double* dv, double* dpk,
-                       double* dpv) {
+static void attn_bwd_entries(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                             const double* q, const double* k, const double* v, const double* o,
+                             const double* lse, const double* dout, const double* pk, const double* pv,
+                             const int32_t* idx, double* dq, double* dk, double* dv, double* dpk,
+                             double* dpv, int complement) {
   const int64_t R = llsa_ref_pyramid_rows(n, B, L);
-  const int me = max_entries(B, L, K, Le);
+  const int me = complement ? max_entries_complement(n, B, L, K, Le) : max_entries(B, L, K, Le);
   int nthr = 1;
 #ifdef _OPENMP
   nthr = omp_get_max_threads();
@@ -481,7 +482,8 @@ void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
         double delta = 0.0;
         for (int c = 0; c < d; ++c) delta += gov[c] * ov[c];
         for (int c = 0; c < d; ++c) DQ[qi * d + c] = 0.0;
-        const int ne = build_entries(n, B, L, K, Le, I, qi, E);
+        const int ne = complement ? build_entries_complement(n, B, L, K, Le, I, qi, E)
+                                  : build_entries(n, B, L, K, Le, I, qi, E);
         for (int e = 0; e < ne; ++e) {
           const double *kv, *vv;
           int64_t arow;
@@ -538,6 +540,23 @@ void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le
   }
   free(acc_k);
   free(acc_v);
+}
+
+void llsa_ref_attn_bwd(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                       const double* q, const double* k, const double* v, const double* o,
+                       const double* lse, const double* dout, const double* pk, const double* pv,
+                       const int32_t* idx, double* dq, double* dk, double* dv, double* dpk,
+                       double* dpv) {
+  attn_bwd_entries(bh, n, d, B, L, K, Le, sigma, q, k, v, o, lse, dout, pk, pv, idx, dq, dk, dv, dpk, dpv, 0);
+}
+
+/* The backward over the complement-partition entry set. */
+void llsa_ref_attn_bwd_complement(int64_t bh, int64_t n, int d, int B, int L, int K, int Le, double sigma,
+                                  const double* q, const double* k, const double* v, const double* o,
+                                  const double* lse, const double* dout, const double* pk, const double* pv,
+                                  const int32_t* idx, double* dq, double* dk, double* dv, double* dpk,
+                                  double* dpv) {
+  attn_bwd_entries(bh, n, d, B, L, K, Le, sigma, q, k, v, o, lse, dout, pk, pv, idx, dq, dk, dv, dpk, dpv, 1);
 }
 
 /*

@@ -72,3 +72,64 @@ def test_everything_kept_is_dense_attention(n, B, L):
     idx, _ = oracle.select(oracle.pool(q, B, L), pk, n, B, L, K)
     o, _ = oracle.attn_fwd(q, k, v, pk, pv, idx, B, L, K, L, scale, complement=True)
     np.testing.assert_allclose(o, _dense(q, k, v, scale), rtol=0, atol=1e-12)
+
+
+def _dense_grads(q, k, v, dout, scale):
+    qt, kt, vt = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    o.backward(torch.from_numpy(dout))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("n,B,L,K,D", CASES)
+def test_backward_constant_spans_give_dense_gradients(n, B, L, K, D):
+    """K, V constant on every B^L span: every query sees each key once (itself or one pooled ancestor whose
+    logit carries + l ln B), so dQ, dK, dV equal dense attention's gradients (torch autograd, fp64) -- the
+    pooled token's gradient, spread B^-l over its span, is each key's dense gradient.  The selected-token
+    reading's gradients differ."""
+    q, dout = _rand((2, n, D), 14), _rand((2, n, D), 17)
+    k, v = _piecewise((2, n, D), B ** L, 15), _piecewise((2, n, D), B ** L, 16)
+    scale = 1.0 / np.sqrt(D)
+    pk, pv = oracle.pool(k, B, L), oracle.pool(v, B, L)
+    idx, _ = oracle.select(oracle.pool(q, B, L), pk, n, B, L, K)
+    ref = _dense_grads(q, k, v, dout, scale)
+    o, lse = oracle.attn_fwd(q, k, v, pk, pv, idx, B, L, K, L, scale, complement=True)
+    got = oracle.attn_bwd(q, k, v, o, lse, dout, pk, pv, idx, B, L, K, L, scale, complement=True)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-10)
+    o1, lse1 = oracle.attn_fwd(q, k, v, pk, pv, idx, B, L, K, L, scale)
+    sel = oracle.attn_bwd(q, k, v, o1, lse1, dout, pk, pv, idx, B, L, K, L, scale)
+    assert max(np.abs(g - r).max() for g, r in zip(sel, ref)) > 1e-6
+
+
+@pytest.mark.parametrize("n,B,L,K,Le", [(256, 4, 3, 2, 3), (256, 4, 3, 3, 2), (512, 16, 1, 3, 1)])
+def test_backward_matches_finite_differences(n, B, L, K, Le):
+    """Central differences of sum(dO * O) through the oracle's complement forward, with the pyramid re-pooled
+    from the perturbed K and V and the selection held fixed (no gradient through Top-K), on sampled elements
+    of Q, K and V."""
+    D = 8
+    q, k, v, dout = (_rand((1, n, D), s) for s in (21, 22, 23, 24))
+    scale = 1.0 / np.sqrt(D)
+    idx, _ = oracle.select(oracle.pool(q, B, L), oracle.pool(k, B, L), n, B, L, K)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_fwd(qq, kk, vv, oracle.pool(kk, B, L), oracle.pool(vv, B, L), idx, B, L, K, Le, scale,
+                               complement=True)
+        return float((o * dout).sum())
+
+    pk, pv = oracle.pool(k, B, L), oracle.pool(v, B, L)
+    o, lse = oracle.attn_fwd(q, k, v, pk, pv, idx, B, L, K, Le, scale, complement=True)
+    grads = oracle.attn_bwd(q, k, v, o, lse, dout, pk, pv, idx, B, L, K, Le, scale, complement=True)
+    rng = np.random.default_rng(25)
+    h = 1e-5
+    for which in range(3):
+        for _ in range(12):
+            t, c = int(rng.integers(n)), int(rng.integers(D))
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][0, t, c] += h
+            up = loss(*args)
+            args[which][0, t, c] -= 2 * h
+            dn = loss(*args)
+            fd = (up - dn) / (2 * h)
+            assert abs(fd - grads[which][0, t, c]) <= 1e-7 * max(1.0, abs(fd)), (which, t, c, fd,
+                                                                              grads[which][0, t, c])
