@@ -63,14 +63,17 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
 constexpr int kSt = 16 + 8;      // bf16 row stride of the dS^T / P^T tiles (entry rows x 16 queries)
 
 // kT: 16-entry tiles of level >= 2 enrichment entries whose partials are held in registers (K*(L_e-1) <= 16 kT).
-template <int kT>
+// kMaxC, kComp: as in the forward -- the complement reading takes its enrichment entries from the complement
+// lists `esrc` (laid out by `cm`) and leaves the pooled-token gradients to comp_partial.
+template <int kT, int kMaxC, bool kComp>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
                                                       const float* __restrict__ lse, const bf16_t* __restrict__ dout,
                                                       const bf16_t* __restrict__ pk, const bf16_t* __restrict__ pv,
                                                       const int32_t* __restrict__ idx, bf16_t* __restrict__ dq,
                                                       float* __restrict__ delta, float* __restrict__ part_k,
-                                                      float* __restrict__ part_v, Geom g) {
+                                                      float* __restrict__ part_v, const int32_t* __restrict__ esrc,
+                                                      Geom g, CompGeom cm) {
   __shared__ __attribute__((aligned(16))) bf16_t kts[4][32 * kD];      // K tiles (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t vts[4][32 * kD];      // V tiles (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t qsl[4][2][16 * kD];   // Q rows, two slots (swizzled)
@@ -78,11 +81,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   __shared__ __attribute__((aligned(16))) bf16_t osl[4][16 * kD];      // O rows of the next block (swizzled)
   __shared__ __attribute__((aligned(16))) float lsl[4][2][16];         // LSE of the block's queries
   __shared__ __attribute__((aligned(16))) int is1[4][2][32];           // level-1 selection row
-  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxCoarse];    // enrichment selection entries
-  __shared__ __attribute__((aligned(16))) EntryTab tab;                // per-entry constants (shared)
+  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxC];         // enrichment entries' block indices
+  __shared__ __attribute__((aligned(16))) EntryTabT<kMaxC> tab;        // per-entry constants (shared)
   const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  fill_entry_tab(g, tab);
+  if (kComp)
+    fill_entry_tab_complement(g, cm, tab);
+  else
+    fill_entry_tab(g, tab);
   const int n1 = g.rows[1];
   const int gps = (n1 + 15) / 16;
   const Sweep su = xcd_sweep(g.bh * gps, blockIdx.x / 8, gridDim.x / 8);
@@ -90,10 +96,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   const int nblk = 4 * su.count;
   bf16_t* kt = kts[w];
   bf16_t* vt = vts[w];
-  const Plan plan = make_plan(g);
+  const Plan plan = make_plan(g, kComp ? cm.total : g.K * g.Le);
   const int nst = plan.nstages;
-  const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
+  const int nhigh = (!kComp && g.Le >= 2) ? g.K * (g.Le - 1) : 0;
   const size_t slice_elems = (size_t)g.n * kD, slice_rows = (size_t)g.R * kD;
+  const size_t esrc_slice = kComp ? (size_t)cm.slice : (size_t)g.R * g.K;
   const float sl2 = g.scale_log2;
 
   struct Blk {
@@ -125,11 +132,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     if (lane < 16) lds_dma4(lse + (size_t)b.slice * g.n + 16 * b.i + lane, &lsl[w][p][0]);
     const int32_t* I = idx + (size_t)b.slice * g.R * g.K;
     if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + b.i) * g.K + lane, &is1[w][p][0]);
+    const int32_t* E = esrc + b.slice * esrc_slice;
 #pragma unroll
-    for (int jj = 0; jj < kMaxCoarse / 64; ++jj) {
+    for (int jj = 0; jj < kMaxC / 64; ++jj) {
       if (64 * jj < plan.ncoarse) {
         const int e = min(lane + 64 * jj, plan.ncoarse - 1);
-        lds_dma4(I + tab.pos0[e] + (b.i >> tab.shift[e]) * g.K, &es[w][p][64 * jj]);
+        lds_dma4(E + tab.pos0[e] + (b.i >> tab.shift[e]) * tab.stride[e], &es[w][p][64 * jj]);
       }
     }
   };
@@ -602,7 +610,21 @@ struct DkdvLds {
 };
 
 // One work item of wave w.  split: a chunk of a split group (partial sums; the last chunk combines).
-template <bool split>
+// Pooled-gradient shares of a key-block group: share s is level s + 2, whose ancestor j >> 4(l-1) is the same for
+// the group's four blocks; row of the level's gradient array (levels >= 2 only, or every level for the
+// complement reading).
+__device__ __forceinline__ int share_level(int s) { return s + 2; }
+__device__ __forceinline__ int share_count(const Geom& g) { return max(0, min(g.Le, kMaxShares + 1) - 1); }
+template <bool kComp>
+__device__ __forceinline__ size_t share_row(const Geom& g, int slice, int l, int j) {
+  const int a = j >> (4 * (l - 1));
+  return kComp ? (size_t)slice * g.R + g.off[l] + a : (size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + a;
+}
+
+// kComp: the complement reading -- the query blocks of a key block's column do not attend its level-1 pooled
+// token (they kept the block), so nothing is folded into the products; instead each key block adds B^-1 of its
+// own level-1 pooled token's gradient, and the group the shares of levels >= 2 (gk, gv: [slice][R][d]).
+template <bool split, bool kComp>
 __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                           const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                           const float* __restrict__ lse, const float* __restrict__ delta,
@@ -635,8 +657,8 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
   const int c7 = c & 7;
   const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
   const int trr = 4 * gq + (c >> 2);
-  const bool enrich1 = g.Le >= 1;
-  const int nsh = split ? 0 : max(0, min(g.Le, kMaxShares + 1) - 1);  // chunks leave the shares to the combine
+  const bool enrich1 = !kComp && g.Le >= 1;
+  const int nsh = split ? 0 : share_count(g);  // chunks leave the shares to the combine
 
   // column starts of the group's key blocks (lane t: column j0 + t; lane nkb: the end of the last one), as stage
   // numbers of the item (clipped to its stages [s0, s1) of the group)
@@ -664,8 +686,7 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
   };
   if (lane < 32) {
     for (int s = 0; s < nsh; ++s) {
-      const int l = s + 2, a = j0 >> (4 * (l - 1));
-      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + 4 * (lane & 15);
+      const size_t gr = share_row<kComp>(g, slice, share_level(s), j0) * kD + 4 * (lane & 15);
       lds_dma16((lane < 16 ? gk : gv) + gr, &sm.shs[w][s][0][0]);
     }
   }
@@ -712,8 +733,19 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
         kx[t][r] = with_acc ? dk_acc[t][r] * g.scale : 0.f;
         vx[t][r] = with_acc ? dv_acc[t][r] : 0.f;
       }
+    if (kComp && g.Le >= 1) {  // the block's own level-1 pooled token
+      const size_t r1 = share_row<true>(g, slice, 1, j0 + b) * kD + 4 * gq;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 gk4 = *reinterpret_cast<const float4*>(gk + r1 + 16 * t);
+        const float4 gv4 = *reinterpret_cast<const float4*>(gv + r1 + 16 * t);
+        const float wgt = 1.0f / (float)kB;
+        kx[t][0] += gk4.x * wgt; kx[t][1] += gk4.y * wgt; kx[t][2] += gk4.z * wgt; kx[t][3] += gk4.w * wgt;
+        vx[t][0] += gv4.x * wgt; vx[t][1] += gv4.y * wgt; vx[t][2] += gv4.z * wgt; vx[t][3] += gv4.w * wgt;
+      }
+    }
     for (int s = 0; s < nsh; ++s) {
-      const float wgt = 1.0f / (float)(1 << (4 * (s + 2)));
+      const float wgt = 1.0f / (float)(1 << (4 * share_level(s)));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float4 gk4 = *reinterpret_cast<const float4*>(&sm.shs[w][s][0][16 * t + 4 * gq]);
@@ -878,7 +910,7 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
   if (done != sp.z - 1) return;
   __threadfence();
   const int key = lane >> 2, d0 = 16 * (lane & 3);
-  const int nshc = max(0, min(g.Le, kMaxShares + 1) - 1);
+  const int nshc = share_count(g);
   for (int b = 0; b < nkb; ++b) {
     const int cs = __builtin_amdgcn_readlane(cpr, b) - yg, ce = __builtin_amdgcn_readlane(cpr, b + 1) - yg;
     float kx[16], vx[16];
@@ -898,10 +930,21 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) kx[e] *= g.scale;
+    if (kComp && g.Le >= 1) {  // the block's own level-1 pooled token
+      const size_t r1 = share_row<true>(g, slice, 1, j0 + b) * kD + d0;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(gk + r1 + e);
+        const float4 z4 = *reinterpret_cast<const float4*>(gv + r1 + e);
+        const float wgt = 1.0f / (float)kB;
+        kx[e] += a4.x * wgt; kx[e + 1] += a4.y * wgt; kx[e + 2] += a4.z * wgt; kx[e + 3] += a4.w * wgt;
+        vx[e] += z4.x * wgt; vx[e + 1] += z4.y * wgt; vx[e + 2] += z4.z * wgt; vx[e + 3] += z4.w * wgt;
+      }
+    }
     for (int sh = 0; sh < nshc; ++sh) {
-      const int l = sh + 2, a = j0 >> (4 * (l - 1));
+      const int l = share_level(sh);
       const float wgt = 1.0f / (float)(1 << (4 * l));
-      const size_t gr = ((size_t)slice * (g.R - n1) + g.off[l] - n1 + a) * kD + d0;
+      const size_t gr = share_row<kComp>(g, slice, l, j0) * kD + d0;
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
         const float4 a4 = *reinterpret_cast<const float4*>(gk + gr + e);
@@ -922,6 +965,7 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
   }
 }
 
+template <bool kComp>
 __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
@@ -956,14 +1000,53 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   if (item.x < 0) return;
   // two copies of the item code: the one for unsplit groups carries none of the split path
   if (item.w >= 0)
-    dkdv_item<true>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv, g,
+    dkdv_item<true, kComp>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv, g,
                     cg, bd, slice, item, w);
   else
-    dkdv_item<false>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv,
+    dkdv_item<false, kComp>(sm, q, k, v, dout, lse, delta, pk, pv, col_ptr, perm, gk, gv, splits, counters, part, dk, dv,
                      g, cg, bd, slice, item, w);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Work lists, then the dK/dV kernel (one launch each; the caller's timer brackets both).
+template <bool kComp>
+void launch_dkdv(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v, const float* lse,
+                 const void* dout, const void* pk, const void* pv, const int32_t* col_ptr, const int32_t* perm,
+                 void* dk, void* dv, const BwdWs& ws, hipStream_t stream) {
+  const int n1 = g.rows[1];
+  const DkdvBounds bd = dkdv_bounds(g);
+  // split length: twice the stages per resident wavefront (all slices' n_1 K stages spread over the waves
+  // the device holds), at least kSplitMul x the mean group length
+  const int64_t waves = 4 * (int64_t)std::max(1, resident_workgroups((const void*)bwd_dkdv_bf16<kComp>, 256));
+  const int64_t per_wave = ((int64_t)g.bh * n1 * g.K + waves - 1) / waves;
+  const int S = (int)std::min<int64_t>(std::max<int64_t>(kSplitMul * kGroup * g.K, 2 * per_wave), 1 << 30);
+  // items per slice with this S: groups + at most 2 n_1 K / S chunks beyond one per split group
+  const int walk = (int)std::min<int64_t>(bd.items, (n1 + kGroup - 1) / kGroup + 2 * (int64_t)n1 * g.K / S + 1);
+  const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * walk + 3) / 4) : (g.bh * walk + 3) / 4;
+  dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, S, walk);
+  bwd_dkdv_bf16<kComp><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                                                 (const bf16_t*)dout, lse, ws.delta, (const bf16_t*)pk,
+                                                 (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv, ws.items, ws.splits,
+                                                 ws.split_done, ws.dkdv_part, (bf16_t*)dk, (bf16_t*)dv, g, cg, bd,
+                                                 walk);
+}
+
+// Work-list part of a backward workspace, from `p` (null: sizes only); adds its bytes.
+void dkdv_ws(const Geom& g, BwdWs* out, char* p, size_t* bytes) {
+  const DkdvBounds bd = dkdv_bounds(g);
+  const size_t n_items = align256((size_t)g.bh * bd.items * sizeof(int4));
+  const size_t n_splits = align256((size_t)g.bh * bd.splits * sizeof(int4));
+  const size_t n_ctr = align256((size_t)g.bh * bd.splits * sizeof(int32_t));
+  const size_t n_dkdv = align256((size_t)g.bh * bd.slots * kGroup * 2 * 16 * kD * sizeof(float));
+  if (out) {
+    out->items = reinterpret_cast<int4*>(p);
+    out->splits = reinterpret_cast<int4*>(p + n_items);
+    out->split_done = reinterpret_cast<int32_t*>(p + n_items + n_splits);
+    out->dkdv_part = reinterpret_cast<float*>(p + n_items + n_splits + n_ctr);
+  }
+  *bytes += n_items + n_splits + n_ctr + n_dkdv;
+}
 
 }  // namespace
 
@@ -972,11 +1055,7 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
   const size_t n_delta = align256((size_t)g.bh * g.n * sizeof(float));
   const size_t n_part = nhigh ? align256((size_t)g.bh * g.rows[2] * nhigh * kD * sizeof(float)) : 0;
   const size_t n_g = nhigh ? align256((size_t)g.bh * (g.R - g.rows[1]) * kD * sizeof(float)) : 0;
-  const DkdvBounds bd = dkdv_bounds(g);
-  const size_t n_items = align256((size_t)g.bh * bd.items * sizeof(int4));
-  const size_t n_splits = align256((size_t)g.bh * bd.splits * sizeof(int4));
-  const size_t n_ctr = align256((size_t)g.bh * bd.splits * sizeof(int32_t));
-  const size_t n_dkdv = align256((size_t)g.bh * bd.slots * kGroup * 2 * 16 * kD * sizeof(float));
+  size_t bytes = n_delta + 2 * n_part + 2 * n_g;
   if (out) {
     char* p = static_cast<char*>(base);
     out->delta = reinterpret_cast<float*>(p);
@@ -989,15 +1068,26 @@ size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base) {
     p += n_g;
     out->gv = nhigh ? reinterpret_cast<float*>(p) : nullptr;
     p += n_g;
-    out->items = reinterpret_cast<int4*>(p);
-    p += n_items;
-    out->splits = reinterpret_cast<int4*>(p);
-    p += n_splits;
-    out->split_done = reinterpret_cast<int32_t*>(p);
-    p += n_ctr;
-    out->dkdv_part = reinterpret_cast<float*>(p);
   }
-  return n_delta + 2 * n_part + 2 * n_g + n_items + n_splits + n_ctr + n_dkdv;
+  dkdv_ws(g, out, out ? static_cast<char*>(base) + bytes : nullptr, &bytes);
+  return bytes;
+}
+
+size_t bwd_comp_ws_layout(const Geom& g, const PartGeom& pg, BwdWs* out, void* base) {
+  const size_t n_delta = align256((size_t)g.bh * g.n * sizeof(float));
+  const size_t n_g = align256((size_t)g.bh * g.R * kD * sizeof(float));
+  const size_t n_part = align256((size_t)g.bh * pg.n2u * pg.nc * 2 * kD * sizeof(float));
+  size_t bytes = n_delta + 2 * n_g + n_part;
+  if (out) {
+    char* p = static_cast<char*>(base);
+    out->delta = reinterpret_cast<float*>(p);
+    out->gk = reinterpret_cast<float*>(p + n_delta);
+    out->gv = reinterpret_cast<float*>(p + n_delta + n_g);
+    out->part_k = reinterpret_cast<float*>(p + n_delta + 2 * n_g);  // the pooled-gradient partials
+    out->part_v = nullptr;
+  }
+  dkdv_ws(g, out, out ? static_cast<char*>(base) + bytes : nullptr, &bytes);
+  return bytes;
 }
 
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
@@ -1009,11 +1099,11 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   {
     LaunchTimer timer(kBwdDq, stream);
     const int nhigh = g.Le >= 2 ? g.K * (g.Le - 1) : 0;
-    auto kernel = nhigh <= 16 ? bwd_dq_bf16<1> : bwd_dq_bf16<2>;
+    auto kernel = nhigh <= 16 ? bwd_dq_bf16<1, kMaxCoarse, false> : bwd_dq_bf16<2, kMaxCoarse, false>;
     kernel<<<persistent_grid((const void*)kernel, 256, groups), 256, 0, stream>>>(
         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, lse, (const bf16_t*)dout,
         (const bf16_t*)pk, (const bf16_t*)pv,
-        idx, (bf16_t*)dq, ws.delta, ws.part_k, ws.part_v, g);
+        idx, (bf16_t*)dq, ws.delta, ws.part_k, ws.part_v, idx, g, CompGeom{});
   }
   if (g.Le >= 2) {
     int tokens = 0;
@@ -1024,21 +1114,30 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    const DkdvBounds bd = dkdv_bounds(g);
-    // split length: twice the stages per resident wavefront (all slices' n_1 K stages spread over the waves
-    // the device holds), at least kSplitMul x the mean group length
-    const int64_t waves = 4 * (int64_t)std::max(1, resident_workgroups((const void*)bwd_dkdv_bf16, 256));
-    const int64_t per_wave = ((int64_t)g.bh * n1 * g.K + waves - 1) / waves;
-    const int S = (int)std::min<int64_t>(std::max<int64_t>(kSplitMul * kGroup * g.K, 2 * per_wave), 1 << 30);
-    // items per slice with this S: groups + at most 2 n_1 K / S chunks beyond one per split group
-    const int walk = (int)std::min<int64_t>(bd.items, (n1 + kGroup - 1) / kGroup + 2 * (int64_t)n1 * g.K / S + 1);
-    const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * walk + 3) / 4) : (g.bh * walk + 3) / 4;
-    dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, S, walk);
-    bwd_dkdv_bf16<<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
-                                            (const bf16_t*)dout, lse, ws.delta, (const bf16_t*)pk,
-                                            (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv, ws.items,
-                                            ws.splits, ws.split_done, ws.dkdv_part, (bf16_t*)dk, (bf16_t*)dv, g,
-                                            cg, bd, walk);
+    launch_dkdv<false>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_complement(const Geom& g, const CscGeom& cg, const CompGeom& cm, const PartGeom& pg,
+                                      const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                      const void* dout, const void* pk, const void* pv, const int32_t* idx,
+                                      const int32_t* comp, const int32_t* col_ptr, const int32_t* perm, void* dq,
+                                      void* dk, void* dv, const BwdWs& ws, hipStream_t stream) {
+  const int groups = g.bh * ((g.rows[1] + 15) / 16);
+  {
+    LaunchTimer timer(kBwdDq, stream);
+    auto kernel = bwd_dq_bf16<1, kMaxComplement, true>;
+    kernel<<<persistent_grid((const void*)kernel, 256, groups), 256, 0, stream>>>(
+        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)o, lse, (const bf16_t*)dout,
+        (const bf16_t*)pk, (const bf16_t*)pv, idx, (bf16_t*)dq, ws.delta, nullptr, nullptr, comp, g, cm);
+  }
+  hipError_t e = launch_comp_grads(g, cg, pg, q, dout, lse, ws.delta, pk, pv, idx, col_ptr, perm, ws.part_k, ws.gk,
+                                   ws.gv, stream);
+  if (e != hipSuccess) return e;
+  {
+    LaunchTimer timer(kBwdDkdv, stream);
+    launch_dkdv<true>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, stream);
   }
   return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "entries.hpp"
 #include "launch.hpp"
 #include "llsa.h"
@@ -148,6 +150,57 @@ llsa::CompGeom comp_geom(const Resolved& r) {
 }
 size_t complement_ws(const Resolved& r) { return align256((size_t)r.bh * comp_geom(r).slice * sizeof(int32_t)); }
 
+// CSC of levels 1..T (the layout llsa_index_transpose produces for T = max(1, L_e)).
+llsa::CscGeom csc_geom(const Resolved& r, int T) {
+  llsa::CscGeom cg;
+  memset(&cg, 0, sizeof(cg));
+  cg.T = T;
+  int cpo = 0, pmo = 0;
+  for (int l = 1; l <= T; ++l) {
+    cg.cp_off[l] = cpo;
+    cg.pm_off[l] = pmo;
+    cpo += r.g.rows[l] + 1;
+    pmo += r.g.rows[l] * r.g.K;
+  }
+  cg.cp_len = cpo;
+  cg.pm_len = pmo;
+  return cg;
+}
+
+// Backward of the complement reading: its pooled-gradient reduction reads the CSC of level l + 1 for every
+// l <= L_e below the coarsest level, so it builds the CSC of levels 1..min(L_e + 1, L) itself.
+llsa::CscGeom comp_csc_geom(const Resolved& r) { return csc_geom(r, std::max(1, std::min(r.g.Le + 1, r.g.L))); }
+llsa::PartGeom part_geom(const Resolved& r) {
+  llsa::PartGeom pg;
+  memset(&pg, 0, sizeof(pg));
+  pg.n2u = (r.g.rows[1] + 15) / 16;
+  for (int l = 1; l <= r.g.Le; ++l) {
+    pg.ncand[l] = l == r.g.L ? r.g.rows[l] : llsa::kB * r.g.K;
+    pg.xoff[l] = pg.nc;
+    pg.nc += pg.ncand[l];
+  }
+  return pg;
+}
+// [complement lists | col_ptr | perm | transpose counters | transpose staging | backward workspace]
+struct CompBwdParts {
+  size_t lists, cp, pm, cnt, tmp, bwd;
+};
+CompBwdParts comp_bwd_parts(const Resolved& r) {
+  const llsa::CscGeom cg = comp_csc_geom(r);
+  CompBwdParts z;
+  z.lists = complement_ws(r);
+  z.cp = align256((size_t)r.bh * cg.cp_len * sizeof(int32_t));
+  z.pm = align256((size_t)r.bh * cg.pm_len * sizeof(int32_t));
+  z.cnt = z.cp;
+  z.tmp = z.pm;
+  z.bwd = llsa::bwd_comp_ws_layout(r.g, part_geom(r), nullptr, nullptr);
+  return z;
+}
+size_t comp_bwd_ws(const Resolved& r) {
+  const CompBwdParts z = comp_bwd_parts(r);
+  return z.lists + z.cp + z.pm + z.cnt + z.tmp + z.bwd;
+}
+
 #define LLSA_TRY(x)          \
   do {                       \
     const int _s = (x);      \
@@ -189,6 +242,7 @@ size_t llsa_workspace_bytes(const llsa_problem* prob, int op) {
   if (op == LLSA_OP_INDEX_TRANSPOSE) return transpose_ws(r);
   if (op == LLSA_OP_ATTN_BWD) return llsa::bwd_ws_layout(r.g, nullptr, nullptr);
   if (op == LLSA_OP_ATTN_FWD_COMPLEMENT) return complement_ws(r);
+  if (op == LLSA_OP_ATTN_BWD_COMPLEMENT) return comp_bwd_ws(r);
   return 0;
 }
 
@@ -319,6 +373,38 @@ int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const 
   llsa::bwd_ws_layout(r.g, &w, ws);
   return launched(llsa::launch_attn_bwd(r.g, r.cg, q, k, v, o, lse, dout, pk, pv, idx, col_ptr, perm, dq, dk, dv, w,
                                         (hipStream_t)stream));
+}
+
+int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
+                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
+  const llsa::CompGeom cm = comp_geom(r);
+  if (cm.total > llsa::kMaxComplement) return LLSA_ERR_UNSUPPORTED;
+  if (r.bh == 0) return LLSA_OK;
+  LLSA_TRY(check_ptrs({q, k, v, o, lse, dout, pk, pv, idx, dq, dk, dv}));
+  if (!ws || ws_bytes < comp_bwd_ws(r)) return LLSA_ERR_WORKSPACE;
+  LLSA_TRY(check_ptrs({ws}));
+  LLSA_TRY(check_device());
+  const CompBwdParts z = comp_bwd_parts(r);
+  char* p = static_cast<char*>(ws);
+  int32_t* comp = reinterpret_cast<int32_t*>(p);
+  int32_t* col_ptr = reinterpret_cast<int32_t*>(p + z.lists);
+  int32_t* perm = reinterpret_cast<int32_t*>(p + z.lists + z.cp);
+  int32_t* cnt = reinterpret_cast<int32_t*>(p + z.lists + z.cp + z.pm);
+  int32_t* tmp = reinterpret_cast<int32_t*>(p + z.lists + z.cp + z.pm + z.cnt);
+  llsa::BwdWs w;
+  const llsa::PartGeom pg = part_geom(r);
+  llsa::bwd_comp_ws_layout(r.g, pg, &w, p + z.lists + z.cp + z.pm + z.cnt + z.tmp);
+  const llsa::CscGeom cg = comp_csc_geom(r);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = llsa::launch_complement_lists(r.g, cm, idx, comp, st);
+  if (e == hipSuccess) e = llsa::launch_index_transpose(r.g, cg, idx, col_ptr, perm, cnt, tmp, st);
+  if (e != hipSuccess) return LLSA_ERR_LAUNCH;
+  return launched(llsa::launch_attn_bwd_complement(r.g, cg, cm, pg, q, k, v, o, lse, dout, pk, pv, idx, comp, col_ptr,
+                                                   perm, dq, dk, dv, w, st));
 }
 
 }  // extern "C"

@@ -53,6 +53,17 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
                            const void* pk, const void* pv, const int32_t* idx, void* o, float* lse,
                            hipStream_t stream);
 struct CompGeom;
+// Candidate layout of the complement reading's pooled-gradient partials: per slice, n2u units of 16 fine
+// blocks, each with nc partial rows (levels 1..L_e: ncand[l] candidates from row xoff[l]; 16 K below the
+// coarsest level, n_L there), a row = d K values then d V values (fp32).
+struct PartGeom {
+  int n2u, nc;
+  int ncand[kMaxLevels + 1], xoff[kMaxLevels + 1];
+};
+hipError_t launch_comp_grads(const Geom& g, const CscGeom& cg, const PartGeom& pg, const void* q, const void* dout,
+                             const float* lse, const float* delta, const void* pk, const void* pv,
+                             const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, float* part,
+                             float* gk, float* gv, hipStream_t stream);
 hipError_t launch_complement_lists(const Geom& g, const CompGeom& cm, const int32_t* idx, int32_t* comp,
                                    hipStream_t stream);
 hipError_t launch_attn_fwd_complement(const Geom& g, const CompGeom& cm, const void* q, const void* k,
@@ -80,6 +91,16 @@ struct DkdvBounds {
 };
 DkdvBounds dkdv_bounds(const Geom& g);
 size_t bwd_ws_layout(const Geom& g, BwdWs* out, void* base);
+struct PartGeom;
+struct CompGeom;
+// The complement reading's backward workspace: delta, pooled gradients of every level (gk, gv: [bh][R][d]),
+// the pooled-gradient partials (in part_k) and the dK/dV work lists.
+size_t bwd_comp_ws_layout(const Geom& g, const PartGeom& pg, BwdWs* out, void* base);
+hipError_t launch_attn_bwd_complement(const Geom& g, const CscGeom& cg, const CompGeom& cm, const PartGeom& pg,
+                                      const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                      const void* dout, const void* pk, const void* pv, const int32_t* idx,
+                                      const int32_t* comp, const int32_t* col_ptr, const int32_t* perm, void* dq,
+                                      void* dk, void* dv, const BwdWs& ws, hipStream_t stream);
 hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, const void* pk, const void* pv,
                            const int32_t* idx, const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk,

@@ -23,7 +23,7 @@ F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_PARAM, ERR_DEVICE = \
     -1, -2, -3, -4, -5, -6, -7, -8, -9
-OP_INDEX_TRANSPOSE, OP_ATTN_BWD, OP_ATTN_FWD_COMPLEMENT = 1, 2, 3
+OP_INDEX_TRANSPOSE, OP_ATTN_BWD, OP_ATTN_FWD_COMPLEMENT, OP_ATTN_BWD_COMPLEMENT = 1, 2, 3, 4
 KERNELS = ("pool", "select", "attn_fwd", "transpose", "bwd_dq", "bwd_reduce", "bwd_dkdv",
            "select_exhaustive", "reorder", "complement")  # LLSA_KERNEL_* order
 
@@ -59,10 +59,11 @@ _lib.llsa_select_exhaustive.argtypes = [_P, _vp, _vp, _vp, _vp]
 _lib.llsa_reorder.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]
 _lib.llsa_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.llsa_attn_fwd_complement.argtypes = [_P] + [_vp] * 9 + [_sz, _vp]
+_lib.llsa_attn_bwd_complement.argtypes = [_P] + [_vp] * 13 + [_sz, _vp]
 _lib.llsa_index_transpose.argtypes = [_P, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.llsa_attn_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
 for _f in ("llsa_build_pyramid", "llsa_select", "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd",
-           "llsa_attn_fwd_complement", "llsa_index_transpose", "llsa_attn_bwd"):
+           "llsa_attn_fwd_complement", "llsa_attn_bwd_complement", "llsa_index_transpose", "llsa_attn_bwd"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.llsa_resolve.argtypes = [_P, _P]
 _lib.llsa_resolve.restype = ctypes.c_int
@@ -175,6 +176,15 @@ def attn_fwd_complement(prob, q, k, v, pk, pv, idx, o, lse, ws, stream=None):
     _check(_lib.llsa_attn_fwd_complement(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(pk), _ptr(pv),
                                          _ptr(idx), _ptr(o), _ptr(lse), _ptr(ws), nbytes, _stream(stream)),
            "llsa_attn_fwd_complement")
+
+
+def attn_bwd_complement(prob, q, k, v, o, lse, dout, pk, pv, idx, dq, dk, dv, ws, stream=None):
+    """Backward under the complement-partition reading (ws: OP_ATTN_BWD_COMPLEMENT bytes)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.llsa_attn_bwd_complement(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         _ptr(dout), _ptr(pk), _ptr(pv), _ptr(idx), _ptr(dq), _ptr(dk), _ptr(dv),
+                                         _ptr(ws), nbytes, _stream(stream)),
+           "llsa_attn_bwd_complement")
 
 
 def index_transpose(prob, idx, col_ptr, perm, ws, stream=None):

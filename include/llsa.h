@@ -67,7 +67,12 @@ typedef struct {
 } llsa_problem;
 
 /* Operation ids for llsa_workspace_bytes. */
-enum { LLSA_OP_INDEX_TRANSPOSE = 1, LLSA_OP_ATTN_BWD = 2, LLSA_OP_ATTN_FWD_COMPLEMENT = 3 };
+enum {
+  LLSA_OP_INDEX_TRANSPOSE = 1,
+  LLSA_OP_ATTN_BWD = 2,
+  LLSA_OP_ATTN_FWD_COMPLEMENT = 3,
+  LLSA_OP_ATTN_BWD_COMPLEMENT = 4
+};
 
 /*
  * llsa_build_pyramid -- hierarchical compression [LLSA review, "Core claim"; "What carries the
@@ -155,6 +160,23 @@ int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const 
 int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v,
                              const void* pk, const void* pv, const int32_t* idx, void* o, float* lse, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * llsa_attn_bwd_complement -- the backward of llsa_attn_fwd_complement [LLSA review, "If this is right" (the
+ * backward uses only the sparse indices) and "Core claim" (pooled tokens, weight B^l)]: dQ, dK, dV through the
+ * same entry sets; a level-l pooled token's gradient reaches each of the B^l raw tokens it averages with factor
+ * B^-l.  Every gradient element is summed in a fixed order (bitwise reproducible).
+ *   q, k, v, o, lse, dout, pk, pv, idx, dq, dk, dv: as llsa_attn_bwd (bf16 only), with o and lse from
+ *      llsa_attn_fwd_complement; idx from llsa_select.
+ *   ws scratch of llsa_workspace_bytes(prob, LLSA_OP_ATTN_BWD_COMPLEMENT) bytes (caller-owned): the complement
+ *      lists, the CSC of levels 1..min(L_e + 1, L) (built here), Delta, per-level pooled gradients and their
+ *      partial sums (fp32, 512 bytes per candidate per 256 queries).
+ * Limit: as llsa_attn_fwd_complement (LLSA_ERR_UNSUPPORTED).
+ */
+int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const void* pk, const void* pv,
+                             const int32_t* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /*
  * llsa_index_transpose -- CSR -> CSC of the selection of levels 1..T, T = max(1, L_e) [LLSA review,

@@ -25,7 +25,8 @@ def _declared():
 def test_exports_every_declared_symbol(L):
     names = _declared()
     assert {"llsa_build_pyramid", "llsa_select", "llsa_attn_fwd", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd_complement"} <= set(names)
+            "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd_complement",
+            "llsa_attn_bwd_complement"} <= set(names)
     for n in names:
         assert hasattr(L.lib(), n), n
 
@@ -109,6 +110,15 @@ def test_complement_forward_host_checks(L):
     assert f.llsa_attn_fwd_complement(ctypes.byref(big), *args, 64, 1 << 30, None) == L.ERR_UNSUPPORTED
     empty = L.problem(0, 4, 65536)
     assert f.llsa_attn_fwd_complement(ctypes.byref(empty), *([None] * 8), None, 0, None) == L.OK
+    # backward: 13 pointers, then the workspace
+    nb = L.workspace_bytes(p, L.OP_ATTN_BWD_COMPLEMENT)
+    assert nb > need
+    bargs = [16] * 12
+    assert f.llsa_attn_bwd_complement(ctypes.byref(p), *bargs, 64, nb - 1, None) == L.ERR_WORKSPACE
+    assert f.llsa_attn_bwd_complement(ctypes.byref(p), *([None] * 12), 64, nb, None) == L.ERR_NULL
+    assert f.llsa_attn_bwd_complement(ctypes.byref(pf), *bargs, 64, nb, None) == L.ERR_DTYPE
+    assert f.llsa_attn_bwd_complement(ctypes.byref(big), *bargs, 64, 1 << 30, None) == L.ERR_UNSUPPORTED
+    assert f.llsa_attn_bwd_complement(ctypes.byref(empty), *([None] * 12), None, 0, None) == L.OK
 
 
 def test_empty_batch_is_a_no_op(L):
