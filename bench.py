@@ -329,12 +329,42 @@ def main():
         fam_c = llsa.timing_read()
         llsa.timing_enable(False)
         lists_ms, fwd_ms = fam_c["complement"][0] / reps, fam_c["attn_fwd"][0] / reps
+        # the whole step under this reading: pyramid, selection, forward, backward (which builds its own lists
+        # and CSC of levels 1..min(L_e + 1, L))
+        ws_cb = torch.empty(max(1, llsa.workspace_bytes(p, llsa.OP_ATTN_BWD_COMPLEMENT)), dtype=torch.uint8,
+                            device="cuda")
+        dq_c, dk_c, dv_c = (torch.empty_like(q) for _ in range(3))
+
+        def step_c():
+            b.pyramid(q, k, v, stream)
+            llsa.select(p, b.pq, b.pk, b.idx, stream)
+            llsa.attn_fwd_complement(p, q, k, v, b.pka, b.pva, b.idx, o_c, lse_c, ws_c, stream)
+            llsa.attn_bwd_complement(p, q, k, v, o_c, lse_c, do, b.pka, b.pva, b.idx, dq_c, dk_c, dv_c, ws_cb,
+                                     stream)
+
+        for _ in range(2):
+            step_c()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step_c()
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) * 1e3 / reps
+        llsa.timing_enable(True)
+        for _ in range(reps):
+            step_c()
+        torch.cuda.synchronize()
+        fam_s = llsa.timing_read()
+        llsa.timing_enable(False)
         complement = {"entries_per_fine_block": total, "selected_entries_per_fine_block": p.topk * p.enrich_levels,
                       "lists_ms": round(lists_ms, 4), "attn_fwd_ms": round(fwd_ms, 4),
                       "attn_fwd_alg_GBps": round(a_fwd["bytes"] / (fwd_ms * 1e-3) / 1e9, 1),
                       "attn_fwd_alg_TFLOPs": round(a_fwd["flops"] / (fwd_ms * 1e-3) / 1e12, 2),
-                      "selected_reading_attn_fwd_ms": kernels["attn_fwd"]["ms_per_step"]}
-        del ws_c, o_c, lse_c
+                      "selected_reading_attn_fwd_ms": kernels["attn_fwd"]["ms_per_step"],
+                      "fwdbwd_ms_per_step": round(step_ms, 4),
+                      "fwdbwd_kernels_ms_per_step": {nm: round(tc[0] / reps, 4) for nm, tc in fam_s.items() if tc[1]},
+                      "workspace_bytes_bwd": ws_cb.numel()}
+        del ws_c, o_c, lse_c, ws_cb, dq_c, dk_c, dv_c
 
     dense = None
     if args.dense:
