@@ -26,6 +26,7 @@ namespace llsa {
 namespace {
 
 constexpr int kMaxSlotsPerLane = 8;  // up to 512 candidates per query row
+constexpr int kRoundsMaxK = 8;       // Top-K by rounds of maxima up to this K (and 128 candidates), else bitwise search
 
 // Order-preserving map of an fp32 score to uint32 (+0 and -0 compare equal).
 __device__ __forceinline__ uint32_t ord_key(float s) {
@@ -106,10 +107,92 @@ __device__ __forceinline__ void topk_rows(const float* sc, int ldc, int ncand, i
   }
 }
 
+// Wave-wide maximum of an unsigned value (every lane gets it): xor 1 and 2 within quads, rotations by 4 and 8
+// within 16-lane rows (DPP), then the row and half swaps.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E /* quad_perm [2,3,0,1] */, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124 /* row_ror:4 */, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)b[0], (uint32_t)b[1]);
+}
+
+// The same Top-K by K rounds of "take the largest remaining key, the lowest slot among equal ones" -- the order
+// (score descending, block index ascending) of the tie rule -- for small K: per round one wave maximum on the
+// vector unit and two ballots, where the bitwise search spends 32 scalar-heavy steps.  Rows interleaved as
+// above; the kept slots are compacted in slot order at the end.
+template <int kM>
+__device__ __forceinline__ void topk_rows_rounds(const float* sc, int ldc, int ncand, int nq, int K, int w,
+                                                 int lane, int32_t* out_rows, const int32_t* picks, int coarsest) {
+  constexpr int kR = 4;
+  uint32_t key[kR][kM];
+  uint32_t kept[kR][kM];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int row = 4 * w + r;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const int s = lane + 64 * m;
+      key[r][m] = (row < nq && s < ncand) ? ord_key(sc[row * ldc + s]) : 0u;  // real keys are >= 0x007FFFFF
+      kept[r][m] = 0u;
+    }
+  }
+  for (int i = 0; i < K; ++i) {
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      uint32_t v = key[r][0];
+#pragma unroll
+      for (int m = 1; m < kM; ++m) v = max(v, key[r][m]);
+      const uint32_t mx = wave_max_u32(v);
+      // lowest slot holding mx: the first group m with a match, its lowest lane
+      int pick_m = kM, pick_l = 0;
+#pragma unroll
+      for (int m = kM - 1; m >= 0; --m) {
+        const uint64_t b = __ballot(key[r][m] == mx);
+        if (b) {
+          pick_m = m;
+          pick_l = (int)__builtin_ctzll(b);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const bool hit = m == pick_m && lane == pick_l;
+        kept[r][m] |= hit ? 1u : 0u;
+        key[r][m] = hit ? 0u : key[r][m];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int row = 4 * w + r;
+    if (row >= nq) break;
+    int32_t* out = out_rows + (size_t)row * K;
+    int sel_before = 0;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const uint64_t selm = __ballot(kept[r][m] != 0u);
+      if (kept[r][m]) {
+        const int s = lane + 64 * m;
+        const int blk = coarsest ? s : picks[s >> 4] * kB + (s & 15);
+        out[sel_before + lanes_below(selm)] = blk;
+      }
+      sel_before += popc64(selm);
+    }
+  }
+}
+
 __device__ __forceinline__ void topk_dispatch(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
                                               int32_t* out_rows, const int32_t* picks, int coarsest) {
   const int M = (ncand + 63) / 64;
-  if (M <= 1)
+  if (K <= kRoundsMaxK && M <= 2) {
+    if (M <= 1)
+      topk_rows_rounds<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+    else
+      topk_rows_rounds<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  } else if (M <= 1)
     topk_rows<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
   else if (M == 2)
     topk_rows<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
