@@ -1,4 +1,5 @@
-"""GPU parity at the benchmark sizes, in the launch configuration bench.py times, on sampled slices.
+"""GPU parity at the full workload sizes (the benchmark one in the launch configuration bench.py times), on
+sampled slices.
 
 The whole chain runs on every (batch, head) slice of the N = 65536 forward+backward workload (16 heads, K = 8,
 L = 3) and of the N = 262144 one (8 heads, K = 16, L = 3 -- the backward's two-tile path for the level >= 2
@@ -75,3 +76,31 @@ def test_fullsize_n65536_16_heads(L):
 
 def test_fullsize_n262144_K16(L):
     _run_sampled(L, inputs.WORKLOADS["fwdbwd_bf16_n262144"], samples=(5,))
+
+
+def test_fullsize_fwd_n16384_8_heads(L):
+    """The N = 16384 forward workload (8 heads, i.i.d. inputs, K = 8, L = 2): the GPU chain on every slice,
+    selection parity on sampled slices, then O and LSE element by element on them with the oracle's selection."""
+    w = inputs.WORKLOADS["fwd_bf16_n16384"]
+    x = inputs.make_inputs(w)
+    q, k, v = (_dev(x[nm]) for nm in ("q", "k", "v"))
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels), backward=False)
+    b.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(b.o.float()).all()
+    idx = b.idx.clone()
+    for s in (2, 7):
+        ex = {nm: x[nm].exact.reshape(w.bh, w.n, w.d)[s:s + 1] for nm in ("q", "k", "v")}
+        ref = oracle.run(ex["q"], ex["k"], ex["v"], w.block, w.topk, levels=w.levels)
+        compared, total = selection_parity(idx[s:s + 1].cpu().numpy(), ref["idx"], ref["pq"], ref["pk"], w.n,
+                                           w.block, w.levels, w.topk)
+        assert compared >= 0.9 * total
+        idx2 = idx.clone()
+        idx2[s] = torch.from_numpy(ref["idx"][0]).cuda()
+        L.attn_fwd(b.prob, q, k, v, b.pka, b.pva, idx2, b.o, b.lse)
+        torch.cuda.synchronize()
+        g = host(b.o).reshape(w.bh, w.n, w.d)[s:s + 1]
+        worst = check_close("O", g.reshape(1, -1), ref["o"].reshape(1, -1), w.dtype)
+        lse_err = np.abs(host(b.lse).reshape(w.bh, w.n)[s] - ref["lse"][0]).max()
+        assert lse_err <= 2e-2, lse_err
+        print(f"{w.name} slice {s}: selection rows compared {compared}/{total}, O {worst:.2e}, lse {lse_err:.2e}")
