@@ -409,17 +409,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
 // 2. Pooled-token gradients of levels 2..Le from the per-(level-2 unit, slot) partials via the CSC.
 // grid.x = sum_{l=2..Le} n_l, grid.y = slice; 256 threads.  Token j of level l sums, over the CSR positions
 // p = u*K + s of its column, the partials of entry (l, s) of the B^(l-2) level-2 units under unit u.  Those
-// (position, unit) items are dealt round-robin to the four waves (lane = dim), each wave adds its items in
-// order with four items' loads in flight, and the wave sums are added in wave order: a fixed order, so
-// the result is reproducible.
+// (position, unit) items go four to a wave instruction -- lane l takes item 4 i + l / 16 of its wave's share
+// and dims 4 (l % 16) .. +3 of its K and V rows (16-byte loads), eight items of a wave in flight -- and are
+// summed in a fixed order: per lane in item order, then the four item lanes of a wave, then the four waves.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__ col_ptr,
                                                      const int32_t* __restrict__ perm,
                                                      const float* __restrict__ part_k,
                                                      const float* __restrict__ part_v, float* __restrict__ gk,
                                                      float* __restrict__ gv, Geom g, CscGeom cg) {
-  __shared__ float red[2][4][kD];
-  const int slice = blockIdx.y, d = threadIdx.x & 63;
+  __shared__ float4 red[2][4][16];
+  const int slice = blockIdx.y, lane = threadIdx.x & 63, q4 = lane >> 4, d4 = 4 * (lane & 15);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int x = blockIdx.x, l = 2;
   while (x >= g.rows[l]) {
@@ -434,39 +434,50 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
   const int sh = 4 * (l - 2);  // level-2 units per level-l unit: 1 << sh
   const int y0 = cp[j];
   const int items = (cp[j + 1] - y0) << sh;
-  const float* PKs = part_k + (size_t)slice * n2 * nhigh * kD + d;
-  const float* PVs = part_v + (size_t)slice * n2 * nhigh * kD + d;
-  float ak = 0.f, av = 0.f;
-  for (int q0 = w; q0 < items; q0 += 16) {
-    float xk[4], xv[4];
+  const float* PKs = part_k + (size_t)slice * n2 * nhigh * kD + d4;
+  const float* PVs = part_v + (size_t)slice * n2 * nhigh * kD + d4;
+  float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
+  // wave w takes items 16 r + 4 w + q4 (r = 0, 1, ...): two rounds of four lanes' items per iteration
+  for (int q0 = 4 * w + q4; q0 < items; q0 += 32) {
+    float4 xk[2], xv[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = q0 + 4 * i;
-      xk[i] = xv[i] = 0.f;
+    for (int i = 0; i < 2; ++i) {
+      const int q = q0 + 16 * i;
+      xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (q < items) {
         const int p = pm[y0 + (q >> sh)];
         const int u = p / g.K, slot = p - u * g.K;
         const int u2 = (u << sh) + (q & ((1 << sh) - 1));
         const size_t off = ((size_t)u2 * nhigh + (l - 2) * g.K + slot) * kD;
-        xk[i] = PKs[off];
-        xv[i] = PVs[off];
+        xk[i] = *reinterpret_cast<const float4*>(PKs + off);
+        xv[i] = *reinterpret_cast<const float4*>(PVs + off);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ak += xk[i];
-      av += xv[i];
+    for (int i = 0; i < 2; ++i) {
+      ak.x += xk[i].x; ak.y += xk[i].y; ak.z += xk[i].z; ak.w += xk[i].w;
+      av.x += xv[i].x; av.y += xv[i].y; av.z += xv[i].z; av.w += xv[i].w;
     }
   }
-  red[0][w][d] = ak;
-  red[1][w][d] = av;
+  // the four item lanes of each dim group (lanes d, d + 16, d + 32, d + 48), the same order in every lane
+  float4 sk, sv;
+  sk.x = group_sum(ak.x); sk.y = group_sum(ak.y); sk.z = group_sum(ak.z); sk.w = group_sum(ak.w);
+  sv.x = group_sum(av.x); sv.y = group_sum(av.y); sv.z = group_sum(av.z); sv.w = group_sum(av.w);
+  if (q4 == 0) {
+    red[0][w][lane] = sk;
+    red[1][w][lane] = sv;
+  }
   __syncthreads();
-  if (w == 0) {
-    const float sk = ((red[0][0][d] + red[0][1][d]) + red[0][2][d]) + red[0][3][d];
-    const float sv = ((red[1][0][d] + red[1][1][d]) + red[1][2][d]) + red[1][3][d];
-    const size_t o = ((size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + j) * kD + d;
-    gk[o] = sk;
-    gv[o] = sv;
+  if (w == 0 && q4 < 2) {
+    const int dl = lane & 15;
+    float4 r = red[q4][0][dl];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      const float4 z = red[q4][ww][dl];
+      r.x += z.x; r.y += z.y; r.z += z.z; r.w += z.w;
+    }
+    const size_t o = ((size_t)slice * (g.R - g.rows[1]) + g.off[l] - g.rows[1] + j) * kD + d4;
+    *reinterpret_cast<float4*>((q4 == 0 ? gk : gv) + o) = r;
   }
 }
 
