@@ -45,8 +45,6 @@ struct Geom {
 typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
 typedef float hf32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
-
 // Two fp32 -> packed bf16 pair, round-to-nearest-even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const hf32x2 x = {lo, hi};
@@ -79,8 +77,6 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
   r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
   return r;
 }
-
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // v of lane l ^ 8 (within each 16-lane row): a DPP row rotation by 8 on the VALU.
 __device__ __forceinline__ float xor8_f(float v) {
@@ -131,16 +127,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
   __builtin_memcpy(&r, &v, 16);
   return r;
-}
-
-// Eight consecutive fp32 values -> bf16x8 (RNE).
-__device__ __forceinline__ bf16x8 f32x8_to_bf16x8(const float4 a, const float4 b) {
-  uint4 u;
-  u.x = pack_bf16x2(a.x, a.y);
-  u.y = pack_bf16x2(a.z, a.w);
-  u.z = pack_bf16x2(b.x, b.y);
-  u.w = pack_bf16x2(b.z, b.w);
-  return as_bf16x8(u);
 }
 
 }  // namespace llsa
