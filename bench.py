@@ -106,7 +106,14 @@ def oracle_baseline(w, x, budget_s=20.0):
         if t_all >= budget_s:
             break
     ms_full = t_all / done * w.bh * 1e3
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(ms_full, 1), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"{done} of {w.bh} (batch, head) slices of the {WORKLOAD} workload, full chain "
                       f"(pool, select, forward, transpose, backward) in fp64; {t_all:.1f} s measured, "
                       f"scaled by {w.bh}/{done} to one step"}
@@ -167,12 +174,17 @@ def main():
                     help="also time dense PyTorch SDPA (flash / memory-efficient backend) at the same shapes")
     ap.add_argument("--complement", action="store_true",
                     help="also time the forward under the complement-partition reading of the enrichment")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time the other workloads: the forward chain (pool, select, forward) of the N = 4096 "
+                         "fp32, N = 16384 and N = 65536 forward workloads, the whole step of the N = 262144 one")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each follow a 1 GiB buffer write (L2 and MALL flushed)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of COPY_PROBE_BYTES after the warm-up (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE; see hierarchical_sparse_attention_mean_amd/profiling.py)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
               "(batch x heads) with no exchange, but only the one-GPU share is built and measured)",
               file=sys.stderr)
         sys.exit(2)
@@ -366,6 +378,58 @@ def main():
                       "workspace_bytes_bwd": ws_cb.numel()}
         del ws_c, o_c, lse_c, ws_cb, dq_c, dk_c, dv_c
 
+    cold = None
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(args.steps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del flush
+        cold = {"median_ms": round(float(np.median(times)), 4), "min_ms": round(min(times), 4),
+                "max_ms": round(max(times), 4), "steps": args.steps}
+
+    configs = None
+    if args.configs:
+        configs = {}
+        for name in ("tiny_fwd_f32_n4096", "fwd_bf16_n16384", "fwd_bf16_n65536", "fwdbwd_bf16_n262144"):
+            wc = inputs.WORKLOADS[name]
+            xc = inputs.make_inputs(wc)
+            tc = {}
+            for nm, tt in xc.items():
+                arr = tt.store
+                tc[nm] = (torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16) if arr.dtype == np.uint16
+                          else torch.from_numpy(np.ascontiguousarray(arr)).cuda())
+            bc = llsa.Buffers(llsa.problem(wc.batch, wc.heads, wc.n, wc.d, wc.block, wc.topk, wc.levels,
+                                           dtype=llsa.BF16 if wc.dtype == "bf16" else llsa.F32),
+                              backward=wc.backward)
+            if wc.backward:
+                def run_c():
+                    bc.forward_backward(tc["q"], tc["k"], tc["v"], tc["dout"], stream, side)
+            else:
+                def run_c():
+                    bc.forward(tc["q"], tc["k"], tc["v"], stream)
+            for _ in range(3):
+                run_c()
+            torch.cuda.synchronize()
+            reps = max(5, args.steps // 2)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                run_c()
+            torch.cuda.synchronize()
+            configs[name] = {"ms_per_step": round((time.perf_counter() - t0) * 1e3 / reps, 4),
+                             "step": "pool+select+forward+transpose+backward" if wc.backward
+                             else "pool+select+forward",
+                             "batch": wc.batch, "heads": wc.heads, "seq_len": wc.n, "dtype": wc.dtype, "topk": wc.topk,
+                             "levels": wc.levels}
+            del bc, tc, xc
+            torch.cuda.empty_cache()
+
     dense = None
     if args.dense:
         fwd_chain = sum(kernels[nm]["ms_per_step"] for nm in ("pool", "select", "attn_fwd"))
@@ -394,6 +458,8 @@ def main():
         "exhaustive_selection": exhaustive,
         "reordered_chain": reordered,
         "complement_forward": complement,
+        "cold_steps": cold,
+        "other_workloads": configs,
         "input_gen_s": round(gen_s, 1),
     }
     print(json.dumps(rec))
