@@ -140,6 +140,23 @@ def kernel_stats_summary(directory: str, title: str, command: str) -> str:
     return "\n".join(lines)
 
 
+def l2_hits_summary(directory: str, kernels: list, title: str, command: str) -> str:
+    """L2 (TCC) hit rate per kernel from a rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum run: mean per dispatch."""
+    path = _csv_in(directory)
+    hit, miss = _per_dispatch(path, "TCC_HIT_sum"), _per_dispatch(path, "TCC_MISS_sum")
+    lines = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             "| kernel | dispatches | L2 hits per dispatch | L2 misses per dispatch | hit rate |", "|---|---|---|---|---|"]
+    for k in kernels:
+        ds = [d for d, (nm, _) in hit.items() if k in nm and d in miss]
+        if not ds:
+            continue
+        h = sum(hit[d][1] for d in ds) / len(ds)
+        m = sum(miss[d][1] for d in ds) / len(ds)
+        lines.append(f"| {k} | {len(ds)} | {h:.4g} | {m:.4g} | {h / max(h + m, 1.0):.3f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -154,9 +171,16 @@ def main():
     t.add_argument("--kernel", required=True)
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
+    h = sub.add_parser("l2-hits")
+    h.add_argument("--dir", required=True)
+    h.add_argument("--kernels", required=True, help="comma-separated kernel name substrings")
+    h.add_argument("--title", required=True)
+    h.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "kernel-stats":
         print(kernel_stats_summary(a.dir, a.title, a.command))
+    elif a.cmd == "l2-hits":
+        print(l2_hits_summary(a.dir, a.kernels.split(","), a.title, a.command))
     else:
         print(traffic_summary(a.fetch, a.write, a.copy_bytes, a.kernel, a.workload, a.command))
 
