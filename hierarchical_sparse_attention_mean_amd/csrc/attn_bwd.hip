@@ -15,12 +15,16 @@
 //      reduces the four waves in LDS in a fixed order (partials per level-2 unit and slot).
 //   2. coarse_reduce: for each pooled token of levels >= 2, sums the partials of the (unit, slot) pairs
 //      that kept it, found through that level's CSC column (no atomics).
-//   3. bwd_dkdv (K-major, one wavefront per fine key block): walks the key block's CSC column of level 1
-//      -- the query blocks that kept it -- and accumulates dK, dV for its 16 keys.  The same query
-//      blocks are exactly those that attend the block's level-1 pooled token, so that token's gradient
-//      (scaled by B^-1) is folded into the same products, and the B^-l share of the level >= 2 tokens is
-//      added before the bf16 store.
-// Every gradient element is owned by one wavefront: no floating-point atomics, bitwise reproducible.
+//   3. dkdv_order, then bwd_dkdv (K-major, one wavefront per work item: a group of four key blocks, or a
+//      chunk of a long group's stages): walks the key blocks' CSC columns of level 1 -- the query blocks that
+//      kept them -- and accumulates dK, dV for their keys.  The same query blocks are exactly those that
+//      attend a block's level-1 pooled token, so that token's gradient (scaled by B^-1) is folded into the
+//      same products, and the B^-l share of the level >= 2 tokens is added before the bf16 store.  Chunks of
+//      a split group write fp32 partials; the last chunk to finish adds them in chunk order.
+// The complement reading of the enrichment (launch_attn_bwd_complement) runs bwd_dq over the complement
+// lists, its pooled-token gradients in complement.hip, and bwd_dkdv without the level-1 fold.
+// Every gradient element is summed in a fixed order: no floating-point atomics, bitwise reproducible (the
+// only atomic is the integer count of a split group's finished chunks).
 #include "common.hpp"
 #include "entries.hpp"
 #include "launch.hpp"
