@@ -41,6 +41,10 @@ CASES = [
     ("f32_n4096_K7_Le1", inputs.custom(1, 2, 4096, 64, "f32", seed=18, topk=7, levels=2), 2, 1),
     ("bf16_field_n65536_L3_h1", inputs.custom(1, 1, 65536, 64, "bf16", seed=19, kind="field", topk=8, levels=3,
                                               backward=True), 3, -1),
+    # the largest coarsest level (n_L = 512 candidates per unit), the largest K, the deepest pyramid (L = 4)
+    ("bf16_n8192_L1_nL512", inputs.custom(1, 1, 8192, 64, "bf16", seed=23, topk=8, levels=1, backward=True), 1, -1),
+    ("bf16_n65536_L2_K32", inputs.custom(1, 1, 65536, 64, "bf16", seed=24, topk=32, levels=2, backward=True), 2, -1),
+    ("bf16_n1048576_L4", inputs.custom(1, 1, 1 << 20, 64, "bf16", seed=25, topk=8, levels=4, backward=True), 4, -1),
     # hub inputs: a few key blocks kept by every query block, so the dK/dV kernel splits their groups
     ("bf16_hub_n4096_split", inputs.custom(1, 2, 4096, 64, "bf16", seed=21, kind="hub", topk=8, levels=2,
                                            backward=True), 2, -1),
