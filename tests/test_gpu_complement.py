@@ -123,6 +123,8 @@ BWD_CASES = [
     ("field_n65536_L3", inputs.custom(1, 1, 65536, 64, "bf16", seed=48, kind="field", topk=8, levels=3,
                                       backward=True), 3, -1),
     ("n65536_L3_Le2", inputs.custom(1, 1, 65536, 64, "bf16", seed=49, topk=4, levels=3, backward=True), 3, 2),
+    # 504 entries per fine block: all but K of the 512 coarsest blocks
+    ("n8192_L1_nL512", inputs.custom(1, 2, 8192, 64, "bf16", seed=50, topk=8, levels=1, backward=True), 1, -1),
 ]
 
 
