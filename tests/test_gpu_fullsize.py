@@ -104,3 +104,34 @@ def test_fullsize_fwd_n16384_8_heads(L):
         lse_err = np.abs(host(b.lse).reshape(w.bh, w.n)[s] - ref["lse"][0]).max()
         assert lse_err <= 2e-2, lse_err
         print(f"{w.name} slice {s}: selection rows compared {compared}/{total}, O {worst:.2e}, lse {lse_err:.2e}")
+
+
+def test_two_stream_chain_matches_one_stream(L):
+    """The chain as bench.py times it -- the index transpose on a second stream, beside the forward
+    (Buffers.forward_backward) -- gives bit for bit what the one-stream chain gives, over back-to-back steps on
+    alternating inputs with no synchronisation between them (each step's outputs are copied on the main stream
+    before the next step starts), so that a step that overtook its predecessor's reads would show."""
+    import dataclasses
+    w = inputs.WORKLOADS["fwdbwd_bf16_n65536"]
+    sets = []
+    for seed in (w.seed, w.seed + 1):
+        x = inputs.make_inputs(dataclasses.replace(w, seed=seed), with_dout=True)
+        sets.append([_dev(x[nm]) for nm in ("q", "k", "v", "dout")])
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    outs = lambda: [t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)]
+    ref = []
+    for q, k, v, do in sets:
+        b.forward(q, k, v)
+        b.backward(q, k, v, do)
+        ref.append(outs())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    got = []
+    for s in (0, 1, 0, 1):
+        b.forward_backward(*sets[s], stream, side)
+        got.append((s, outs()))
+    torch.cuda.synchronize()
+    for s, g in got:
+        for nm, a, r in zip(("idx", "O", "lse", "dq", "dk", "dv"), g, ref[s]):
+            assert torch.equal(a, r), (s, nm)
