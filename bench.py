@@ -30,6 +30,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "LLSA fwd+bwd ms at N=65536 (MFMA util %, selection HBM GB/s)"
 COPY_PROBE_BYTES = 256 << 20
 WORKLOAD = "fwdbwd_bf16_n65536"
+WARM_STEPS = 50                # steps of the per-step (median, min, max) distributions
 
 
 KERNEL_SYMBOL = {"pool": "pool_levels12", "select": "select_level", "attn_fwd": "attn_fwd_bf16",
@@ -162,7 +163,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--reorder", action="store_true",
@@ -177,8 +178,8 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="also time the other workloads: the forward chain (pool, select, forward) of the N = 4096 "
                          "fp32, N = 16384 and N = 65536 forward workloads, the whole step of the N = 262144 one")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps that each follow a 1 GiB buffer write (L2 and MALL flushed)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the per-step timings that each follow a 1 GiB buffer write (L2 and MALL flushed)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain device copy of COPY_PROBE_BYTES after the warm-up (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE; see hierarchical_sparse_attention_mean_amd/profiling.py)")
@@ -378,21 +379,29 @@ def main():
                       "workspace_bytes_bwd": ws_cb.numel()}
         del ws_c, o_c, lse_c, ws_cb, dq_c, dk_c, dv_c
 
-    cold = None
-    if args.cold:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # per-step distributions (hipEvents on the main stream, which joins the side stream before the backward):
+    # warm = steps back to back as above, each timed alone; cold = each step right after a 1 GiB buffer write,
+    # which flushes the L2s and the MALL
+    def step_times(n, flush=None):
         times = []
-        for _ in range(args.steps):
-            flush.fill_(1)
+        for _ in range(n):
+            if flush is not None:
+                flush.fill_(1)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             step()
             e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
+        return {"median_ms": round(float(np.median(times)), 4), "min_ms": round(min(times), 4),
+                "max_ms": round(max(times), 4), "steps": n}
+
+    warm = step_times(WARM_STEPS)
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = step_times(WARM_STEPS, flush)
         del flush
-        cold = {"median_ms": round(float(np.median(times)), 4), "min_ms": round(min(times), 4),
-                "max_ms": round(max(times), 4), "steps": args.steps}
 
     configs = None
     if args.configs:
@@ -458,6 +467,7 @@ def main():
         "exhaustive_selection": exhaustive,
         "reordered_chain": reordered,
         "complement_forward": complement,
+        "warm_steps": warm,
         "cold_steps": cold,
         "other_workloads": configs,
         "input_gen_s": round(gen_s, 1),
