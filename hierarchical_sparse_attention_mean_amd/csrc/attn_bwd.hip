@@ -155,17 +155,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   int ij = 0, is = 0;
   Blk cur = blk(0), nxt = blk(1);
   float dlt = 0.f, lse2 = 0.f;
-  // B operands (natural order) of the current block's Q and dO rows, re-read from their slots at each stage
-  // (holding them in registers would push the kernel past its register budget)
-  auto qd_ops = [&](bf16x8& qa0, bf16x8& qa1, bf16x8& da0, bf16x8& da1) {
-    const int c7 = c & 7;
-    const bf16_t* qr = &qsl[w][par][c * kD];
-    const bf16_t* dr = &dsl[w][par][c * kD];
-    qa0 = *reinterpret_cast<const bf16x8*>(qr + ((gq ^ c7) << 3));
-    qa1 = *reinterpret_cast<const bf16x8*>(qr + (((4 + gq) ^ c7) << 3));
-    da0 = *reinterpret_cast<const bf16x8*>(dr + ((gq ^ c7) << 3));
-    da1 = *reinterpret_cast<const bf16x8*>(dr + (((4 + gq) ^ c7) << 3));
-  };
+  // B operands (natural order) of the current block's Q and dO rows, read from their slots at block start
+  bf16x8 qa0, qa1, da0, da1;
   f32x4 dq_acc[4], gk_acc[kT][4], gv_acc[kT][4];
 #pragma unroll
   for (int T = 0; T < kT; ++T)
@@ -178,11 +169,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     const bf16_t* qr = &qsl[w][par][c * kD];
     const bf16_t* dr = &dsl[w][par][c * kD];
     const bf16_t* orr = &osl[w][c * kD];
-    (void)qr;
     const uint4 d0 = *reinterpret_cast<const uint4*>(dr + ((gq ^ c7) << 3));
     const uint4 d1 = *reinterpret_cast<const uint4*>(dr + (((4 + gq) ^ c7) << 3));
     const uint4 o0 = *reinterpret_cast<const uint4*>(orr + ((gq ^ c7) << 3));
     const uint4 o1 = *reinterpret_cast<const uint4*>(orr + (((4 + gq) ^ c7) << 3));
+    qa0 = *reinterpret_cast<const bf16x8*>(qr + ((gq ^ c7) << 3));
+    qa1 = *reinterpret_cast<const bf16x8*>(qr + (((4 + gq) ^ c7) << 3));
+    da0 = as_bf16x8(d0);
+    da1 = as_bf16x8(d1);
     lse2 = lsl[w][par][c] * kLog2e;
     wait_lds();  // the O slot is refilled below
     dlt = group_sum(dot16_bf16(d0, d1, o0, o1));
@@ -261,8 +255,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     }
     const int c7 = c & 7;
     const int a0 = c * kD + ((gq ^ c7) << 3), a1 = c * kD + (((4 + gq) ^ c7) << 3);
-    bf16x8 qa0, qa1, da0, da1;
-    qd_ops(qa0, qa1, da0, da1);
     float ds[8], pr[8];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
