@@ -26,7 +26,8 @@ namespace llsa {
 namespace {
 
 constexpr int kMaxSlotsPerLane = 8;  // up to 512 candidates per query row
-constexpr int kRoundsMaxK = 8;       // Top-K by rounds of maxima up to this K (and 128 candidates), else bitwise search
+constexpr int kMergeMaxK = 8;        // Top-K by sorted-list merges up to this K and kMergeMaxCand candidates,
+constexpr int kMergeMaxCand = 128;   // else the bitwise threshold search
 
 // Order-preserving map of an fp32 score to uint32 (+0 and -0 compare equal).
 __device__ __forceinline__ uint32_t ord_key(float s) {
@@ -107,92 +108,92 @@ __device__ __forceinline__ void topk_rows(const float* sc, int ldc, int ncand, i
   }
 }
 
-// Wave-wide maximum of an unsigned value (every lane gets it): xor 1 and 2 within quads, rotations by 4 and 8
-// within 16-lane rows (DPP), then the row and half swaps.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1 /* quad_perm [1,0,3,2] */, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E /* quad_perm [2,3,0,1] */, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124 /* row_ror:4 */, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128 /* row_ror:8 */, 0xf, 0xf, false));
-  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = max((uint32_t)a[0], (uint32_t)a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max((uint32_t)b[0], (uint32_t)b[1]);
+// Compare-exchange of two keys, the larger first.
+__device__ __forceinline__ void cx(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = max(a, b), lo = min(a, b);
+  a = hi;
+  b = lo;
 }
 
-// The same Top-K by K rounds of "take the largest remaining key, the lowest slot among equal ones" -- the order
-// (score descending, block index ascending) of the tie rule -- for small K: per round one wave maximum on the
-// vector unit and two ballots, where the bitwise search spends 32 scalar-heavy steps.  Rows interleaved as
-// above; the kept slots are compacted in slot order at the end.
-template <int kM>
-__device__ __forceinline__ void topk_rows_rounds(const float* sc, int ldc, int ncand, int nq, int K, int w,
-                                                 int lane, int32_t* out_rows, const int32_t* picks, int coarsest) {
-  constexpr int kR = 4;
-  uint32_t key[kR][kM];
-  uint32_t kept[kR][kM];
+// One merge step of the per-lane sorted (descending) 8-key lists: the partner lane's list comes over DPP
+// (`ctrl`), the element-wise maxima of this list and the partner's reversed list are the 8 largest keys of the
+// two (a bitonic sequence), and a half-cleaner network sorts them again.
+template <int kCtrl>
+__device__ __forceinline__ void merge8(uint32_t t[8]) {
+  uint32_t c[8];
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int row = 4 * w + r;
+  for (int i = 0; i < 8; ++i)
+    c[i] = max(t[i], (uint32_t)__builtin_amdgcn_mov_dpp((int)t[7 - i], kCtrl, 0xf, 0xf, false));
 #pragma unroll
-    for (int m = 0; m < kM; ++m) {
-      const int s = lane + 64 * m;
-      key[r][m] = (row < nq && s < ncand) ? ord_key(sc[row * ldc + s]) : 0u;  // real keys are >= 0x007FFFFF
-      kept[r][m] = 0u;
-    }
+  for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & d) == 0) cx(c[i], c[i + d]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = c[i];
+}
+
+// Top-K for K <= 8 and at most 128 candidates.  Row 4w + r of the workgroup goes to quarter-wave r (lanes
+// 16r .. 16r+15); lane l16 holds the 8 slots l16 + 16i.
+//   1. Each lane sorts its 8 keys (a 19-comparator network).
+//   2. Four merge steps with the lanes 1 and 2 apart (quad swaps), then 4 and 8 apart (row rotations): every
+//      lane of the quarter ends up with the row's 8 largest keys, sorted.  The K-th of them is the threshold T.
+//   3. The kept slots are taken as in topk_rows: keys above T, then keys equal to T in ascending slot order,
+//      compacted in ascending slot order with ballot prefix counts restricted to the quarter.
+// So the result equals the exact Top-K with ties to the lower slot (the lower block index).
+__device__ __forceinline__ void topk_rows_merge(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
+                                                int32_t* out_rows, const int32_t* picks, int coarsest) {
+  const int r = lane >> 4, l16 = lane & 15, row = 4 * w + r;
+  const bool live = row < nq;
+  uint32_t key[8], t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = l16 + 16 * i;
+    // invalid slots and rows past nq get key 0, below every real score's key (-inf maps to 0x007FFFFF)
+    key[i] = (live && s < ncand) ? ord_key(sc[row * ldc + s]) : 0u;
+    t[i] = key[i];
   }
-  for (int i = 0; i < K; ++i) {
+  cx(t[0], t[2]); cx(t[1], t[3]); cx(t[4], t[6]); cx(t[5], t[7]);
+  cx(t[0], t[4]); cx(t[1], t[5]); cx(t[2], t[6]); cx(t[3], t[7]);
+  cx(t[0], t[1]); cx(t[2], t[3]); cx(t[4], t[5]); cx(t[6], t[7]);
+  cx(t[2], t[4]); cx(t[3], t[5]);
+  cx(t[1], t[4]); cx(t[3], t[6]);
+  cx(t[1], t[2]); cx(t[3], t[4]); cx(t[5], t[6]);
+  merge8<0xB1 /* quad_perm [1,0,3,2] */>(t);
+  merge8<0x4E /* quad_perm [2,3,0,1] */>(t);
+  merge8<0x124 /* row_ror:4 */>(t);
+  merge8<0x128 /* row_ror:8 */>(t);
+  uint32_t T = t[0];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      uint32_t v = key[r][0];
+  for (int i = 1; i < 8; ++i) T = i == K - 1 ? t[i] : T;
+  const uint64_t qmask = 0xFFFFull << (16 * r);
+  int greater = 0;
 #pragma unroll
-      for (int m = 1; m < kM; ++m) v = max(v, key[r][m]);
-      const uint32_t mx = wave_max_u32(v);
-      // lowest slot holding mx: the first group m with a match, its lowest lane
-      int pick_m = kM, pick_l = 0;
+  for (int i = 0; i < 8; ++i) greater += popc64(__ballot(key[i] > T) & qmask);
+  const int need = K - greater;  // ties at T to take, lowest slots first
+  int eq_before = 0, sel_before = 0;
+  int32_t* out = out_rows + (size_t)row * K;
 #pragma unroll
-      for (int m = kM - 1; m >= 0; --m) {
-        const uint64_t b = __ballot(key[r][m] == mx);
-        if (b) {
-          pick_m = m;
-          pick_l = (int)__builtin_ctzll(b);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < kM; ++m) {
-        const bool hit = m == pick_m && lane == pick_l;
-        kept[r][m] |= hit ? 1u : 0u;
-        key[r][m] = hit ? 0u : key[r][m];
-      }
+  for (int i = 0; i < 8; ++i) {
+    const uint64_t eqm = __ballot(key[i] == T) & qmask;
+    const bool sel = key[i] > T || (key[i] == T && eq_before + lanes_below(eqm) < need);
+    const uint64_t selm = __ballot(sel) & qmask;
+    if (sel && live) {
+      const int s = l16 + 16 * i;
+      const int blk = coarsest ? s : picks[s >> 4] * kB + (s & 15);
+      out[sel_before + lanes_below(selm)] = blk;
     }
-  }
-#pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int row = 4 * w + r;
-    if (row >= nq) break;
-    int32_t* out = out_rows + (size_t)row * K;
-    int sel_before = 0;
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-      const uint64_t selm = __ballot(kept[r][m] != 0u);
-      if (kept[r][m]) {
-        const int s = lane + 64 * m;
-        const int blk = coarsest ? s : picks[s >> 4] * kB + (s & 15);
-        out[sel_before + lanes_below(selm)] = blk;
-      }
-      sel_before += popc64(selm);
-    }
+    eq_before += popc64(eqm);
+    sel_before += popc64(selm);
   }
 }
 
 __device__ __forceinline__ void topk_dispatch(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
                                               int32_t* out_rows, const int32_t* picks, int coarsest) {
   const int M = (ncand + 63) / 64;
-  if (K <= kRoundsMaxK && M <= 2) {
-    if (M <= 1)
-      topk_rows_rounds<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-    else
-      topk_rows_rounds<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-  } else if (M <= 1)
+  if (K <= kMergeMaxK && ncand <= kMergeMaxCand)
+    topk_rows_merge(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  else if (M <= 1)
     topk_rows<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
   else if (M == 2)
     topk_rows<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
