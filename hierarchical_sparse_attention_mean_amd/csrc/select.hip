@@ -26,8 +26,10 @@ namespace llsa {
 namespace {
 
 constexpr int kMaxSlotsPerLane = 8;  // up to 512 candidates per query row
-constexpr int kMergeMaxK = 8;        // Top-K by sorted-list merges up to this K and kMergeMaxCand candidates,
-constexpr int kMergeMaxCand = 128;   // else the bitwise threshold search
+// Top-K modes (a template parameter of select_level, so that each instance holds only its own registers):
+// sorted-list merges of 8 keys per lane (K <= 8, at most 128 candidates), of 16 keys per lane (K <= 16, at most
+// 256 candidates), else the bitwise threshold search.
+enum TopkMode { kMerge8 = 0, kMerge16 = 1, kBitwise = 2 };
 
 // Order-preserving map of an fp32 score to uint32 (+0 and -0 compare equal).
 __device__ __forceinline__ uint32_t ord_key(float s) {
@@ -115,66 +117,88 @@ __device__ __forceinline__ void cx(uint32_t& a, uint32_t& b) {
   b = lo;
 }
 
-// One merge step of the per-lane sorted (descending) 8-key lists: the partner lane's list comes over DPP
-// (`ctrl`), the element-wise maxima of this list and the partner's reversed list are the 8 largest keys of the
-// two (a bitonic sequence), and a half-cleaner network sorts them again.
-template <int kCtrl>
-__device__ __forceinline__ void merge8(uint32_t t[8]) {
-  uint32_t c[8];
+// Sorts a lane's kL keys, largest first: the 19-comparator network for 8 keys, a bitonic network for 16.
+template <int kL>
+__device__ __forceinline__ void sort_desc(uint32_t t[kL]) {
+  if constexpr (kL == 8) {
+    cx(t[0], t[2]); cx(t[1], t[3]); cx(t[4], t[6]); cx(t[5], t[7]);
+    cx(t[0], t[4]); cx(t[1], t[5]); cx(t[2], t[6]); cx(t[3], t[7]);
+    cx(t[0], t[1]); cx(t[2], t[3]); cx(t[4], t[5]); cx(t[6], t[7]);
+    cx(t[2], t[4]); cx(t[3], t[5]);
+    cx(t[1], t[4]); cx(t[3], t[6]);
+    cx(t[1], t[2]); cx(t[3], t[4]); cx(t[5], t[6]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    c[i] = max(t[i], (uint32_t)__builtin_amdgcn_mov_dpp((int)t[7 - i], kCtrl, 0xf, 0xf, false));
+    for (int k = 2; k <= kL; k <<= 1)
 #pragma unroll
-  for (int d = 4; d >= 1; d >>= 1)
+      for (int j = k >> 1; j >= 1; j >>= 1)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if ((i & d) == 0) cx(c[i], c[i + d]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = c[i];
+        for (int i = 0; i < kL; ++i)
+          if ((i ^ j) > i) {
+            if ((i & k) == 0)
+              cx(t[i], t[i ^ j]);
+            else
+              cx(t[i ^ j], t[i]);
+          }
+  }
 }
 
-// Top-K for K <= 8 and at most 128 candidates.  Row 4w + r of the workgroup goes to quarter-wave r (lanes
-// 16r .. 16r+15); lane l16 holds the 8 slots l16 + 16i.
-//   1. Each lane sorts its 8 keys (a 19-comparator network).
+// One merge step of the per-lane sorted (descending) kL-key lists: the partner lane's list comes over DPP
+// (`kCtrl`), the element-wise maxima of this list and the partner's reversed list are the kL largest keys of
+// the two (a bitonic sequence), and a half-cleaner network sorts them again.
+template <int kL, int kCtrl>
+__device__ __forceinline__ void merge_lists(uint32_t t[kL]) {
+  uint32_t c[kL];
+#pragma unroll
+  for (int i = 0; i < kL; ++i)
+    c[i] = max(t[i], (uint32_t)__builtin_amdgcn_mov_dpp((int)t[kL - 1 - i], kCtrl, 0xf, 0xf, false));
+#pragma unroll
+  for (int d = kL / 2; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < kL; ++i)
+      if ((i & d) == 0) cx(c[i], c[i + d]);
+#pragma unroll
+  for (int i = 0; i < kL; ++i) t[i] = c[i];
+}
+
+// Top-K for K <= kL and at most 16 kL candidates.  Row 4w + r of the workgroup goes to quarter-wave r (lanes
+// 16r .. 16r+15); lane l16 holds the kL slots l16 + 16i.
+//   1. Each lane sorts its keys (sort_desc).
 //   2. Four merge steps with the lanes 1 and 2 apart (quad swaps), then 4 and 8 apart (row rotations): every
-//      lane of the quarter ends up with the row's 8 largest keys, sorted.  The K-th of them is the threshold T.
+//      lane of the quarter ends up with the row's kL largest keys, sorted.  The K-th of them is the threshold T.
 //   3. The kept slots are taken as in topk_rows: keys above T, then keys equal to T in ascending slot order,
 //      compacted in ascending slot order with ballot prefix counts restricted to the quarter.
 // So the result equals the exact Top-K with ties to the lower slot (the lower block index).
+template <int kL>
 __device__ __forceinline__ void topk_rows_merge(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
                                                 int32_t* out_rows, const int32_t* picks, int coarsest) {
   const int r = lane >> 4, l16 = lane & 15, row = 4 * w + r;
   const bool live = row < nq;
-  uint32_t key[8], t[8];
+  uint32_t key[kL], t[kL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kL; ++i) {
     const int s = l16 + 16 * i;
     // invalid slots and rows past nq get key 0, below every real score's key (-inf maps to 0x007FFFFF)
     key[i] = (live && s < ncand) ? ord_key(sc[row * ldc + s]) : 0u;
     t[i] = key[i];
   }
-  cx(t[0], t[2]); cx(t[1], t[3]); cx(t[4], t[6]); cx(t[5], t[7]);
-  cx(t[0], t[4]); cx(t[1], t[5]); cx(t[2], t[6]); cx(t[3], t[7]);
-  cx(t[0], t[1]); cx(t[2], t[3]); cx(t[4], t[5]); cx(t[6], t[7]);
-  cx(t[2], t[4]); cx(t[3], t[5]);
-  cx(t[1], t[4]); cx(t[3], t[6]);
-  cx(t[1], t[2]); cx(t[3], t[4]); cx(t[5], t[6]);
-  merge8<0xB1 /* quad_perm [1,0,3,2] */>(t);
-  merge8<0x4E /* quad_perm [2,3,0,1] */>(t);
-  merge8<0x124 /* row_ror:4 */>(t);
-  merge8<0x128 /* row_ror:8 */>(t);
+  sort_desc<kL>(t);
+  merge_lists<kL, 0xB1 /* quad_perm [1,0,3,2] */>(t);
+  merge_lists<kL, 0x4E /* quad_perm [2,3,0,1] */>(t);
+  merge_lists<kL, 0x124 /* row_ror:4 */>(t);
+  merge_lists<kL, 0x128 /* row_ror:8 */>(t);
   uint32_t T = t[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) T = i == K - 1 ? t[i] : T;
+  for (int i = 1; i < kL; ++i) T = i == K - 1 ? t[i] : T;
   const uint64_t qmask = 0xFFFFull << (16 * r);
   int greater = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) greater += popc64(__ballot(key[i] > T) & qmask);
+  for (int i = 0; i < kL; ++i) greater += popc64(__ballot(key[i] > T) & qmask);
   const int need = K - greater;  // ties at T to take, lowest slots first
   int eq_before = 0, sel_before = 0;
   int32_t* out = out_rows + (size_t)row * K;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kL; ++i) {
     const uint64_t eqm = __ballot(key[i] == T) & qmask;
     const bool sel = key[i] > T || (key[i] == T && eq_before + lanes_below(eqm) < need);
     const uint64_t selm = __ballot(sel) & qmask;
@@ -188,24 +212,34 @@ __device__ __forceinline__ void topk_rows_merge(const float* sc, int ldc, int nc
   }
 }
 
+__host__ __device__ constexpr int topk_mode(int K, int ncand) {
+  return (K <= 8 && ncand <= 128) ? kMerge8 : (K <= 16 && ncand <= 256) ? kMerge16 : kBitwise;
+}
+
+template <int kMode>
 __device__ __forceinline__ void topk_dispatch(const float* sc, int ldc, int ncand, int nq, int K, int w, int lane,
                                               int32_t* out_rows, const int32_t* picks, int coarsest) {
-  const int M = (ncand + 63) / 64;
-  if (K <= kMergeMaxK && ncand <= kMergeMaxCand)
-    topk_rows_merge(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-  else if (M <= 1)
-    topk_rows<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-  else if (M == 2)
-    topk_rows<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-  else if (M <= 4)
-    topk_rows<4>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
-  else
-    topk_rows<kMaxSlotsPerLane>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  if constexpr (kMode == kMerge8) {
+    topk_rows_merge<8>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  } else if constexpr (kMode == kMerge16) {
+    topk_rows_merge<16>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  } else {
+    const int M = (ncand + 63) / 64;
+    if (M <= 1)
+      topk_rows<1>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+    else if (M == 2)
+      topk_rows<2>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+    else if (M <= 4)
+      topk_rows<4>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+    else
+      topk_rows<kMaxSlotsPerLane>(sc, ldc, ncand, nq, K, w, lane, out_rows, picks, coarsest);
+  }
 }
 
 // Coarsest: grid.x = 16-row query tiles, grid.y = slice.  Descent: 1-D grid over (slice, parent unit at
 // level+1), remapped so that consecutive parents run on one XCD and its L2 holds their slices' pooled keys.
 // Dynamic LDS: 16 rows x ldc floats of scores.
+template <int kMode>
 __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq, const float* __restrict__ pk,
                                                     int32_t* __restrict__ idx, Geom g, int level, int coarsest,
                                                     int ncand, int ldc) {
@@ -287,7 +321,7 @@ __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq
   }
   __syncthreads();
 
-  topk_dispatch(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, pks, coarsest);
+  topk_dispatch<kMode>(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, pks, coarsest);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -424,6 +458,22 @@ __global__ __launch_bounds__(256) void select_exhaustive(const float* __restrict
 
 }  // namespace
 
+// select_level's instance for the level's Top-K mode
+static void launch_select_level(dim3 grid, int ldc, hipStream_t stream, const float* pq, const float* pk, int32_t* idx,
+                         const Geom& g, int level, int coarsest, int ncand) {
+  const size_t lds = 16 * ldc * sizeof(float);
+  switch (topk_mode(g.K, ncand)) {
+    case kMerge8:
+      select_level<kMerge8><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+      break;
+    case kMerge16:
+      select_level<kMerge16><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+      break;
+    default:
+      select_level<kBitwise><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+  }
+}
+
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream) {
   // coarsest level: all n_L blocks are candidates
   {
@@ -432,7 +482,7 @@ hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_
     const int ldc = ncand + 4;
     dim3 grid((nL + 15) / 16, g.bh);
     LaunchTimer timer(kSelect, stream);
-    select_level<<<grid, 256, 16 * ldc * sizeof(float), stream>>>(pq, pk, idx, g, g.L, 1, nL, ldc);
+    launch_select_level(grid, ldc, stream, pq, pk, idx, g, g.L, 1, nL);
   }
   for (int l = g.L - 1; l >= 1; --l) {
     const int ncand = g.K * kB;
@@ -440,7 +490,7 @@ hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_
     // one workgroup per (slice, parent), on a 1-D grid remapped so that an XCD takes consecutive parents
     const int grid = g.rows[l + 1] * g.bh;
     LaunchTimer timer(kSelect, stream);
-    select_level<<<grid, 256, 16 * ldc * sizeof(float), stream>>>(pq, pk, idx, g, l, 0, ncand, ldc);
+    launch_select_level(dim3(grid), ldc, stream, pq, pk, idx, g, l, 0, ncand);
   }
   return hipGetLastError();
 }
