@@ -319,8 +319,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     const uint4 x0 = *reinterpret_cast<const uint4*>(kt + r * kD + ((ch ^ r) << 3));
     const uint4 x1 = *reinterpret_cast<const uint4*>(kt + (8 + r) * kD + ((ch ^ r) << 3));
     bf16_t* ob = dq + cur.slice * slice_elems + (size_t)16 * cur.i * kD + r * kD + 8 * ch;
-    st16(ob, x0);
-    st16(ob + 8 * kD, x1);
+    st16_nt(ob, x0);
+    st16_nt(ob + 8 * kD, x1);
   };
 
   // End of the workgroup's ju-th unit: fixed-order reduction of the four waves' partials through LDS (the
@@ -771,10 +771,10 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
     const int r = lane >> 3, ch = lane & 7;
     const int o0 = r * kD + ((ch ^ r) << 3);
     const size_t go = base + ((size_t)16 * (j0 + b) + r) * kD + 8 * ch;
-    st16(dk + go, *reinterpret_cast<const uint4*>(qt + o0));
-    st16(dk + go + 8 * kD, *reinterpret_cast<const uint4*>(qt + o0 + 8 * kD));
-    st16(dv + go, *reinterpret_cast<const uint4*>(dt + o0));
-    st16(dv + go + 8 * kD, *reinterpret_cast<const uint4*>(dt + o0 + 8 * kD));
+    st16_nt(dk + go, *reinterpret_cast<const uint4*>(qt + o0));
+    st16_nt(dk + go + 8 * kD, *reinterpret_cast<const uint4*>(qt + o0 + 8 * kD));
+    st16_nt(dv + go, *reinterpret_cast<const uint4*>(dt + o0));
+    st16_nt(dv + go + 8 * kD, *reinterpret_cast<const uint4*>(dt + o0 + 8 * kD));
   };
 
   int cb = next_nonempty(-1);  // key block being consumed
@@ -961,13 +961,13 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
       }
     }
     const size_t go = base + ((size_t)16 * (j0 + b) + key) * kD + d0;
-    st16(dk + go, make_uint4(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]), pack_bf16x2(kx[4], kx[5]),
+    st16_nt(dk + go, make_uint4(pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3]), pack_bf16x2(kx[4], kx[5]),
                              pack_bf16x2(kx[6], kx[7])));
-    st16(dk + go + 8, make_uint4(pack_bf16x2(kx[8], kx[9]), pack_bf16x2(kx[10], kx[11]),
+    st16_nt(dk + go + 8, make_uint4(pack_bf16x2(kx[8], kx[9]), pack_bf16x2(kx[10], kx[11]),
                                  pack_bf16x2(kx[12], kx[13]), pack_bf16x2(kx[14], kx[15])));
-    st16(dv + go, make_uint4(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]), pack_bf16x2(vx[4], vx[5]),
+    st16_nt(dv + go, make_uint4(pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3]), pack_bf16x2(vx[4], vx[5]),
                              pack_bf16x2(vx[6], vx[7])));
-    st16(dv + go + 8, make_uint4(pack_bf16x2(vx[8], vx[9]), pack_bf16x2(vx[10], vx[11]),
+    st16_nt(dv + go + 8, make_uint4(pack_bf16x2(vx[8], vx[9]), pack_bf16x2(vx[10], vx[11]),
                                  pack_bf16x2(vx[12], vx[13]), pack_bf16x2(vx[14], vx[15])));
   }
 }

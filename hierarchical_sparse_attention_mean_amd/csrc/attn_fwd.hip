@@ -219,8 +219,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     const int ro = (lane >> 3) * kLd + 8 * (lane & 7), go = (lane >> 3) * kD + 8 * (lane & 7);
     const uint4 o0 = *reinterpret_cast<const uint4*>(kt + ro);
     const uint4 o1 = *reinterpret_cast<const uint4*>(kt + ro + 8 * kLd);
-    st16(ob + go, o0);
-    st16(ob + go + 8 * kD, o1);
+    st16_nt(ob + go, o0);
+    st16_nt(ob + go + 8 * kD, o1);
     if (gq == 0) lse[(size_t)cslice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
   };
 

@@ -121,7 +121,13 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
 
 // 16-byte global loads / stores.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // for the non-temporal builtins
+// Non-temporal 16-byte store, for the attention outputs (O, dQ, dK, dV), which nothing in the same pass reads
+// back soon: written through, they leave the caches to the K, V, Q and dO rows the kernels still gather.
+__device__ __forceinline__ void st16_nt(void* p, uint4 v) {
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;

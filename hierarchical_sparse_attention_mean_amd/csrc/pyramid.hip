@@ -19,8 +19,6 @@ namespace llsa {
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 template <typename T>
 struct ChunkRegs;
 
