@@ -127,12 +127,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   auto prefetch = [&](int j, int p) {
     const Blk b = blk(j);
     const size_t rb = b.slice * slice_elems + (size_t)16 * b.i * kD + swz_dma_src(lane);
-    lds_dma16(q + rb, &qsl[w][p][0]);
-    lds_dma16(q + rb + 8 * kD, &qsl[w][p][8 * kD]);
-    lds_dma16(dout + rb, &dsl[w][p][0]);
-    lds_dma16(dout + rb + 8 * kD, &dsl[w][p][8 * kD]);
-    lds_dma16(o + rb, &osl[w][0]);
-    lds_dma16(o + rb + 8 * kD, &osl[w][8 * kD]);
+    lds_dma16_nt(q + rb, &qsl[w][p][0]);
+    lds_dma16_nt(q + rb + 8 * kD, &qsl[w][p][8 * kD]);
+    lds_dma16_nt(dout + rb, &dsl[w][p][0]);
+    lds_dma16_nt(dout + rb + 8 * kD, &dsl[w][p][8 * kD]);
+    lds_dma16_nt(o + rb, &osl[w][0]);
+    lds_dma16_nt(o + rb + 8 * kD, &osl[w][8 * kD]);
     if (lane < 16) lds_dma4(lse + (size_t)b.slice * g.n + 16 * b.i + lane, &lsl[w][p][0]);
     const int32_t* I = idx + (size_t)b.slice * g.R * g.K;
     if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + b.i) * g.K + lane, &is1[w][p][0]);

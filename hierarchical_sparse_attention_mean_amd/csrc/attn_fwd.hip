@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
     const int gb = wb.first + wb.stride * min(j, wb.count - 1);
     const int slice = uniform(gb / g.rows[1]), i = gb - slice * g.rows[1];
     const bf16_t* qrows = q + slice * slice_elems + (size_t)16 * i * kD;  // 2 KB, contiguous
-    lds_dma16(qrows + 8 * lane, &qs[w][0]);
-    lds_dma16(qrows + 512 + 8 * lane, &qs[w][512]);
+    lds_dma16_nt(qrows + 8 * lane, &qs[w][0]);
+    lds_dma16_nt(qrows + 512 + 8 * lane, &qs[w][512]);
     const int32_t* I = idx + (size_t)slice * g.R * g.K;
     if (lane < g.K) lds_dma4(I + (size_t)(g.off[1] + i) * g.K + lane, &is1[w][p][0]);
     const int32_t* E = esrc + slice * esrc_slice;

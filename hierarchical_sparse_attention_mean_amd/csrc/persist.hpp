@@ -18,6 +18,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void lds_dma16(const void* src, const void* dst) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
 }
+// The same copy with the non-temporal hint, for rows a kernel reads once (a block's Q, dO, O rows): they then
+// leave the caches to the gathered K and V rows.
+__device__ __forceinline__ void lds_dma16_nt(const void* src, const void* dst) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
 __device__ __forceinline__ void lds_dma4(const void* src, const void* dst) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
 }
