@@ -22,20 +22,21 @@ namespace {
 template <typename T>
 struct ChunkRegs;
 
-// bf16: 8 rows x 8 dims = 8 x 16 bytes per thread.  nt: non-temporal loads (used for Q, which nothing after
-// the pyramid gathers: the attention kernels gather K and V rows, some of which then still sit in the caches;
-// measured 0.909 -> 0.900 ms per N = 65536 step, against 0.902 ms with all three tensors non-temporal).
+// bf16: 8 rows x 8 dims = 8 x 16 bytes per thread, non-temporal loads: the raw tensors are read once here, and
+// the attention kernels then gather K and V from HBM with the caches left to their gathers (two-stream step at
+// N = 65536: 0.906 -> 0.897 ms with Q non-temporal, then -> 0.864 ms for all three once the attention kernels'
+// own once-read rows and outputs were non-temporal too).
 template <>
 struct ChunkRegs<bf16_t> {
   uint4 r[8];
-  __device__ void load(const bf16_t* base, int valid, bool nt) {
+  __device__ void load(const bf16_t* base, int valid) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (valid && nt) {
+      if (valid) {
         const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + j * kD));
         r[j] = make_uint4(x.x, x.y, x.z, x.w);
       } else {
-        r[j] = valid ? ld16(base + j * kD) : make_uint4(0, 0, 0, 0);
+        r[j] = make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -58,7 +59,7 @@ struct ChunkRegs<bf16_t> {
 template <>
 struct ChunkRegs<float> {
   float4 r[16];
-  __device__ void load(const float* base, int valid, bool /*nt: plain loads for the small fp32 workloads*/) {
+  __device__ void load(const float* base, int valid) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       r[2 * j] = valid ? *reinterpret_cast<const float4*>(base + j * kD) : make_float4(0, 0, 0, 0);
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void pool_levels12(const T* __restrict__ q, co
   const float inv = 1.0f / (float)kB;
 
   ChunkRegs<T> cur;
-  cur.load(src + ((size_t)256 * gc + u1 * 16 + half * 8) * kD + dim0, row1 < g.rows[1], tensor == 0);
+  cur.load(src + ((size_t)256 * gc + u1 * 16 + half * 8) * kD + dim0, row1 < g.rows[1]);
   float s[8];
   cur.sum(s);
 #pragma unroll
