@@ -445,8 +445,11 @@ __global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__
         const int u = p / g.K, slot = p - u * g.K;
         const int u2 = (u << sh) + (q & ((1 << sh) - 1));
         const size_t off = ((size_t)u2 * nhigh + (l - 2) * g.K + slot) * kD;
-        xk[i] = *reinterpret_cast<const float4*>(PKs + off);
-        xv[i] = *reinterpret_cast<const float4*>(PVs + off);
+        // partials are read once: non-temporal loads
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(PKs + off));
+        const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(PVs + off));
+        xk[i] = make_float4(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w));
+        xv[i] = make_float4(__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w));
       }
     }
 #pragma unroll

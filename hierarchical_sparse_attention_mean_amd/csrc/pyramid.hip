@@ -107,7 +107,14 @@ __global__ __launch_bounds__(256) void pool_levels12(const T* __restrict__ q, co
   const int col = dim0 + 4 * half;
   if (row1 < g.rows[1]) {
     const size_t o = (size_t)(g.off[1] + row1) * kD + col;
-    *reinterpret_cast<float4*>(dst + o) = make_float4(m[0], m[1], m[2], m[3]);
+    if (tensor == 2) {
+      // the fp32 V pyramid: an output that no later step of a bf16 pass reads (the attention kernels read the
+      // bf16 copy), stored non-temporally
+      const u32x4 x = {__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])};
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + o));
+    } else {
+      *reinterpret_cast<float4*>(dst + o) = make_float4(m[0], m[1], m[2], m[3]);
+    }
     if (dsth) *reinterpret_cast<uint2*>(dsth + o) = make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]));
   }
   if (g.L >= 2) {
