@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "entries.hpp"
 #include "launch.hpp"
@@ -98,18 +99,21 @@ int resolve(const llsa_problem* in, Resolved* r) {
   return LLSA_OK;
 }
 
-// The kernels are built for gfx950 only; check the current device once per device.
+// The kernels are built for gfx950 only; check the current device once per device (the cached answer is an
+// atomic: concurrent first calls may both query, and store the same value).
 int check_device() {
-  static int state[64];  // 0 unknown, 1 gfx950, -1 other
+  static std::atomic<int> state[64];  // 0 unknown, 1 gfx950, -1 other
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LLSA_ERR_DEVICE;
   if (dev < 0 || dev >= 64) return LLSA_ERR_DEVICE;
-  if (state[dev] == 0) {
+  int st = state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LLSA_ERR_DEVICE;
-    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    state[dev].store(st, std::memory_order_relaxed);
   }
-  return state[dev] == 1 ? LLSA_OK : LLSA_ERR_DEVICE;
+  return st == 1 ? LLSA_OK : LLSA_ERR_DEVICE;
 }
 
 int check_ptrs(std::initializer_list<const void*> ptrs) {
@@ -209,6 +213,21 @@ size_t comp_bwd_ws(const Resolved& r) {
 
 }  // namespace
 
+namespace llsa {
+// For llsa_index_transpose_noalloc (noalloc.hip): the validated geometry of a transpose and the bytes of its
+// workspace (column counters first, then the staging array).
+int resolve_transpose(const llsa_problem* prob, Geom* g, CscGeom* cg, size_t* cnt_bytes, size_t* ws_bytes) {
+  Resolved r;
+  LLSA_TRY(resolve(prob, &r));
+  *g = r.g;
+  *cg = r.cg;
+  *cnt_bytes = transpose_cnt_bytes(r);
+  *ws_bytes = transpose_ws(r);
+  return LLSA_OK;
+}
+int check_device_gfx950() { return check_device(); }
+}  // namespace llsa
+
 extern "C" {
 
 int llsa_resolve(const llsa_problem* prob, llsa_problem* out) {
@@ -258,6 +277,7 @@ const char* llsa_status_string(int status) {
     case LLSA_ERR_LAUNCH: return "kernel launch failed";
     case LLSA_ERR_PARAM: return "scale is not finite";
     case LLSA_ERR_DEVICE: return "the current device is not gfx950";
+    case LLSA_ERR_SCRATCH: return "the transpose workspace exceeds the static scratch of llsa_index_transpose_noalloc (16 MiB)";
     default: return "unknown status";
   }
 }

@@ -23,6 +23,8 @@ F32, BF16 = 0, 1
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_PARAM, ERR_DEVICE = \
     -1, -2, -3, -4, -5, -6, -7, -8, -9
+ERR_SCRATCH = -10
+NOALLOC_SCRATCH_BYTES = 16 << 20   # LLSA_NOALLOC_SCRATCH_BYTES
 OP_INDEX_TRANSPOSE, OP_ATTN_BWD, OP_ATTN_FWD_COMPLEMENT, OP_ATTN_BWD_COMPLEMENT = 1, 2, 3, 4
 KERNELS = ("pool", "select", "attn_fwd", "transpose", "bwd_dq", "bwd_reduce", "bwd_dkdv",
            "select_exhaustive", "reorder", "complement")  # LLSA_KERNEL_* order
@@ -61,9 +63,11 @@ _lib.llsa_attn_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.llsa_attn_fwd_complement.argtypes = [_P] + [_vp] * 9 + [_sz, _vp]
 _lib.llsa_attn_bwd_complement.argtypes = [_P] + [_vp] * 13 + [_sz, _vp]
 _lib.llsa_index_transpose.argtypes = [_P, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.llsa_index_transpose_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp]
 _lib.llsa_attn_bwd.argtypes = [_P] + [_vp] * 15 + [_sz, _vp]
 for _f in ("llsa_build_pyramid", "llsa_select", "llsa_select_exhaustive", "llsa_reorder", "llsa_attn_fwd",
-           "llsa_attn_fwd_complement", "llsa_attn_bwd_complement", "llsa_index_transpose", "llsa_attn_bwd"):
+           "llsa_attn_fwd_complement", "llsa_attn_bwd_complement", "llsa_index_transpose", "llsa_index_transpose_noalloc",
+           "llsa_attn_bwd"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.llsa_resolve.argtypes = [_P, _P]
 _lib.llsa_resolve.restype = ctypes.c_int
@@ -191,6 +195,12 @@ def index_transpose(prob, idx, col_ptr, perm, ws, stream=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.llsa_index_transpose(ctypes.byref(prob), _ptr(idx), _ptr(col_ptr), _ptr(perm), _ptr(ws), nbytes,
                                      _stream(stream)), "llsa_index_transpose")
+
+
+def index_transpose_noalloc(prob, idx, col_ptr, perm, stream=None):
+    """llsa_index_transpose with its workspace in the library's static device scratch (allocates nothing)."""
+    _check(_lib.llsa_index_transpose_noalloc(ctypes.byref(prob), _ptr(idx), _ptr(col_ptr), _ptr(perm),
+                                             _stream(stream)), "llsa_index_transpose_noalloc")
 
 
 def attn_bwd(prob, q, k, v, o, lse, dout, pk, pv, idx, col_ptr, perm, dq, dk, dv, ws, stream=None):

@@ -33,6 +33,7 @@
 #ifndef LLSA_H
 #define LLSA_H
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -52,7 +53,8 @@ enum {
   LLSA_ERR_WORKSPACE = -6,   /* workspace pointer NULL or ws_bytes smaller than required          */
   LLSA_ERR_LAUNCH = -7,      /* a kernel launch failed (hipGetLastError)                           */
   LLSA_ERR_PARAM = -8,       /* scale not finite                                                   */
-  LLSA_ERR_DEVICE = -9       /* current device is not gfx950                                       */
+  LLSA_ERR_DEVICE = -9,      /* current device is not gfx950                                       */
+  LLSA_ERR_SCRATCH = -10     /* the problem needs more than the static scratch of a no-alloc call   */
 };
 
 /* Problem description; every entry point takes the same struct. */
@@ -189,6 +191,24 @@ int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void
  */
 int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * llsa_index_transpose_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): llsa_index_transpose with the same inputs, outputs and
+ * result, its workspace taken from a library-owned static device array of LLSA_NOALLOC_SCRATCH_BYTES bytes
+ * instead of a caller buffer.  Allocates nothing (no hipMalloc, hipFree or allocating library call); the
+ * array's device address is looked up once per device, on the first call with that device current.
+ *   idx, col_ptr, perm: as llsa_index_transpose.
+ * Errors: as llsa_index_transpose, plus LLSA_ERR_SCRATCH (nothing launched) when
+ * llsa_workspace_bytes(prob, LLSA_OP_INDEX_TRANSPOSE) exceeds LLSA_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. batch*heads =
+ * 16 at n = 65536, K = 8 needs 2.5 MB; batch*heads = 8 at n = 262144, K = 16 needs 9.5 MB).
+ * Every call on one GPU uses that GPU's single array, which keeps the last call's contents (the kernels clear
+ * what must start at zero themselves): calls that overlap in time on one GPU -- on different streams, or from
+ * different host threads -- race and give undefined results.  Serialise them (one stream, or events).
+ */
+#define LLSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int llsa_index_transpose_noalloc(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm,
+                                 hipStream_t stream);
 
 /*
  * llsa_attn_bwd -- gradients of the enriched sparse attention [LLSA review, "If this is right"

@@ -138,7 +138,7 @@ def test_workspace_is_linear_in_n(L):
 
 
 def test_status_strings(L):
-    for s in range(0, -10, -1):
+    for s in range(0, -11, -1):
         assert L.status_string(s) != "unknown status"
     assert L.status_string(-99) == "unknown status"
 
@@ -161,3 +161,19 @@ def test_reorder_validation(L):
     assert f.llsa_reorder(ctypes.byref(p), 32, 2048, 1, 16, 32, None) == L.ERR_SHAPE   # 64 does not divide 32
     assert f.llsa_reorder(ctypes.byref(p), 256, 256, 1, 16, 16, None) == L.ERR_PARAM   # in place
     assert f.llsa_reorder(ctypes.byref(p), 256, 256, 1, 16, 40, None) == L.ERR_ALIGN
+
+
+def test_noalloc_transpose_host_checks(L):
+    """The no-alloc transpose rejects a problem whose workspace exceeds the static scratch before touching the
+    device, and otherwise validates like llsa_index_transpose."""
+    f = L.lib()
+    fits = L.problem(1, 8, 262144, topk=16)                 # 9.5 MB of workspace
+    assert L.workspace_bytes(fits, L.OP_INDEX_TRANSPOSE) <= L.NOALLOC_SCRATCH_BYTES
+    big = L.problem(1, 16, 262144, topk=16)                 # 19 MB > 16 MiB
+    assert L.workspace_bytes(big, L.OP_INDEX_TRANSPOSE) > L.NOALLOC_SCRATCH_BYTES
+    assert f.llsa_index_transpose_noalloc(ctypes.byref(big), 16, 32, 48, None) == L.ERR_SCRATCH
+    assert f.llsa_index_transpose_noalloc(ctypes.byref(fits), None, 32, 48, None) == L.ERR_NULL
+    assert f.llsa_index_transpose_noalloc(ctypes.byref(fits), 16, 32, 40, None) == L.ERR_ALIGN
+    assert f.llsa_index_transpose_noalloc(ctypes.byref(L.problem(1, 2, 4096 + 16)), 16, 32, 48, None) == L.ERR_SHAPE
+    assert f.llsa_index_transpose_noalloc(ctypes.byref(L.problem(0, 2, 4096)), None, None, None, None) == L.OK
+    assert L.status_string(L.ERR_SCRATCH) != "unknown status"
