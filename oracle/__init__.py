@@ -78,6 +78,14 @@ def _load():
     return lib
 
 
+def _finite(name: str, *arrays):
+    """Non-finite inputs are outside the method's definition: the oracle refuses them instead of returning
+    whatever the arithmetic makes of them."""
+    for a in arrays:
+        if a is not None and not np.all(np.isfinite(a)):
+            raise ValueError(f"oracle.{name}: input holds a non-finite value")
+
+
 def _d(a: np.ndarray):
     assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"], (a.dtype, a.flags)
     return a.ctypes.data_as(_pd)
@@ -112,6 +120,7 @@ def level_offset(n: int, block: int, level: int) -> int:
 def pool(x: np.ndarray, block: int, levels: int) -> np.ndarray:
     """Mean-pooled pyramid of x [bh, n, d] -> [bh, R, d]."""
     x = np.ascontiguousarray(x, dtype=np.float64)
+    _finite("pool", x)
     bh, n, d = x.shape
     out = np.empty((bh, pyramid_rows(n, block, levels), d), np.float64)
     _load().llsa_ref_pool(bh, n, d, block, levels, _d(x), _d(out))
@@ -122,6 +131,7 @@ def select(pq: np.ndarray, pk: np.ndarray, n: int, block: int, levels: int, topk
     """Hierarchical Top-K.  Returns (idx [bh, R, K] int32, scored_pairs)."""
     pq = np.ascontiguousarray(pq, dtype=np.float64)
     pk = np.ascontiguousarray(pk, dtype=np.float64)
+    _finite("select", pq, pk)
     bh, R, d = pq.shape
     idx = np.empty((bh, R, topk), np.int32)
     pairs = _load().llsa_ref_select(bh, n, d, block, levels, topk, _d(pq), _d(pk), _i(idx))
@@ -132,6 +142,7 @@ def attn_fwd(q, k, v, pk, pv, idx, block, levels, topk, enrich_levels, scale, co
     """Enriched sparse attention forward.  Returns (o [bh, n, d], lse [bh, n]).  complement=True takes the
     complement-partition reading of the enrichment (the unkept candidates of every level)."""
     q, k, v, pk, pv = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, pk, pv))
+    _finite("attn_fwd", q, k, v, pk, pv)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     bh, n, d = q.shape
     o = np.empty_like(q)
@@ -179,6 +190,7 @@ def attn_bwd(q, k, v, o, lse, dout, pk, pv, idx, block, levels, topk, enrich_lev
     complement=True takes the complement-partition reading of the enrichment."""
     q, k, v, o, dout, pk, pv = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, o, dout, pk, pv))
     lse = np.ascontiguousarray(lse, dtype=np.float64)
+    _finite("attn_bwd", q, k, v, o, lse, dout, pk, pv)
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     bh, n, d = q.shape
     dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
@@ -202,6 +214,7 @@ def run(q, k, v, block, topk, levels=None, enrich_levels=None, scale=None, dout=
 
     q, k, v (and dout): float64 [bh, n, d].  Returns a dict of every intermediate.
     """
+    _finite("run", q, k, v, dout)
     bh, n, d = q.shape
     L = default_levels(n, block) if not levels else levels
     Le = L if enrich_levels is None or enrich_levels < 0 else enrich_levels

@@ -116,3 +116,17 @@ def test_tie_rule_lower_index_wins():
     # level 2 candidates are children of {0, 1} -> {0..7}; ties keep 0, 1
     off2 = oracle.level_offset(n, B, 2)
     assert all(list(idx[0, off2 + u]) == [0, 1] for u in range(n // 16))
+
+
+@pytest.mark.parametrize("where", ["q", "k", "v", "dout"])
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_oracle_rejects_non_finite_inputs(where, bad):
+    """Non-finite inputs lie outside the method's definition: every oracle step refuses them."""
+    rng = np.random.default_rng(3)
+    x = {nm: rng.standard_normal((1, 64, 4)) for nm in ("q", "k", "v", "dout")}
+    x[where][0, 17, 2] = bad
+    with pytest.raises(ValueError, match="non-finite"):
+        oracle.run(x["q"], x["k"], x["v"], 4, 2, levels=2, dout=x["dout"])
+    if where != "dout":
+        with pytest.raises(ValueError, match="non-finite"):
+            oracle.pool(x[where], 4, 2)
