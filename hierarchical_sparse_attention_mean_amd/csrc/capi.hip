@@ -283,7 +283,7 @@ const char* llsa_status_string(int status) {
 }
 
 int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq, float* pk,
-                       float* pv, void* pk_bf16, void* pv_bf16, void* stream) {
+                       float* pv, void* pk_bf16, void* pv_bf16, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
@@ -292,29 +292,29 @@ int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, c
   if (bf16) LLSA_TRY(check_ptrs({pk_bf16, pv_bf16}));
   LLSA_TRY(check_device());
   return launched(llsa::launch_pyramid(r.g, bf16, q, k, v, pq, pk, pv, bf16 ? pk_bf16 : nullptr,
-                                       bf16 ? pv_bf16 : nullptr, (hipStream_t)stream));
+                                       bf16 ? pv_bf16 : nullptr, stream));
 }
 
-int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, void* stream) {
+int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
   LLSA_TRY(check_ptrs({pq, pk, idx}));
   LLSA_TRY(check_device());
-  return launched(llsa::launch_select(r.g, pq, pk, idx, (hipStream_t)stream));
+  return launched(llsa::launch_select(r.g, pq, pk, idx, stream));
 }
 
-int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, void* stream) {
+int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
   LLSA_TRY(check_ptrs({pq, pk, idx1}));
   LLSA_TRY(check_device());
-  return launched(llsa::launch_select_exhaustive(r.g, pq, pk, idx1, (hipStream_t)stream));
+  return launched(llsa::launch_select_exhaustive(r.g, pq, pk, idx1, stream));
 }
 
 int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32_t to_local, const void* x, void* y,
-                 void* stream) {
+                 hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   const int64_t S = (int64_t)1 << (2 * r.g.L);  // 4^L
@@ -325,23 +325,23 @@ int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32
   if (x == y) return LLSA_ERR_PARAM;
   LLSA_TRY(check_device());
   return launched(llsa::launch_reorder(r.g, r.p.dtype == LLSA_BF16 ? 2 : 4, grid_w, to_local != 0, x, y,
-                                       (hipStream_t)stream));
+                                       stream));
 }
 
 int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
-                  const void* pv, const int32_t* idx, void* o, float* lse, void* stream) {
+                  const void* pv, const int32_t* idx, void* o, float* lse, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
   LLSA_TRY(check_ptrs({q, k, v, pk, pv, idx, o, lse}));
   LLSA_TRY(check_device());
   return launched(
-      llsa::launch_attn_fwd(r.g, r.p.dtype == LLSA_BF16, q, k, v, pk, pv, idx, o, lse, (hipStream_t)stream));
+      llsa::launch_attn_fwd(r.g, r.p.dtype == LLSA_BF16, q, k, v, pk, pv, idx, o, lse, stream));
 }
 
 int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
                              const void* pv, const int32_t* idx, void* o, float* lse, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
@@ -354,14 +354,14 @@ int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void
   if (need > 0) LLSA_TRY(check_ptrs({ws}));
   LLSA_TRY(check_device());
   int32_t* comp = static_cast<int32_t*>(ws);
-  hipError_t e = llsa::launch_complement_lists(r.g, cm, idx, comp, (hipStream_t)stream);
+  hipError_t e = llsa::launch_complement_lists(r.g, cm, idx, comp, stream);
   if (e != hipSuccess) return LLSA_ERR_LAUNCH;
   return launched(llsa::launch_attn_fwd_complement(r.g, cm, q, k, v, pk, pv, idx, comp ? comp : idx, o, lse,
-                                                   (hipStream_t)stream));
+                                                   stream));
 }
 
 int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.bh == 0) return LLSA_OK;
@@ -372,13 +372,13 @@ int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* 
   LLSA_TRY(check_device());
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* tmp = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + transpose_cnt_bytes(r));
-  return launched(llsa::launch_index_transpose(r.g, r.cg, idx, col_ptr, perm, cnt, tmp, (hipStream_t)stream));
+  return launched(llsa::launch_index_transpose(r.g, r.cg, idx, col_ptr, perm, cnt, tmp, stream));
 }
 
 int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
                   const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  size_t ws_bytes, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
@@ -392,12 +392,12 @@ int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const 
   llsa::BwdWs w;
   llsa::bwd_ws_layout(r.g, &w, ws);
   return launched(llsa::launch_attn_bwd(r.g, r.cg, q, k, v, o, lse, dout, pk, pv, idx, col_ptr, perm, dq, dk, dv, w,
-                                        (hipStream_t)stream));
+                                        stream));
 }
 
 int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
-                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+                             void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, hipStream_t stream) {
   Resolved r;
   LLSA_TRY(resolve(prob, &r));
   if (r.p.dtype != LLSA_BF16) return LLSA_ERR_DTYPE;
@@ -419,7 +419,7 @@ int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void
   const llsa::PartGeom pg = part_geom(r);
   llsa::bwd_comp_ws_layout(r.g, pg, &w, p + z.lists + z.cp + z.pm + z.cnt + z.tmp);
   const llsa::CscGeom cg = comp_csc_geom(r);
-  const hipStream_t st = (hipStream_t)stream;
+  const hipStream_t st = stream;
   hipError_t e = llsa::launch_complement_lists(r.g, cm, idx, comp, st);
   if (e == hipSuccess) e = llsa::launch_index_transpose(r.g, cg, idx, col_ptr, perm, cnt, tmp, st);
   if (e != hipSuccess) return LLSA_ERR_LAUNCH;

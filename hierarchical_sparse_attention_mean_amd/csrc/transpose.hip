@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void csc_count(const int32_t* __restrict__ idx
   int p;
   const int l = entry_level(cg, x, &p);
   const int j = idx[(size_t)slice * g.R * g.K + (size_t)g.off[l] * g.K + p];
-  atomicAdd(&cnt[(size_t)slice * cg.cp_len + cg.cp_off[l] + j + 1], 1);
+  // an index outside [0, n_l) (not a selection) is skipped below 0 and clamped above, as in every transpose
+  // kernel, so that no write leaves the arrays; the result is then unspecified
+  if (j >= 0) atomicAdd(&cnt[(size_t)slice * cg.cp_len + cg.cp_off[l] + min(j, g.rows[l] - 1) + 1], 1);
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
@@ -292,7 +294,8 @@ __global__ __launch_bounds__(256) void csc_scatter(const int32_t* __restrict__ i
   int p;
   const int l = entry_level(cg, x, &p);
   const int j = idx[(size_t)slice * g.R * g.K + (size_t)g.off[l] * g.K + p];
-  const int slot = atomicAdd(&cursor[(size_t)slice * cg.cp_len + cg.cp_off[l] + j], 1);
+  if (j < 0) return;
+  const int slot = atomicAdd(&cursor[(size_t)slice * cg.cp_len + cg.cp_off[l] + min(j, g.rows[l] - 1)], 1);
   tmp[(size_t)slice * cg.pm_len + cg.pm_off[l] + slot] = p;
 }
 
@@ -305,7 +308,9 @@ __global__ __launch_bounds__(256) void csc_order(const int32_t* __restrict__ idx
   const int slice = blockIdx.y;
   int p;
   const int l = entry_level(cg, x, &p);
-  const int j = idx[(size_t)slice * g.R * g.K + (size_t)g.off[l] * g.K + p];
+  const int jr = idx[(size_t)slice * g.R * g.K + (size_t)g.off[l] * g.K + p];
+  if (jr < 0) return;
+  const int j = min(jr, g.rows[l] - 1);
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[l];
   const int32_t* col = tmp + (size_t)slice * cg.pm_len + cg.pm_off[l];
   const int b = cp[j], e = cp[j + 1];

@@ -7,7 +7,6 @@ loudly (ImportError) when the library has not been built -- there is no CPU fall
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -271,7 +270,3 @@ class Buffers:
         stream.wait_event(self._ev[1])
         attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pka, self.pva, self.idx, self.col_ptr, self.perm,
                  self.dq, self.dk, self.dv, self.ws_b, stream)
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)

@@ -11,9 +11,21 @@
  * Tensors are device pointers into caller-owned memory.  Raw tensors Q, K, V, O, dO, dQ, dK, dV are
  * [batch][heads][n][d], contiguous, d fastest, stored as fp32 or bf16 (llsa_problem.dtype).
  * The pooled pyramid is fp32 [batch*heads][R][d] with R = sum_{l=1..L} n_l and n_l = n / B^l; level l
- * starts at row sum_{l'<l} n_l'.  The attention entry points read the pooled K and V pyramids in the raw
- * dtype: the fp32 pyramids for fp32 problems, their bf16 copies (same layout) for bf16 problems.  Selection indices are int32 [batch*heads][R][K] (same row order),
- * each row ascending.  The CSC of level l (l = 1..T, T = max(1, L_e)) is col_ptr (n_l + 1 entries,
+ * starts at row sum_{l'<l} n_l'.  Selection indices are int32 [batch*heads][R][K] (same row order), each row
+ * ascending.
+ * Pooled K and V in the attention calls (an amendment of the five-call contract, which passes the fp32
+ * pyramids): llsa_attn_fwd and llsa_attn_bwd read the pooled K and V pyramids in the raw dtype -- the fp32
+ * pyramids themselves for fp32 problems; for bf16 problems their bf16 copies (same layout, rounded to nearest
+ * even), which llsa_build_pyramid writes beside the fp32 pyramids (pk_bf16, pv_bf16).  The bf16 products round
+ * pooled tokens to bf16 anyway, so the copies change no result; reading fp32 rows instead doubles the bytes
+ * of every enrichment gather, measured on MI355X as one more 32-entry stage per fine block: +48 us per step at
+ * n = 65536, 16 heads, K = 8, L = 3 (0.873 -> 0.921 ms: forward +20 us, dQ +32 us) and +0.10 ms at n = 262144,
+ * 8 heads, K = 16 (2.76 -> 2.86 ms), with identical outputs.
+ * Index inputs: every idx passed to a call must be a selection as llsa_select writes it -- values of level l in
+ * [0, n_l), rows ascending, each unit's picks children of its parent's picks.  The attention calls gather rows
+ * at those indices without checking them: any other idx is undefined behaviour (an out-of-range value reads
+ * outside the tensors).  The transposes skip negative and clamp too-large values, so they never write outside
+ * their arrays, but their result for such an idx is unspecified.  The CSC of level l (l = 1..T, T = max(1, L_e)) is col_ptr (n_l + 1 entries,
  * relative to the level) and perm (n_l * K entries, each a CSR position p = u*K + k, ascending within
  * a column); levels are concatenated per batch*head in level order.
  *
@@ -84,10 +96,11 @@ enum {
  *   pq, pk, pv out: fp32 pyramids [batch*heads][R][d].
  *   pk_bf16, pv_bf16 out (bf16 problems; ignored and may be NULL for fp32): the pooled K and V pyramids
  *             rounded to bf16 (round to nearest even), bf16 [batch*heads][R][d] -- the pyramid operands of
- *             llsa_attn_fwd / llsa_attn_bwd, whose bf16 products round pooled tokens to bf16.
+ *             llsa_attn_fwd / llsa_attn_bwd, whose bf16 products round pooled tokens to bf16.  These two
+ *             parameters extend the five-call contract (see "Pooled K and V in the attention calls" above).
  */
 int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, const void* v, float* pq,
-                       float* pk, float* pv, void* pk_bf16, void* pv_bf16, void* stream);
+                       float* pk, float* pv, void* pk_bf16, void* pv_bf16, hipStream_t stream);
 
 /*
  * llsa_select -- hierarchical Top-K [LLSA review, "Core claim"; "What carries the argument";
@@ -98,7 +111,7 @@ int llsa_build_pyramid(const llsa_problem* prob, const void* q, const void* k, c
  *   pq, pk in : fp32 pyramids from llsa_build_pyramid.
  *   idx    out: int32 [batch*heads][R][K], each row ascending.
  */
-int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, void* stream);
+int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx, hipStream_t stream);
 
 /*
  * llsa_select_exhaustive -- single-level exhaustive Top-K, the quadratic baseline the hierarchy replaces
@@ -110,7 +123,7 @@ int llsa_select(const llsa_problem* prob, const float* pq, const float* pk, int3
  *   idx1   out: int32 [batch*heads][n_1][K].
  * Limits as llsa_select, except that n_1 is not limited by n_L <= 512.
  */
-int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, void* stream);
+int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const float* pk, int32_t* idx1, hipStream_t stream);
 
 /*
  * llsa_reorder -- 2-D-local index reordering of the token rows [LLSA review, domain-assumption ledger: after
@@ -125,7 +138,7 @@ int llsa_select_exhaustive(const llsa_problem* prob, const float* pq, const floa
  *   x in, y out: raw tensors [batch][heads][n][d] (dtype), distinct buffers (LLSA_ERR_PARAM if x == y).
  */
 int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32_t to_local, const void* x, void* y,
-                 void* stream);
+                 hipStream_t stream);
 
 /*
  * llsa_attn_fwd -- sparse block attention with hierarchical KV enrichment [LLSA review, "Core
@@ -133,16 +146,16 @@ int llsa_reorder(const llsa_problem* prob, int32_t grid_h, int32_t grid_w, int32
  * raw tokens of every level-1 block in idx row i (logit sigma*q.k) and, for l = 1..L_e, the level-l
  * pooled tokens kept by its level-l ancestor unit i/B^(l-1) (logit sigma*q.k + l*ln B, i.e. weight
  * B^l).  Only the sparse indices are read; no dense mask exists.
- *   q, k, v in : raw tensors (dtype).  idx in: from llsa_select.
+ *   q, k, v in : raw tensors (dtype).  idx in: from llsa_select (any other idx: undefined behaviour).
  *   pk, pv  in : pooled K and V pyramids in the raw dtype (fp32: pk, pv of llsa_build_pyramid; bf16: its
- *                pk_bf16, pv_bf16).
+ *                pk_bf16, pv_bf16 -- the amendment described above).
  *   o   out: [batch][heads][n][d] (dtype).
  *   lse out: fp32 [batch*heads][n], natural-log log-sum-exp of each query's logits (for backward).
  * bf16 runs the products on bf16 MFMA with fp32 accumulation (pooled K/V in bf16, probabilities rounded
  * to bf16 for the PV product); fp32 computes in fp32.
  */
 int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* pk,
-                  const void* pv, const int32_t* idx, void* o, float* lse, void* stream);
+                  const void* pv, const int32_t* idx, void* o, float* lse, hipStream_t stream);
 
 /*
  * llsa_attn_fwd_complement -- the forward under the complement-partition reading of the enrichment, the
@@ -161,7 +174,7 @@ int llsa_attn_fwd(const llsa_problem* prob, const void* q, const void* k, const 
  */
 int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v,
                              const void* pk, const void* pv, const int32_t* idx, void* o, float* lse, void* ws,
-                             size_t ws_bytes, void* stream);
+                             size_t ws_bytes, hipStream_t stream);
 
 /*
  * llsa_attn_bwd_complement -- the backward of llsa_attn_fwd_complement [LLSA review, "If this is right" (the
@@ -178,19 +191,19 @@ int llsa_attn_fwd_complement(const llsa_problem* prob, const void* q, const void
 int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const void* pk, const void* pv,
                              const int32_t* idx, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                             void* stream);
+                             hipStream_t stream);
 
 /*
  * llsa_index_transpose -- CSR -> CSC of the selection of levels 1..T, T = max(1, L_e) [LLSA review,
  * "What carries the argument": a CSR-to-CSC scan gives each key block its query blocks without a
  * dense N x N mask].  Column j of level l lists the CSR positions p = u*K + k with idx = j, ascending.
- *   idx     in : from llsa_select.
+ *   idx     in : from llsa_select (other values: skipped below 0, clamped above n_l - 1, result unspecified).
  *   col_ptr out: int32 [batch*heads][llsa_colptr_len].
  *   perm    out: int32 [batch*heads][llsa_perm_len].
  *   ws      scratch of llsa_workspace_bytes(prob, LLSA_OP_INDEX_TRANSPOSE) bytes (caller-owned).
  */
 int llsa_index_transpose(const llsa_problem* prob, const int32_t* idx, int32_t* col_ptr, int32_t* perm,
-                         void* ws, size_t ws_bytes, void* stream);
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * llsa_index_transpose_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture,
@@ -218,15 +231,16 @@ int llsa_index_transpose_noalloc(const llsa_problem* prob, const int32_t* idx, i
  * B^-l.  No gradient flows through the Top-K choice or into pooled queries.  Key-side gradients are
  * gathered per key block through the CSC (no atomics).  bf16 only in this version (LLSA_ERR_DTYPE for
  * fp32).
- *   q, k, v, o, dout in: raw tensors (dtype); lse in: from llsa_attn_fwd; pk, pv (bf16), idx: as forward;
- *   col_ptr, perm in: from llsa_index_transpose.
+ *   q, k, v, o, dout in: raw tensors (dtype); lse in: from llsa_attn_fwd; pk, pv (bf16 copies), idx: as
+ *   forward (idx from llsa_select: any other idx is undefined behaviour);
+ *   col_ptr, perm in: from llsa_index_transpose of the same idx.
  *   dq, dk, dv out: raw tensors (dtype).
  *   ws scratch of llsa_workspace_bytes(prob, LLSA_OP_ATTN_BWD) bytes (caller-owned).
  */
 int llsa_attn_bwd(const llsa_problem* prob, const void* q, const void* k, const void* v, const void* o,
                   const float* lse, const void* dout, const void* pk, const void* pv, const int32_t* idx,
                   const int32_t* col_ptr, const int32_t* perm, void* dq, void* dk, void* dv, void* ws,
-                  size_t ws_bytes, void* stream);
+                  size_t ws_bytes, hipStream_t stream);
 
 /* ---- host-only helpers (no GPU work) ---------------------------------------------------------- */
 

@@ -177,3 +177,44 @@ def test_noalloc_transpose_host_checks(L):
     assert f.llsa_index_transpose_noalloc(ctypes.byref(L.problem(1, 2, 4096 + 16)), 16, 32, 48, None) == L.ERR_SHAPE
     assert f.llsa_index_transpose_noalloc(ctypes.byref(L.problem(0, 2, 4096)), None, None, None, None) == L.OK
     assert L.status_string(L.ERR_SCRATCH) != "unknown status"
+
+
+# The five calls of the contract, parameter types in order (names dropped).  CONTRACT is the problem-level
+# statement (fp32 pyramids into the attention calls); AMENDED lists the one documented difference: bf16 problems
+# pass the bf16 copies of the pooled K, V pyramids, which llsa_build_pyramid writes as two more outputs.
+CONTRACT = {
+    "llsa_build_pyramid": ["const llsa_problem*", "const void*", "const void*", "const void*", "float*", "float*",
+                           "float*", "hipStream_t"],
+    "llsa_select": ["const llsa_problem*", "const float*", "const float*", "int32_t*", "hipStream_t"],
+    "llsa_attn_fwd": ["const llsa_problem*", "const void*", "const void*", "const void*", "const float*",
+                      "const float*", "const int32_t*", "void*", "float*", "hipStream_t"],
+    "llsa_index_transpose": ["const llsa_problem*", "const int32_t*", "int32_t*", "int32_t*", "void*", "size_t",
+                             "hipStream_t"],
+    "llsa_attn_bwd": ["const llsa_problem*", "const void*", "const void*", "const void*", "const void*",
+                      "const float*", "const void*", "const float*", "const float*", "const int32_t*",
+                      "const int32_t*", "const int32_t*", "void*", "void*", "void*", "void*", "size_t",
+                      "hipStream_t"],
+}
+AMENDED = {
+    "llsa_build_pyramid": lambda t: t[:7] + ["void*", "void*"] + t[7:],
+    "llsa_attn_fwd": lambda t: t[:4] + ["const void*", "const void*"] + t[6:],
+    "llsa_attn_bwd": lambda t: t[:7] + ["const void*", "const void*"] + t[9:],
+}
+
+
+def _param_types(name):
+    src = open(os.path.join(ROOT, "include", "llsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    m = re.search(r"\bint\s+" + name + r"\s*\((.*?)\)\s*;", src, flags=re.S)
+    assert m, name
+    out = []
+    for p in m.group(1).split(","):
+        p = " ".join(p.split())
+        out.append(re.sub(r"\s*\b\w+$", "", p).replace(" *", "*"))
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(CONTRACT))
+def test_hot_path_signatures(name):
+    want = AMENDED.get(name, lambda t: t)(CONTRACT[name])
+    assert _param_types(name) == want
