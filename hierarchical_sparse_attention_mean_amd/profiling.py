@@ -10,7 +10,8 @@ is built from; ``bench.py`` reports the figure only while that hash still matche
         --copy-bytes N --kernel NAME --workload NAME --command "..." > profiles/NAME_WORKLOAD_traffic.md
 
 The ``kernel-stats`` subcommand turns a ``rocprofv3 --kernel-trace --stats`` run into the per-kernel table kept
-under ``profiles/``.
+under ``profiles/``; ``counters`` turns ``rocprofv3 --pmc`` runs of other counters (MFMA busy cycles, LDS bank
+conflicts, texture-unit busy, wave wait cycles) into per-kernel means and derived percentages.
 """
 from __future__ import annotations
 
@@ -157,6 +158,96 @@ def l2_hits_summary(directory: str, kernels: list, title: str, command: str) -> 
     return "\n".join(lines)
 
 
+CUS, SIMDS, XCDS = 256, 1024, 8   # MI355X: compute units, SIMDs (4 per CU), XCDs
+
+
+def _per_dispatch_all(path: str):
+    """{dispatch id: (kernel name, {counter: value})} from a counter_collection CSV, each counter summed over the
+    rows it has for the dispatch.  GRBM_GUI_ACTIVE comes as one row holding the sum over the XCDs (it reads about
+    8x the dispatch's duration in cycles), so the kernel's cycles are GRBM_GUI_ACTIVE / 8; the summary checks this
+    against the dispatch's timestamps (the implied clock).  The dispatch duration (ns) is kept as 'duration_ns'."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    names, dur = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = r["Dispatch_Id"]
+            vals[d][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            names[d] = r["Kernel_Name"]
+            dur[d] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = {}
+    for d, cs in vals.items():
+        c = {k: sum(v) for k, v in cs.items()}
+        if "GRBM_GUI_ACTIVE" in c:
+            c["GRBM_GUI_ACTIVE"] /= XCDS
+        c["duration_ns"] = dur[d]
+        out[d] = (names[d], c)
+    return out
+
+
+# derived figures: (label, counters needed, formula over the per-dispatch means)
+_DERIVED = [
+    ("dispatch duration, us (timestamps)", ("duration_ns",), lambda c: c["duration_ns"] / 1e3),
+    ("implied clock, GHz (GRBM_GUI_ACTIVE / 8 / duration)", ("GRBM_GUI_ACTIVE", "duration_ns"),
+     lambda c: c["GRBM_GUI_ACTIVE"] / c["duration_ns"]),
+    ("MFMA busy, % of SIMD cycles", ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+     lambda c: 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * SIMDS)),
+    ("bf16 MFMA TFLOP issued per dispatch", ("SQ_INSTS_VALU_MFMA_MOPS_BF16",),
+     lambda c: c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12),
+    ("LDS bank conflicts, % of LDS active cycles", ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+     lambda c: 100.0 * c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)),
+    ("LDS active, % of CU cycles", ("SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"),
+     lambda c: 100.0 * c["SQ_LDS_IDX_ACTIVE"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+    ("texture address (TA) busy, % of CU cycles", ("TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE"),
+     lambda c: 100.0 * c["TA_TA_BUSY_sum"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+    ("texture data (TD) busy, % of CU cycles", ("TD_TD_BUSY_sum", "GRBM_GUI_ACTIVE"),
+     lambda c: 100.0 * c["TD_TD_BUSY_sum"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+    ("CU busy, % of cycles", ("SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"),
+     lambda c: 100.0 * c["SQ_BUSY_CU_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+    ("VALU instructions issued, % of wave cycles", ("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+     lambda c: 100.0 * c["SQ_ACTIVE_INST_VALU"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
+    ("LDS instructions issued, % of wave cycles", ("SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+     lambda c: 100.0 * c["SQ_ACTIVE_INST_LDS"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
+    ("vector memory instructions issued, % of wave cycles", ("SQ_ACTIVE_INST_VMEM", "SQ_WAVE_CYCLES"),
+     lambda c: 100.0 * c["SQ_ACTIVE_INST_VMEM"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
+    ("waves waiting on a dependency (s_waitcnt), % of wave cycles", ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+     lambda c: 100.0 * c["SQ_WAIT_INST_ANY"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
+    ("waves waiting for anything, % of wave cycles", ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+     lambda c: 100.0 * c["SQ_WAIT_ANY"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
+    ("waves per CU (average)", ("SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
+     lambda c: c["SQ_WAVE_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+]
+
+
+def counters_summary(directories: list, kernels: list, title: str, commands: list) -> str:
+    """Per-kernel means of raw counters over the dispatches of one or more rocprofv3 --pmc runs, and the derived
+    figures that the counters present allow (MFMA busy, LDS bank conflicts, TA/TD busy, where waves wait)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in directories:
+        for _, (nm, cs) in _per_dispatch_all(_csv_in(d)).items():
+            for k in kernels:
+                if re.search(r"\b" + k + r"\b", nm):
+                    for c, v in cs.items():
+                        per[k][c].append(v)
+    lines = [f"# {title}", "", "Commands (from the repository root, on one MI355X):", "", "```", *commands, "```", "",
+             "Counters are summed over their hardware instances per dispatch, then averaged over the dispatches; kernel "
+             f"cycles = GRBM_GUI_ACTIVE / {XCDS} (the counter sums the XCDs); {CUS} CUs, {SIMDS} SIMDs.  Profiled "
+             "dispatches run one at a time (the transpose is not beside the forward).", ""]
+    for k in kernels:
+        if k not in per:
+            continue
+        mean = {c: sum(v) / len(v) for c, v in per[k].items()}
+        nd = max(len(v) for v in per[k].values())
+        lines += [f"## {k}", "", f"dispatches: {nd}", "", "| derived | value |", "|---|---|"]
+        for label, need, f in _DERIVED:
+            if all(n in mean for n in need):
+                lines.append(f"| {label} | {f(mean):.4g} |")
+        lines += ["", "| counter | mean per dispatch |", "|---|---|"]
+        for c in sorted(mean):
+            lines.append(f"| {c} | {mean[c]:.6g} |")
+        lines.append("")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -176,7 +267,15 @@ def main():
     h.add_argument("--kernels", required=True, help="comma-separated kernel name substrings")
     h.add_argument("--title", required=True)
     h.add_argument("--command", required=True)
+    cs = sub.add_parser("counters")
+    cs.add_argument("--dirs", required=True, help="comma-separated rocprofv3 --pmc output directories")
+    cs.add_argument("--kernels", required=True, help="comma-separated kernel names")
+    cs.add_argument("--title", required=True)
+    cs.add_argument("--command", action="append", required=True)
     a = ap.parse_args()
+    if a.cmd == "counters":
+        print(counters_summary(a.dirs.split(","), a.kernels.split(","), a.title, a.command))
+        return
     if a.cmd == "kernel-stats":
         print(kernel_stats_summary(a.dir, a.title, a.command))
     elif a.cmd == "l2-hits":

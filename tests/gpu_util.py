@@ -3,6 +3,7 @@ the output tolerances."""
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import torch
@@ -11,6 +12,15 @@ import oracle
 from hierarchical_sparse_attention_mean_amd import inputs
 
 BF16_REL = 2e-2   # bf16 outputs: per (b, h) slice, max |gpu - ref| <= 2e-2 * max |ref|
+# bf16 outputs, row by row (a row = one token's d values): max |gpu - ref| <= ROW_REL * max |ref row| + floor * max
+# |ref slice|.  O and dV (and any output not named) are convex or positive-weight combinations of bf16 operands and
+# meet the relative bound on every row (floor 1e-3 for rows that are nearly zero).  dQ and dK are sums of
+# dS = P (dP - Delta) terms; on smooth inputs dP - Delta cancels, so a row that is small next to its terms keeps
+# the bf16 rounding of those terms: observed up to 1.2e-2 (dQ) and 1.0e-2 (dK) of the slice maximum beyond the
+# relative part on the parity cases, hence a floor of 1.6e-2 for them.
+ROW_REL = 2e-2
+ROW_FLOOR = {"dq": 1.6e-2, "dk": 1.6e-2}
+ROW_FLOOR_DEFAULT = 1e-3
 F32_ABS = 1e-4    # fp32 outputs: max |gpu - ref| <= 1e-4
 GAP_REL = 1e-3    # selection compared only where the K-th and (K+1)-th scores differ by > 1e-3 relative
 
@@ -33,22 +43,64 @@ def flat(x: np.ndarray) -> np.ndarray:
     return x.reshape(-1, x.shape[-2], x.shape[-1])
 
 
-def check_close(name, gpu, ref, dtype):
-    """Per-slice tolerance of the outputs; returns the worst normalised error."""
+def error_stats(gpu, ref, d=64):
+    """Element-wise error statistics of one output: quantiles of |err| / max|ref row| over rows (a row = one
+    token's d values) and of |err| / (|ref| + 1e-3 max|ref|) over elements, so that small-magnitude rows and
+    elements are visible beside the slice-normalised maximum."""
+    g, r = gpu.reshape(-1, d), ref.reshape(-1, d)
+    err = np.abs(g - r)
+    scale = np.abs(r).max()
+    row = err.max(1) / np.maximum(np.abs(r).max(1), 1e-30)
+    elem = (err / (np.abs(r) + 1e-3 * max(scale, 1e-30))).ravel()
+    q = lambda a, p: float(np.quantile(a, p))
+    smax = max(scale, 1e-30)
+    floor = float(np.max(np.maximum(err.max(1) - 2e-2 * np.abs(r).max(1), 0.0)) / smax)
+    return {"floor_needed": floor, "row_p50": q(row, 0.5), "row_p99": q(row, 0.99), "row_p999": q(row, 0.999), "row_max": float(row.max()),
+            "elem_p50": q(elem, 0.5), "elem_p99": q(elem, 0.99), "elem_p999": q(elem, 0.999),
+            "elem_max": float(elem.max()), "rows": int(g.shape[0])}
+
+
+def check_close(name, gpu, ref, dtype, d=64):
+    """Tolerances of an output, per (b, h) slice: fp32 max |err| <= 1e-4 (element-wise); bf16 max |err| <= 2e-2
+    max |ref| over the slice, and row by row max |err| <= ROW_REL max |ref row| + floor max |ref slice| (a row is
+    one token's d values; floors above), which bounds small-magnitude rows the slice rule would let through.
+    Prints the element-wise statistics (error_stats); returns the worst slice-normalised error."""
     gpu = gpu.reshape(ref.shape[0], -1)
     ref = ref.reshape(ref.shape[0], -1)
     assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
     worst = 0.0
     for s in range(ref.shape[0]):
         err = np.abs(gpu[s] - ref[s]).max()
+        smax = np.abs(ref[s]).max()
         if dtype == "bf16":
-            lim = BF16_REL * np.abs(ref[s]).max()
-            worst = max(worst, err / max(np.abs(ref[s]).max(), 1e-30))
+            lim = BF16_REL * smax
+            worst = max(worst, err / max(smax, 1e-30))
         else:
             lim = F32_ABS
             worst = max(worst, err)
         assert err <= lim, f"{name}: slice {s}: max abs err {err:.3e} > {lim:.3e}"
+        st = error_stats(gpu[s], ref[s], d)
+        _record(name, dtype, st)
+        if dtype == "bf16":
+            g, r = gpu[s].reshape(-1, d), ref[s].reshape(-1, d)
+            row_err = np.abs(g - r).max(1)
+            row_lim = ROW_REL * np.abs(r).max(1) + ROW_FLOOR.get(name.lower(), ROW_FLOOR_DEFAULT) * smax
+            bad = np.nonzero(row_err > row_lim)[0]
+            assert bad.size == 0, (f"{name}: slice {s}: {bad.size} rows over the row bound, first {bad[0]}: "
+                                   f"err {row_err[bad[0]]:.3e} > {row_lim[bad[0]]:.3e}")
     return worst
+
+
+def _record(name, dtype, st):
+    print(f"  {name} ({dtype}) error quantiles: row p50 {st['row_p50']:.2e} p99 {st['row_p99']:.2e} "
+          f"max {st['row_max']:.2e}; element p50 {st['elem_p50']:.2e} p99 {st['elem_p99']:.2e} "
+          f"max {st['elem_max']:.2e}")
+    path = os.environ.get("LLSA_ERRSTATS")
+    if path:
+        import json
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(name=name, dtype=dtype, test=os.environ.get("PYTEST_CURRENT_TEST", ""), **st))
+                    + "\n")
 
 
 def selection_parity(idx_gpu, idx_ref, pq_ref, pk_ref, n, B, L, K):

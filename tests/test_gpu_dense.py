@@ -1,4 +1,4 @@
-"""The dense-attention comparison at the same shapes (bench.py --dense) and the exact special case that links it
+"""The dense-attention comparison at the same shapes (dense_sdpa in bench.py) and the exact special case that links it
 to the method: when K covers every block and no enrichment level is used (L_e = 0), the enriched sparse
 attention is dense attention (each query attends every raw token once, bias 0).
 
