@@ -1,8 +1,8 @@
 """llsa_index_transpose_noalloc (workspace in the library's static device scratch) against
 llsa_index_transpose (caller workspace): identical col_ptr and perm, bit for bit, over calls in a row on
 one GPU, each later call on a smaller problem than the one before (the scratch keeps the previous call's
-contents).  The three problems take the three code paths of the transpose: counters in global memory
-(n_1 + 1 > 16384), counters in LDS, and the scatter/order path (L_e < L)."""
+contents).  The problems take the code paths of the transpose: counters in global memory (n_1 + 1 > 16384),
+counters in LDS, and the scatter/order path (L_e < L)."""
 import sys
 
 import pytest
@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 # (batch, heads, n, topk, levels, enrich_levels), largest transpose workspace first
 CASES = [
-    (1, 2, 262144, 16, 3, -1),   # global counters + hierarchical fill
+    (1, 1, 1 << 20, 8, 4, -1),   # global counters + hierarchical fill
+    (1, 2, 262144, 16, 3, -1),   # global counters, K = 16
     (1, 4, 65536, 8, 3, 1),      # LDS counters, then scatter + order (T = 1 < L)
     (1, 2, 4096, 8, 2, -1),      # LDS counters + hierarchical fill, small
 ]
