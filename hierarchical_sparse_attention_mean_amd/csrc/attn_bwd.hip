@@ -684,15 +684,17 @@ __device__ __forceinline__ void dkdv_item(DkdvLds& sm, const bf16_t* __restrict_
     return nb;
   };
 
-  // copies of one key block's rows into the (single) block slot, and of the shares
+  // copies of one key block's rows into the (single) block slot, and of the shares.  The block's K, V and
+  // level-1 pooled rows are read by this item alone: non-temporal, so that they leave the L2 to the Q and dO
+  // rows that the stages of other items gather again
   auto dma_block = [&](int b) {
     const size_t r = base + (size_t)16 * (j0 + b) * kD + swz_dma_src(lane);
-    lds_dma16(k + r, &sm.kvs[w][0][0]);
-    lds_dma16(k + r + 8 * kD, &sm.kvs[w][0][8 * kD]);
-    lds_dma16(v + r, &sm.kvs[w][1][0]);
-    lds_dma16(v + r + 8 * kD, &sm.kvs[w][1][8 * kD]);
+    lds_dma16_nt(k + r, &sm.kvs[w][0][0]);
+    lds_dma16_nt(k + r + 8 * kD, &sm.kvs[w][0][8 * kD]);
+    lds_dma16_nt(v + r, &sm.kvs[w][1][0]);
+    lds_dma16_nt(v + r + 8 * kD, &sm.kvs[w][1][8 * kD]);
     if (lane < 16)
-      lds_dma16((lane < 8 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 8 * (lane & 7), &sm.p1s[w][0][0]);
+      lds_dma16_nt((lane < 8 ? pk : pv) + ((size_t)slice * g.R + g.off[1] + j0 + b) * kD + 8 * (lane & 7), &sm.p1s[w][0][0]);
   };
   if (lane < 32) {
     for (int s = 0; s < nsh; ++s) {
