@@ -213,8 +213,9 @@ _DERIVED = [
      lambda c: 100.0 * c["SQ_WAIT_INST_ANY"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
     ("waves waiting for anything, % of wave cycles", ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
      lambda c: 100.0 * c["SQ_WAIT_ANY"] / max(c["SQ_WAVE_CYCLES"], 1.0)),
-    ("waves per CU (average)", ("SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
-     lambda c: c["SQ_WAVE_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * CUS)),
+    # SQ_WAVE_CYCLES counts in units of 4 cycles: waves per SIMD = 4 SQ_WAVE_CYCLES / (cycles * SIMDS)
+    ("resident waves per SIMD (average)", ("SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
+     lambda c: 4.0 * c["SQ_WAVE_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * SIMDS)),
 ]
 
 
