@@ -13,9 +13,10 @@
 //      writes dQ and Delta, and -- because all 256 queries of a level-2 unit share the enrichment tokens
 //      of levels >= 2 -- accumulates their dK^(l), dV^(l) contributions for the unit in registers and
 //      reduces the four waves in LDS in a fixed order (partials per level-2 unit and slot).
-//   2. coarse_reduce: for each pooled token of levels >= 2, sums the partials of the (unit, slot) pairs
-//      that kept it, found through that level's CSC column (no atomics).
-//   3. dkdv_order, then bwd_dkdv (K-major, one wavefront per work item: a group of four key blocks, or a
+//   2. reduce_and_order: for each pooled token of levels >= 2, sums the partials of the (unit, slot) pairs
+//      that kept it, found through that level's CSC column (no atomics); beside it, in the same launch, the
+//      dK/dV work lists (dkdv_order's job, which needs only the CSC).
+//   3. bwd_dkdv (K-major, one wavefront per work item: a group of four key blocks, or a
 //      chunk of a long group's stages): walks the key blocks' CSC columns of level 1 -- the query blocks that
 //      kept them -- and accumulates dK, dV for their keys.  The same query blocks are exactly those that
 //      attend a block's level-1 pooled token, so that token's gradient (scaled by B^-1) is folded into the
@@ -403,21 +404,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
 
 // ------------------------------------------------------------------------------------------------
 // 2. Pooled-token gradients of levels 2..Le from the per-(level-2 unit, slot) partials via the CSC.
-// grid.x = sum_{l=2..Le} n_l, grid.y = slice; 256 threads.  Token j of level l sums, over the CSR positions
+// One 256-thread workgroup per (slice, token) of levels 2..Le.  Token j of level l sums, over the CSR positions
 // p = u*K + s of its column, the partials of entry (l, s) of the B^(l-2) level-2 units under unit u.  Those
 // (position, unit) items go four to a wave instruction -- lane l takes item 4 i + l / 16 of its wave's share
 // and dims 4 (l % 16) .. +3 of its K and V rows (16-byte loads), eight items of a wave in flight -- and are
 // summed in a fixed order: per lane in item order, then the four item lanes of a wave, then the four waves.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void coarse_reduce(const int32_t* __restrict__ col_ptr,
-                                                     const int32_t* __restrict__ perm,
-                                                     const float* __restrict__ part_k,
-                                                     const float* __restrict__ part_v, float* __restrict__ gk,
-                                                     float* __restrict__ gv, Geom g, CscGeom cg) {
+__device__ __forceinline__ void coarse_reduce_block(const int32_t* __restrict__ col_ptr,
+                                                    const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ part_k,
+                                                    const float* __restrict__ part_v, float* __restrict__ gk,
+                                                    float* __restrict__ gv, const Geom& g, const CscGeom& cg,
+                                                    int slice, int token) {
   __shared__ float4 red[2][4][16];
-  const int slice = blockIdx.y, lane = threadIdx.x & 63, q4 = lane >> 4, d4 = 4 * (lane & 15);
+  const int lane = threadIdx.x & 63, q4 = lane >> 4, d4 = 4 * (lane & 15);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int x = blockIdx.x, l = 2;
+  int x = token, l = 2;
   while (x >= g.rows[l]) {
     x -= g.rows[l];
     ++l;
@@ -515,12 +517,15 @@ namespace {
 // group has T_g > S and at most 2 T_g / S chunks).
 // grid.x = slices, 1024 threads.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ col_ptr, int4* __restrict__ items,
-                                                   int4* __restrict__ splits, int32_t* __restrict__ counters,
-                                                   Geom g, CscGeom cg, DkdvBounds bd, int S, int walk) {
-  __shared__ long long wave_tot[16];
+// kT threads (a multiple of 64, at most 1024) build slice `slice`'s list.
+template <int kT>
+__device__ __forceinline__ void dkdv_order_block(const int32_t* __restrict__ col_ptr, int4* __restrict__ items,
+                                                 int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                                 const Geom& g, const CscGeom& cg, const DkdvBounds& bd, int S,
+                                                 int walk, int slice) {
+  __shared__ long long wave_tot[kT / 64];
   __shared__ int carry_s[4], nlong_s;
-  const int slice = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n1 = g.rows[1], gps = (n1 + kGroup - 1) / kGroup;
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
   int4* it_out = items + (size_t)slice * bd.items;
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
     if (lane == 63) wave_tot[w] = inc;
     __syncthreads();
     long long before = 0, tot = 0;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kT / 64; ++i) {
       before += i < w ? wave_tot[i] : 0;
       tot += wave_tot[i];
     }
@@ -554,8 +559,8 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
   if (t < 4) carry_s[t] = 0;
   if (t == 0) nlong_s = 0;
   __syncthreads();
-  if (gps > 1024) {  // items of the long groups, before the others are placed (one chunk of groups needs no pass)
-    for (int base = 0; base < gps; base += 1024) {
+  if (gps > kT) {  // items of the long groups, before the others are placed (one chunk of groups needs no pass)
+    for (int base = 0; base < gps; base += kT) {
       const int T = glen(base + t);
       int e, x, tot, y;
       scan(T > thresh ? chunks(T) : 0, 0, &e, &x, &tot, &y);
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
       __syncthreads();
     }
   }
-  for (int base = 0; base < gps; base += 1024) {
+  for (int base = 0; base < gps; base += kT) {
     const int gi = base + t;
     const int T = glen(gi);
     const bool in = gi < gps, lng = in && T > thresh, split = lng && T > S;
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
     int e0, e1, e2, e3, t0, t1, t2, t3;
     scan(lng ? nch : 0, in && !lng ? 1 : 0, &e0, &e1, &t0, &t1);  // item positions: long groups, the others
     scan(split ? nch : 0, split ? 1 : 0, &e2, &e3, &t2, &t3);      // partial slots, split-group index
-    const int nlong = gps > 1024 ? nlong_s : t0;
+    const int nlong = gps > kT ? nlong_s : t0;
     if (split) {
       const int p0 = carry_s[0] + e0, slot0 = carry_s[2] + e2, si = carry_s[3] + e3;
       for (int c = 0; c < nch; ++c) it_out[p0 + c] = make_int4(gi, c, si, slot0 + c);
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
     }
     __syncthreads();
     if (t == 0) {
-      if (gps <= 1024) nlong_s = t0;
+      if (gps <= kT) nlong_s = t0;
       carry_s[0] += t0;
       carry_s[1] += t1;
       carry_s[2] += t2;
@@ -594,7 +599,34 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
   }
   const int count = nlong_s + carry_s[1];
   // the positions the dK/dV grid walks past the last item hold an end marker (group -1)
-  for (int p = count + t; p < walk; p += 1024) it_out[p] = make_int4(-1, 0, 0, -1);
+  for (int p = count + t; p < walk; p += kT) it_out[p] = make_int4(-1, 0, 0, -1);
+}
+
+// grid.x = slices, 1024 threads.
+__global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ col_ptr, int4* __restrict__ items,
+                                                   int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                                   Geom g, CscGeom cg, DkdvBounds bd, int S, int walk) {
+  dkdv_order_block<1024>(col_ptr, items, splits, counters, g, cg, bd, S, walk, blockIdx.x);
+}
+
+// The pooled-token reduction (step 2) and the dK/dV work lists (step 3a) in one launch: they are independent --
+// the lists need only the CSC, the reduction the dQ kernel's partials.  Blocks 0 .. slices-1 build the lists
+// (256 threads each), block slices + slice * tokens + j reduces token j of the slice's levels 2..Le.
+__global__ __launch_bounds__(256) void reduce_and_order(const int32_t* __restrict__ col_ptr,
+                                                        const int32_t* __restrict__ perm,
+                                                        const float* __restrict__ part_k,
+                                                        const float* __restrict__ part_v, float* __restrict__ gk,
+                                                        float* __restrict__ gv, int4* __restrict__ items,
+                                                        int4* __restrict__ splits, int32_t* __restrict__ counters,
+                                                        Geom g, CscGeom cg, DkdvBounds bd, int S, int walk,
+                                                        int tokens) {
+  const int b = blockIdx.x;
+  if (b < g.bh) {
+    dkdv_order_block<256>(col_ptr, items, splits, counters, g, cg, bd, S, walk, b);
+    return;
+  }
+  const int slice = (b - g.bh) / tokens;
+  coarse_reduce_block(col_ptr, perm, part_k, part_v, gk, gv, g, cg, slice, b - g.bh - slice * tokens);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1021,22 +1053,36 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Work lists, then the dK/dV kernel (one launch each; the caller's timer brackets both).
+// Split length and list length of the dK/dV work lists.
+struct DkdvPlan {
+  int S;     // groups longer than S stages are split
+  int walk;  // item positions per slice the kernel walks
+};
 template <bool kComp>
-void launch_dkdv(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v, const float* lse,
-                 const void* dout, const void* pk, const void* pv, const int32_t* col_ptr, const int32_t* perm,
-                 void* dk, void* dv, const BwdWs& ws, hipStream_t stream) {
+DkdvPlan dkdv_plan(const Geom& g) {
   const int n1 = g.rows[1];
   const DkdvBounds bd = dkdv_bounds(g);
   // split length: twice the stages per resident wavefront (all slices' n_1 K stages spread over the waves
   // the device holds), at least kSplitMul x the mean group length
   const int64_t waves = 4 * (int64_t)std::max(1, resident_workgroups((const void*)bwd_dkdv_bf16<kComp>, 256));
   const int64_t per_wave = ((int64_t)g.bh * n1 * g.K + waves - 1) / waves;
-  const int S = (int)std::min<int64_t>(std::max<int64_t>(kSplitMul * kGroup * g.K, 2 * per_wave), 1 << 30);
+  DkdvPlan pl;
+  pl.S = (int)std::min<int64_t>(std::max<int64_t>(kSplitMul * kGroup * g.K, 2 * per_wave), 1 << 30);
   // items per slice with this S: groups + at most 2 n_1 K / S chunks beyond one per split group
-  const int walk = (int)std::min<int64_t>(bd.items, (n1 + kGroup - 1) / kGroup + 2 * (int64_t)n1 * g.K / S + 1);
+  pl.walk = (int)std::min<int64_t>(bd.items, (n1 + kGroup - 1) / kGroup + 2 * (int64_t)n1 * g.K / pl.S + 1);
+  return pl;
+}
+
+// The work lists (unless lists_ready: built already, with the same plan), then the dK/dV kernel.
+template <bool kComp>
+void launch_dkdv(const Geom& g, const CscGeom& cg, const void* q, const void* k, const void* v, const float* lse,
+                 const void* dout, const void* pk, const void* pv, const int32_t* col_ptr, const int32_t* perm,
+                 void* dk, void* dv, const BwdWs& ws, const DkdvPlan& pl, bool lists_ready, hipStream_t stream) {
+  const DkdvBounds bd = dkdv_bounds(g);
+  const int walk = pl.walk;
   const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * walk + 3) / 4) : (g.bh * walk + 3) / 4;
-  dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, S, walk);
+  if (!lists_ready)
+    dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, pl.S, walk);
   bwd_dkdv_bf16<kComp><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
                                                  (const bf16_t*)dout, lse, ws.delta, (const bf16_t*)pk,
                                                  (const bf16_t*)pv, col_ptr, perm, ws.gk, ws.gv, ws.items, ws.splits,
@@ -1117,16 +1163,19 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
         (const bf16_t*)pk, (const bf16_t*)pv,
         idx, (bf16_t*)dq, ws.delta, ws.part_k, ws.part_v, idx, g, CompGeom{});
   }
+  const DkdvPlan pl = dkdv_plan<false>(g);
   if (g.Le >= 2) {
+    // the pooled-token reduction, with the dK/dV work lists built beside it
     int tokens = 0;
     for (int l = 2; l <= g.Le; ++l) tokens += g.rows[l];
     LaunchTimer timer(kBwdReduce, stream);
-    coarse_reduce<<<dim3(tokens, g.bh), 256, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, g,
-                                                          cg);
+    reduce_and_order<<<g.bh + tokens * g.bh, 256, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv,
+                                                                ws.items, ws.splits, ws.split_done, g, cg,
+                                                                dkdv_bounds(g), pl.S, pl.walk, tokens);
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    launch_dkdv<false>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, stream);
+    launch_dkdv<false>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, pl, g.Le >= 2, stream);
   }
   return hipGetLastError();
 }
@@ -1149,7 +1198,8 @@ hipError_t launch_attn_bwd_complement(const Geom& g, const CscGeom& cg, const Co
   if (e != hipSuccess) return e;
   {
     LaunchTimer timer(kBwdDkdv, stream);
-    launch_dkdv<true>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, stream);
+    launch_dkdv<true>(g, cg, q, k, v, lse, dout, pk, pv, col_ptr, perm, dk, dv, ws, dkdv_plan<true>(g), false,
+                      stream);
   }
   return hipGetLastError();
 }
