@@ -40,7 +40,7 @@ ATTN = ("attn_fwd", "bwd_dq", "bwd_reduce", "bwd_dkdv")
 def kernel_symbol(name, dtype):
     return {"pool": "pool_levels12", "select": "select_level",
             "attn_fwd": "attn_fwd_bf16" if dtype == "bf16" else "attn_fwd_f32",
-            "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "coarse_reduce",
+            "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "reduce_and_order",
             "bwd_dkdv": "bwd_dkdv_bf16"}[name]
 
 

@@ -33,7 +33,7 @@ KERNEL_SOURCES = {
     "attn_fwd_bf16": ["attn_fwd.hip"] + _COMMON,
     "bwd_dq_bf16": ["attn_bwd.hip"] + _COMMON,
     "bwd_dkdv_bf16": ["attn_bwd.hip"] + _COMMON,
-    "coarse_reduce": ["attn_bwd.hip"] + _COMMON,
+    "reduce_and_order": ["attn_bwd.hip"] + _COMMON,
     "pool_levels12": ["pyramid.hip", "common.hpp", "launch.hpp"],
     "select_level": ["select.hip", "common.hpp", "launch.hpp"],
 }
