@@ -18,6 +18,8 @@
 //     taken in ascending slot order and the kept slots are compacted in ascending order with ballot
 //     prefix counts -- candidate slots ascend with block index, so this realises the tie rule and the
 //     ascending row order directly.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -236,34 +238,19 @@ __device__ __forceinline__ void topk_dispatch(const float* sc, int ldc, int ncan
   }
 }
 
-// Coarsest: grid.x = 16-row query tiles, grid.y = slice.  Descent: 1-D grid over (slice, parent unit at
-// level+1), remapped so that consecutive parents run on one XCD and its L2 holds their slices' pooled keys.
-// Dynamic LDS: 16 rows x ldc floats of scores.
+// Scores and Top-K of the query rows q0 .. q0+nq-1 of `level` (nq <= 16), written to `out` (nq rows of K).
+// coarsest: the candidates are all n_L blocks; else the B children of each pick of the parent, read from
+// `cand_picks` (the parent's selection row, in memory or LDS), with `lds_picks` the same picks in LDS for the
+// block numbers of the kept slots.  Dynamic LDS `sc`: 16 rows x ldc floats of scores.  Ends after the Top-K
+// (the caller orders any reuse of sc).
 template <int kMode>
-__global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq, const float* __restrict__ pk,
-                                                    int32_t* __restrict__ idx, Geom g, int level, int coarsest,
-                                                    int ncand, int ldc) {
-  extern __shared__ float sc[];
-  int slice = blockIdx.y, bx = blockIdx.x;
-  if (!coarsest) {
-    const int np = g.rows[level + 1];
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    slice = wg / np; bx = wg - slice * np;
-  }
+__device__ __forceinline__ void select_rows(const float* __restrict__ PQ, const float* __restrict__ PK,
+                                            const Geom& g, int level, int coarsest, int q0, int nq,
+                                            const int32_t* cand_picks, const int32_t* lds_picks, int ncand, int ldc,
+                                            float* sc, int32_t* out) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, gg = lane >> 4;
-  const float* PQ = pq + (size_t)slice * g.R * kD;
-  const float* PK = pk + (size_t)slice * g.R * kD;
-  int32_t* I = idx + (size_t)slice * g.R * g.K;
   const int nl = g.rows[level];
-  const int q0 = 16 * bx;
-  const int nq = coarsest ? min(16, nl - q0) : 16;
-  const int32_t* picks = coarsest ? nullptr : I + (size_t)(g.off[level + 1] + bx) * g.K;
   const int ntiles = (ncand + 15) / 16;
-  // the parent's picks also in LDS, for the block numbers of the kept slots (a global read there would wait
-  // behind the row's stores, which may alias it)
-  __shared__ int pks[32];
-  if (!coarsest && threadIdx.x < g.K) pks[threadIdx.x] = picks[threadIdx.x];
-
   // A operand: this lane's query row (q0 + c); step s = 4m + e uses dim 16m + 4gg + e, so that the four lanes
   // of a row read 64 contiguous bytes per load (the same dim order for both operands).
   float qf[16];
@@ -283,7 +270,7 @@ __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq
       j = 16 * t + c;
       *valid = j < nl;
     } else {
-      j = picks[t] * kB + c;
+      j = cand_picks[t] * kB + c;
       *valid = true;
     }
     return g.off[level] + (*valid ? j : 0);
@@ -321,7 +308,48 @@ __global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq
   }
   __syncthreads();
 
-  topk_dispatch<kMode>(sc, ldc, ncand, nq, g.K, w, lane, I + (size_t)(g.off[level] + q0) * g.K, pks, coarsest);
+  topk_dispatch<kMode>(sc, ldc, ncand, nq, g.K, w, lane, out, lds_picks, coarsest);
+}
+
+// Coarsest: grid.x = 16-row query tiles, grid.y = slice.  Descent: 1-D grid over (slice, parent unit at
+// level+1), remapped so that consecutive parents run on one XCD and its L2 holds their slices' pooled keys.
+// kTop >= 0 (the descent from the coarsest level only): the workgroup first selects its parent's own row of the
+// coarsest level (Top-K mode kTop; the same products and Top-K as the coarsest launch, so the same picks) and
+// keeps it in LDS, which saves the coarsest level its own launch.  Dynamic LDS: 16 rows x ldc floats of scores
+// (ldc covers the coarsest level's candidates too when kTop >= 0).
+template <int kMode, int kTop>
+__global__ __launch_bounds__(256) void select_level(const float* __restrict__ pq, const float* __restrict__ pk,
+                                                    int32_t* __restrict__ idx, Geom g, int level, int coarsest,
+                                                    int ncand, int ldc) {
+  extern __shared__ float sc[];
+  int slice = blockIdx.y, bx = blockIdx.x;
+  if (!coarsest) {
+    const int np = g.rows[level + 1];
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    slice = wg / np; bx = wg - slice * np;
+  }
+  const float* PQ = pq + (size_t)slice * g.R * kD;
+  const float* PK = pk + (size_t)slice * g.R * kD;
+  int32_t* I = idx + (size_t)slice * g.R * g.K;
+  const int nl = g.rows[level];
+  const int q0 = 16 * bx;
+  const int nq = coarsest ? min(16, nl - q0) : 16;
+  // the parent's picks also in LDS, for the block numbers of the kept slots (a global read there would wait
+  // behind the row's stores, which may alias it)
+  __shared__ int pks[32];
+  const int32_t* picks = nullptr;
+  if constexpr (kTop >= 0) {
+    const int nL = g.rows[level + 1];
+    select_rows<kTop>(PQ, PK, g, level + 1, 1, bx, 1, nullptr, nullptr, nL, ldc, sc, pks);
+    __syncthreads();  // the row is in pks, and the scores are read
+    if (threadIdx.x < g.K) I[(size_t)(g.off[level + 1] + bx) * g.K + threadIdx.x] = pks[threadIdx.x];
+    picks = pks;
+  } else {
+    picks = coarsest ? nullptr : I + (size_t)(g.off[level + 1] + bx) * g.K;
+    if (!coarsest && threadIdx.x < g.K) pks[threadIdx.x] = picks[threadIdx.x];
+  }
+  select_rows<kMode>(PQ, PK, g, level, coarsest, q0, nq, picks, pks, ncand, ldc, sc,
+                     I + (size_t)(g.off[level] + q0) * g.K);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -458,39 +486,52 @@ __global__ __launch_bounds__(256) void select_exhaustive(const float* __restrict
 
 }  // namespace
 
-// select_level's instance for the level's Top-K mode
-static void launch_select_level(dim3 grid, int ldc, hipStream_t stream, const float* pq, const float* pk, int32_t* idx,
-                         const Geom& g, int level, int coarsest, int ncand) {
+// select_level's instance for the level's Top-K mode (and, top >= 0, the fused coarsest row's)
+template <int kTop>
+static void launch_select_level_t(dim3 grid, int ldc, hipStream_t stream, const float* pq, const float* pk,
+                                  int32_t* idx, const Geom& g, int level, int coarsest, int ncand) {
   const size_t lds = 16 * ldc * sizeof(float);
   switch (topk_mode(g.K, ncand)) {
     case kMerge8:
-      select_level<kMerge8><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+      select_level<kMerge8, kTop><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
       break;
     case kMerge16:
-      select_level<kMerge16><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+      select_level<kMerge16, kTop><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
       break;
     default:
-      select_level<kBitwise><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
+      select_level<kBitwise, kTop><<<grid, 256, lds, stream>>>(pq, pk, idx, g, level, coarsest, ncand, ldc);
   }
 }
 
 hipError_t launch_select(const Geom& g, const float* pq, const float* pk, int32_t* idx, hipStream_t stream) {
-  // coarsest level: all n_L blocks are candidates
-  {
-    const int nL = g.rows[g.L];
-    const int ncand = ((nL + 15) / 16) * 16;
-    const int ldc = ncand + 4;
-    dim3 grid((nL + 15) / 16, g.bh);
+  const int nL = g.rows[g.L];
+  const int ncandL = ((nL + 15) / 16) * 16;
+  if (g.L == 1) {  // the coarsest level alone: all n_L blocks are candidates
     LaunchTimer timer(kSelect, stream);
-    launch_select_level(grid, ldc, stream, pq, pk, idx, g, g.L, 1, nL);
+    launch_select_level_t<-1>(dim3((nL + 15) / 16, g.bh), ncandL + 4, stream, pq, pk, idx, g, g.L, 1, nL);
+    return hipGetLastError();
   }
   for (int l = g.L - 1; l >= 1; --l) {
     const int ncand = g.K * kB;
-    const int ldc = ncand + 4;
-    // one workgroup per (slice, parent), on a 1-D grid remapped so that an XCD takes consecutive parents
+    // one workgroup per (slice, parent), on a 1-D grid remapped so that an XCD takes consecutive parents; the
+    // first descent also selects its parent's coarsest row
     const int grid = g.rows[l + 1] * g.bh;
     LaunchTimer timer(kSelect, stream);
-    launch_select_level(dim3(grid), ldc, stream, pq, pk, idx, g, l, 0, ncand);
+    if (l == g.L - 1) {
+      const int ldc = std::max(ncand, ncandL) + 4;
+      switch (topk_mode(g.K, nL)) {
+        case kMerge8:
+          launch_select_level_t<kMerge8>(dim3(grid), ldc, stream, pq, pk, idx, g, l, 0, ncand);
+          break;
+        case kMerge16:
+          launch_select_level_t<kMerge16>(dim3(grid), ldc, stream, pq, pk, idx, g, l, 0, ncand);
+          break;
+        default:
+          launch_select_level_t<kBitwise>(dim3(grid), ldc, stream, pq, pk, idx, g, l, 0, ncand);
+      }
+    } else {
+      launch_select_level_t<-1>(dim3(grid), ncand + 4, stream, pq, pk, idx, g, l, 0, ncand);
+    }
   }
   return hipGetLastError();
 }
