@@ -10,8 +10,9 @@
 //   * One 256-thread workgroup per (slice, parent unit at level l+1): its B = 16 child units share the
 //     same K*16 candidate rows, so the scores are a 16 x (16K) x 64 fp32 product, run on
 //     v_mfma_f32_16x16x4_f32 (fp32 keeps the ranking faithful to the exact scores).  The coarsest
-//     level uses the same kernel with "all n_L blocks" as the candidate list, 16 query units per
-//     workgroup.
+//     level uses the same products and Top-K with "all n_L blocks" as the candidate list: for L = 1 in a
+//     launch of its own (16 query units per workgroup), else inside the first descent launch, whose
+//     workgroup selects its parent's coarsest row before the parent's children.
 //   * Top-K per query row without sorting: a 32-step bitwise search for the K-th largest
 //     order-preserving score key (one compare + one ballot per slot group and step, the group count a
 //     compile-time constant), then ties at the threshold are
