@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
                                                       float* __restrict__ delta, float* __restrict__ part_k,
                                                       float* __restrict__ part_v, const int32_t* __restrict__ esrc,
                                                       Geom g, CompGeom cm) {
-  __shared__ __attribute__((aligned(16))) bf16_t kts[4][32 * kD];      // K tiles (swizzled)
-  __shared__ __attribute__((aligned(16))) bf16_t vts[4][32 * kD];      // V tiles (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t kvts[2][4][32 * kD];  // K tiles, then V tiles (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t qsl[4][2][16 * kD];   // Q rows, two slots (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t dsl[4][2][16 * kD];   // dO rows, two slots (swizzled)
   __shared__ __attribute__((aligned(16))) bf16_t osl[4][16 * kD];      // O rows of the next block (swizzled)
@@ -99,8 +98,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   const Sweep su = xcd_sweep(g.bh * gps, blockIdx.x / 8, gridDim.x / 8);
   if (su.count == 0) return;  // uniform over the workgroup
   const int nblk = 4 * su.count;
-  bf16_t* kt = kts[w];
-  bf16_t* vt = vts[w];
+  bf16_t* kt = kvts[0][w];
+  bf16_t* vt = kvts[1][w];
   const Plan plan = make_plan(g, kComp ? cm.total : g.K * g.Le);
   const int nst = plan.nstages;
   const int nhigh = (!kComp && g.Le >= 2) ? g.K * (g.Le - 1) : 0;
@@ -324,49 +323,50 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     st16_nt(ob + 8 * kD, x1);
   };
 
-  // End of the workgroup's ju-th unit: fixed-order reduction of the four waves' partials through LDS (the
-  // K tiles' space), then one store per element.
+  // End of the workgroup's ju-th unit: the four waves' partials summed through LDS (the K and V tiles' space,
+  // free between stages), 16 entries at a time: every wave writes its partials to a region of its own at once,
+  // then each thread sums its elements over the four regions in wave order -- ((w0 + w1) + w2) + w3, a fixed
+  // order -- and stores them.
   auto unit_end = [&](int ju) {
     if (nhigh == 0) return;
     const int U = su.first + su.stride * ju;
     const int slice = uniform(U / gps), u2 = U - slice * gps;
-    float* red = reinterpret_cast<float*>(&kts[0][0]);  // [2][32][kD] fp32 = 16 KB
-    barrier_lds();
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      if (w == ww) {
-#pragma unroll
-        for (int T = 0; T < kT; ++T)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int e = 16 * T + 4 * gq + r, d = 16 * t + c;
-              float* rk = red + e * kD + d;
-              float* rv = red + (32 + e) * kD + d;
-              if (ww == 0) {
-                *rk = gk_acc[T][t][r];
-                *rv = gv_acc[T][t][r];
-              } else {
-                *rk += gk_acc[T][t][r];
-                *rv += gv_acc[T][t][r];
-              }
-            }
-      }
-      barrier_lds();
-    }
+    constexpr int kRegion = 2 * 16 * kD;                       // floats per wave: [K, V][16 entries][kD]
+    float* red = reinterpret_cast<float*>(&kvts[0][0][0]);    // 4 regions = 32 KB
     float* outk = part_k + ((size_t)slice * gps + u2) * nhigh * kD;
     float* outv = part_v + ((size_t)slice * gps + u2) * nhigh * kD;
-    // fully unrolled (no inner loop, whose preheader would make the compiler drain the loads in flight)
 #pragma unroll
-    for (int it = 0; it < 4 * kT; ++it) {
-      const int x = threadIdx.x + 256 * it;
-      if (x < nhigh * kD) {
-        outk[x] = red[x] * g.scale;
-        outv[x] = red[32 * kD + x];
+    for (int T = 0; T < kT; ++T) {
+      barrier_lds();  // the tiles' last reads, or the previous entries' sums, are done
+      float* mine = red + w * kRegion;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * gq + r, d = 16 * t + c;
+          mine[e * kD + d] = gk_acc[T][t][r];
+          mine[(16 + e) * kD + d] = gv_acc[T][t][r];
+        }
+      barrier_lds();
+      // fully unrolled (no inner loop, whose preheader would make the compiler drain the loads in flight)
+#pragma unroll
+      for (int it = 0; it < kRegion / 256; ++it) {
+        const int x = threadIdx.x + 256 * it;  // [K, V][entry][dim] within the region
+        const int xe = x & (16 * kD - 1), eg = 16 * T + (xe >> 6);
+        if (eg < nhigh) {
+          float sum = red[x];
+          sum += red[kRegion + x];
+          sum += red[2 * kRegion + x];
+          sum += red[3 * kRegion + x];
+          const size_t o = (size_t)eg * kD + (xe & (kD - 1));
+          if (x < 16 * kD)
+            outk[o] = sum * g.scale;
+          else
+            outv[o] = sum;
+        }
       }
     }
-    barrier_lds();
+    barrier_lds();  // the tiles are free for the next stage
 #pragma unroll
     for (int T = 0; T < kT; ++T)
 #pragma unroll
