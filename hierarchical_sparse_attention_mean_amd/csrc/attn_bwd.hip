@@ -8,11 +8,11 @@
 //   Pooled level-l tokens pass their gradient to the B^l raw tokens they average with factor B^-l.
 //
 // Kernels, in stream order:
-//   1. bwd_dq (Q-major, one wavefront per fine query block, four waves per workgroup, the workgroup
-//      owning the 16 fine blocks of one level-2 unit): recomputes P over fine and enrichment entries,
-//      writes dQ and Delta, and -- because all 256 queries of a level-2 unit share the enrichment tokens
-//      of levels >= 2 -- accumulates their dK^(l), dV^(l) contributions for the unit in registers and
-//      reduces the four waves in LDS in a fixed order (partials per level-2 unit and slot).
+//   1. bwd_dq (Q-major, each wavefront owning whole level-2 units and running their 16 fine blocks in
+//      turn): recomputes P over fine and enrichment entries, writes dQ and Delta, and -- because all 256
+//      queries of a level-2 unit share the enrichment tokens of levels >= 2 -- accumulates their dK^(l),
+//      dV^(l) contributions for the unit in registers and stores them at the unit's end (partials per
+//      level-2 unit and slot).
 //   2. reduce_and_order: for each pooled token of levels >= 2, sums the partials of the (unit, slot) pairs
 //      that kept it, found through that level's CSC column (no atomics); beside it, in the same launch, the
 //      dK/dV work lists (dkdv_order's job, which needs only the CSC).
@@ -58,10 +58,13 @@ __device__ __forceinline__ bf16x4 pack4(float a, float b, float c, float d) {
 
 // ------------------------------------------------------------------------------------------------
 // 1. dQ, Delta and the level >= 2 pooled-token partials.
-// Persistent: grid = 8 * (workgroups resident per XCD), 256 threads.  A workgroup takes level-2 units
-// (16 fine blocks each) from its XCD's sweep; wave w runs blocks w, w+4, w+8, w+12 of each unit (ragged
-// units run clamped dummy blocks whose results are dropped), and its stage list is the concatenation of
-// those blocks' stages, the next block's first stage in flight while the current one finishes.  A block's
+// Persistent: grid = 8 * (workgroups resident per XCD), 256 threads.  Each wave takes level-2 units (16 fine
+// blocks each) from its XCD's sweep (wave slot 4 * (b / 8) + w) and runs their blocks in order (ragged units
+// run clamped dummy blocks whose results are dropped); its stage list is the concatenation of those blocks'
+// stages, the next block's first stage in flight while the current one finishes.  A unit's pooled-token
+// partials stay in the wave's registers and are stored when its last block ends: the waves of a workgroup never
+// wait for each other (four waves sharing a unit and summing their partials through LDS made the step 13.5 us
+// slower at N = 65536, most of it waves waiting at the unit ends).  A block's
 // Q, dO, O rows, LSE and indices are copied to LDS a whole block ahead (LDS DMA).  Gathered K / V / pyramid
 // rows are loaded coalesced (issue_stage_coalesced) and reordered through swizzled LDS tiles.
 // ------------------------------------------------------------------------------------------------
@@ -95,9 +98,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     fill_entry_tab(g, tab);
   const int n1 = g.rows[1];
   const int gps = (n1 + 15) / 16;
-  const Sweep su = xcd_sweep(g.bh * gps, blockIdx.x / 8, gridDim.x / 8);
-  if (su.count == 0) return;  // uniform over the workgroup
-  const int nblk = 4 * su.count;
+  const Sweep su = xcd_sweep(g.bh * gps, 4 * (blockIdx.x / 8) + w, 4 * (gridDim.x / 8));  // units of this wave
+  if (su.count == 0) return;  // no workgroup barrier is used below
+  const int nblk = 16 * su.count;
   bf16_t* kt = kvts[0][w];
   bf16_t* vt = kvts[1][w];
   const Plan plan = make_plan(g, kComp ? cm.total : g.K * g.Le);
@@ -114,11 +117,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
   // the wave's j-th block (clamped to the last)
   auto blk = [&](int j) {
     const int jc = min(j, nblk - 1);
-    const int U = su.first + su.stride * (jc >> 2);
+    const int U = su.first + su.stride * (jc >> 4);
     Blk b;
     b.slice = uniform(U / gps);
     b.u2 = U - b.slice * gps;
-    const int i = 16 * b.u2 + w + 4 * (jc & 3);
+    const int i = 16 * b.u2 + (jc & 15);
     b.valid = i < n1;
     b.i = min(i, n1 - 1);
     return b;
@@ -331,42 +334,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     if (nhigh == 0) return;
     const int U = su.first + su.stride * ju;
     const int slice = uniform(U / gps), u2 = U - slice * gps;
-    constexpr int kRegion = 2 * 16 * kD;                       // floats per wave: [K, V][16 entries][kD]
-    float* red = reinterpret_cast<float*>(&kvts[0][0][0]);    // 4 regions = 32 KB
     float* outk = part_k + ((size_t)slice * gps + u2) * nhigh * kD;
     float* outv = part_v + ((size_t)slice * gps + u2) * nhigh * kD;
 #pragma unroll
-    for (int T = 0; T < kT; ++T) {
-      barrier_lds();  // the tiles' last reads, or the previous entries' sums, are done
-      float* mine = red + w * kRegion;
+    for (int T = 0; T < kT; ++T)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int e = 4 * gq + r, d = 16 * t + c;
-          mine[e * kD + d] = gk_acc[T][t][r];
-          mine[(16 + e) * kD + d] = gv_acc[T][t][r];
+          const int e = 16 * T + 4 * gq + r, d = 16 * t + c;
+          if (e < nhigh) {
+            outk[e * kD + d] = gk_acc[T][t][r] * g.scale;
+            outv[e * kD + d] = gv_acc[T][t][r];
+          }
         }
-      barrier_lds();
-      // fully unrolled (no inner loop, whose preheader would make the compiler drain the loads in flight)
-#pragma unroll
-      for (int it = 0; it < kRegion / 256; ++it) {
-        const int x = threadIdx.x + 256 * it;  // [K, V][entry][dim] within the region
-        const int xe = x & (16 * kD - 1), eg = 16 * T + (xe >> 6);
-        if (eg < nhigh) {
-          float sum = red[x];
-          sum += red[kRegion + x];
-          sum += red[2 * kRegion + x];
-          sum += red[3 * kRegion + x];
-          const size_t o = (size_t)eg * kD + (xe & (kD - 1));
-          if (x < 16 * kD)
-            outk[o] = sum * g.scale;
-          else
-            outv[o] = sum;
-        }
-      }
-    }
-    barrier_lds();  // the tiles are free for the next stage
 #pragma unroll
     for (int T = 0; T < kT; ++T)
 #pragma unroll
@@ -378,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     if (++cs == nst) {
       finish_block();
       cs = 0;
-      if ((cj & 3) == 3) unit_end(cj >> 2);
+      if ((cj & 15) == 15) unit_end(cj >> 4);
       if (++cj < nblk) {
         par ^= 1;
         cur = nxt;
