@@ -15,8 +15,8 @@ Recipe
   covariance proportional to exp(-r^2 / (2 l^2)) (``l`` = length scale in pixels), made by filtering
   white noise in the Fourier domain with exp(-pi^2 l^2 |f|^2) (f in cycles per pixel); each channel
   is standardised, flattened row-major to ``F`` of shape [H*W, C], projected by ``P`` [C, d] with
-  entries N(0, 1/C), and Q = F P + a*eps_Q, K = F P + a*eps_K, V = F P + a*eps_V with independent
-  eps ~ N(0, 1) and noise amplitude ``a``.
+  entries N(0, 1/C) (the product summed channel by channel, elementwise), and Q = F P + a*eps_Q,
+  K = F P + a*eps_K, V = F P + a*eps_V with independent eps ~ N(0, 1) and noise amplitude ``a``.
 * ``"hub"``: i.i.d. N(0, 1) rows plus a shared direction ``u`` (entries +-1, drawn per slice from the
   projection stream): every query row gets ``hub_gain * u`` and so do the key rows of the first
   ``hub_tokens`` tokens, so that every unit's selection keeps the blocks that hold them -- a few key
@@ -138,7 +138,11 @@ def _slice_values(w: Workload, s: int, d: int):
     if w.kind == "field":
         F = smooth_field(w.seed, s, w.grid, w.length_scale, w.channels)
         P = rng(w.seed, s, STREAM_PROJ).standard_normal((w.channels, d)) / math.sqrt(w.channels)
-        X = F @ P
+        # F P as a channel-by-channel sum of elementwise products: the same bits on every run, machine and
+        # thread (a BLAS product here gave wrong values when slices were drawn on several threads at once)
+        X = F[:, 0:1] * P[0]
+        for c in range(1, w.channels):
+            X = X + F[:, c:c + 1] * P[c]
         return [X + w.noise * rng(w.seed, s, st).standard_normal((n, d))
                 for st in (STREAM_Q, STREAM_K, STREAM_V)]
     if w.kind == "hub":

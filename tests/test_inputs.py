@@ -18,6 +18,19 @@ def test_deterministic_and_slice_independent():
         assert not np.array_equal(a[name].store[0, 0], a[name].store[0, 1])
 
 
+def test_field_slices_drawn_together_equal_slices_drawn_alone():
+    """The largest field workload (262144 tokens per slice): slices drawn on several threads at once hold the
+    same values as each slice drawn alone, on every draw (a threaded BLAS product of F and P once broke this)."""
+    w = inputs.WORKLOADS["fwdbwd_bf16_n262144"]
+    heads = [0, 1, 2, 3]
+    alone = [inputs.make_inputs(w, heads=[s], with_dout=False) for s in heads]
+    for _ in range(2):
+        together = inputs.make_inputs(w, heads=heads, with_dout=False)
+        for name in ("q", "k", "v"):
+            for i in range(len(heads)):
+                assert np.array_equal(together[name].store[0, i], alone[i][name].store[0, 0]), (name, heads[i])
+
+
 def test_bf16_rounding_is_round_to_nearest_even():
     x = np.random.default_rng(0).standard_normal(100000) * 10.0 ** np.random.default_rng(1).integers(-8, 8, 100000)
     bits = inputs.round_to_bf16_bits(x)
