@@ -416,12 +416,14 @@ __device__ __forceinline__ void coarse_reduce_block(const int32_t* __restrict__ 
   const float* PKs = part_k + (size_t)slice * n2 * nhigh * kD + d4;
   const float* PVs = part_v + (size_t)slice * n2 * nhigh * kD + d4;
   float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
-  // wave w takes items 16 r + 4 w + q4 (r = 0, 1, ...): two rounds of four lanes' items per iteration
-  for (int q0 = 4 * w + q4; q0 < items; q0 += 32) {
-    float4 xk[2], xv[2];
+  // wave w takes items 16 r + 4 w + q4 (r = 0, 1, ...), summed per lane in r order; the items of pair m are
+  // 32 m + 4 w + q4 and that + 16 (the second zero past the end), and a pair counts while its first item exists.
+  // Four pairs are loaded per trip (a level-3 token's 8 items per lane at once), then added in pair order.
+  for (int m0 = 0; 32 * m0 + 4 * w + q4 < items; m0 += 4) {
+    float4 xk[8], xv[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = q0 + 16 * i;
+    for (int i = 0; i < 8; ++i) {
+      const int q = 32 * m0 + 4 * w + q4 + 16 * i;
       xk[i] = xv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (q < items) {
         const int p = pm[y0 + (q >> sh)];
@@ -436,9 +438,11 @@ __device__ __forceinline__ void coarse_reduce_block(const int32_t* __restrict__ 
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ak.x += xk[i].x; ak.y += xk[i].y; ak.z += xk[i].z; ak.w += xk[i].w;
-      av.x += xv[i].x; av.y += xv[i].y; av.z += xv[i].z; av.w += xv[i].w;
+    for (int i = 0; i < 8; ++i) {
+      if (32 * (m0 + i / 2) + 4 * w + q4 < items) {
+        ak.x += xk[i].x; ak.y += xk[i].y; ak.z += xk[i].z; ak.w += xk[i].w;
+        av.x += xv[i].x; av.y += xv[i].y; av.z += xv[i].z; av.w += xv[i].w;
+      }
     }
   }
   // the four item lanes of each dim group (lanes d, d + 16, d + 32, d + 48), the same order in every lane
@@ -505,14 +509,13 @@ __device__ __forceinline__ void dkdv_order_block(const int32_t* __restrict__ col
                                                  const Geom& g, const CscGeom& cg, const DkdvBounds& bd, int S,
                                                  int walk, int slice) {
   __shared__ long long wave_tot[kT / 64];
-  __shared__ int carry_s[4], nlong_s;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n1 = g.rows[1], gps = (n1 + kGroup - 1) / kGroup;
   const int32_t* cp = col_ptr + (size_t)slice * cg.cp_len + cg.cp_off[1];
   int4* it_out = items + (size_t)slice * bd.items;
   int4* sp_out = splits + (size_t)slice * bd.splits;
   const int thresh = 2 * kGroup * g.K;  // twice the mean group length
-  auto glen = [&](int gi) { return gi < gps ? cp[min(kGroup * gi + kGroup, n1)] - cp[kGroup * gi] : 0; };
+  auto glen = [&](int gi) { return cp[min(kGroup * gi + kGroup, n1)] - cp[kGroup * gi]; };
   auto chunks = [&](int T) { return T > S ? (T + S - 1) / S : 1; };
   // block-wide exclusive prefix of two counts at once (low and high 32 bits), with the totals
   auto scan = [&](int lo, int hi, int* elo, int* ehi, int* tlo, int* thi) {
@@ -537,50 +540,42 @@ __device__ __forceinline__ void dkdv_order_block(const int32_t* __restrict__ col
     *thi = (int)(tot >> 32);
     __syncthreads();
   };
-  if (t < 4) carry_s[t] = 0;
-  if (t == 0) nlong_s = 0;
-  __syncthreads();
-  if (gps > kT) {  // items of the long groups, before the others are placed (one chunk of groups needs no pass)
-    for (int base = 0; base < gps; base += kT) {
-      const int T = glen(base + t);
-      int e, x, tot, y;
-      scan(T > thresh ? chunks(T) : 0, 0, &e, &x, &tot, &y);
-      if (t == 0) nlong_s += tot;
-      __syncthreads();
-    }
-  }
-  for (int base = 0; base < gps; base += kT) {
-    const int gi = base + t;
+  // Thread t owns the contiguous run of groups [g0, g1): it counts its items, one scan places every run, and
+  // the thread then writes its run's items in group order.
+  const int m = (gps + kT - 1) / kT;
+  const int g0 = min(gps, t * m), g1 = min(gps, g0 + m);
+  int c_long = 0, c_short = 0, c_slot = 0, c_split = 0;
+  for (int gi = g0; gi < g1; ++gi) {
     const int T = glen(gi);
-    const bool in = gi < gps, lng = in && T > thresh, split = lng && T > S;
+    const bool lng = T > thresh, split = lng && T > S;
     const int nch = split ? chunks(T) : 1;
-    int e0, e1, e2, e3, t0, t1, t2, t3;
-    scan(lng ? nch : 0, in && !lng ? 1 : 0, &e0, &e1, &t0, &t1);  // item positions: long groups, the others
-    scan(split ? nch : 0, split ? 1 : 0, &e2, &e3, &t2, &t3);      // partial slots, split-group index
-    const int nlong = gps > kT ? nlong_s : t0;
-    if (split) {
-      const int p0 = carry_s[0] + e0, slot0 = carry_s[2] + e2, si = carry_s[3] + e3;
-      for (int c = 0; c < nch; ++c) it_out[p0 + c] = make_int4(gi, c, si, slot0 + c);
-      sp_out[si] = make_int4(gi, slot0, nch, T);
-      counters[(size_t)slice * bd.splits + si] = 0;
-    } else if (lng) {
-      it_out[carry_s[0] + e0] = make_int4(gi, 0, T, -1);
-    } else if (in) {
-      it_out[nlong + carry_s[1] + e1] = make_int4(gi, 0, T, -1);
-    }
-    __syncthreads();
-    if (t == 0) {
-      if (gps <= kT) nlong_s = t0;
-      carry_s[0] += t0;
-      carry_s[1] += t1;
-      carry_s[2] += t2;
-      carry_s[3] += t3;
-    }
-    __syncthreads();
+    c_long += lng ? nch : 0;
+    c_short += lng ? 0 : 1;
+    c_slot += split ? nch : 0;
+    c_split += split ? 1 : 0;
   }
-  const int count = nlong_s + carry_s[1];
+  int p_long, p_short, p_slot, p_split, nlong, nshort, t2, t3;
+  scan(c_long, c_short, &p_long, &p_short, &nlong, &nshort);  // item positions: long groups, then the others
+  scan(c_slot, c_split, &p_slot, &p_split, &t2, &t3);          // partial slots, split-group index
+  for (int gi = g0; gi < g1; ++gi) {
+    const int T = glen(gi);
+    const bool lng = T > thresh, split = lng && T > S;
+    if (split) {
+      const int nch = chunks(T);
+      for (int c = 0; c < nch; ++c) it_out[p_long + c] = make_int4(gi, c, p_split, p_slot + c);
+      sp_out[p_split] = make_int4(gi, p_slot, nch, T);
+      counters[(size_t)slice * bd.splits + p_split] = 0;
+      p_long += nch;
+      p_slot += nch;
+      ++p_split;
+    } else if (lng) {
+      it_out[p_long++] = make_int4(gi, 0, T, -1);
+    } else {
+      it_out[nlong + p_short++] = make_int4(gi, 0, T, -1);
+    }
+  }
   // the positions the dK/dV grid walks past the last item hold an end marker (group -1)
-  for (int p = count + t; p < walk; p += kT) it_out[p] = make_int4(-1, 0, 0, -1);
+  for (int p = nlong + nshort + t; p < walk; p += kT) it_out[p] = make_int4(-1, 0, 0, -1);
 }
 
 // grid.x = slices, 1024 threads.
@@ -592,7 +587,9 @@ __global__ __launch_bounds__(1024) void dkdv_order(const int32_t* __restrict__ c
 
 // The pooled-token reduction (step 2) and the dK/dV work lists (step 3a) in one launch: they are independent --
 // the lists need only the CSC, the reduction the dQ kernel's partials.  Blocks 0 .. slices-1 build the lists
-// (256 threads each), block slices + slice * tokens + j reduces token j of the slice's levels 2..Le.
+// (256 threads each); block slices + slice * tokens_hi + j reduces token j of the slice's levels 3..Le, and the
+// blocks after those the level-2 tokens, slice by slice: the longest chains (the work lists, the level >= 3
+// columns) start first.
 __global__ __launch_bounds__(256) void reduce_and_order(const int32_t* __restrict__ col_ptr,
                                                         const int32_t* __restrict__ perm,
                                                         const float* __restrict__ part_k,
@@ -600,14 +597,21 @@ __global__ __launch_bounds__(256) void reduce_and_order(const int32_t* __restric
                                                         float* __restrict__ gv, int4* __restrict__ items,
                                                         int4* __restrict__ splits, int32_t* __restrict__ counters,
                                                         Geom g, CscGeom cg, DkdvBounds bd, int S, int walk,
-                                                        int tokens) {
+                                                        int tokens_hi) {
   const int b = blockIdx.x;
   if (b < g.bh) {
     dkdv_order_block<256>(col_ptr, items, splits, counters, g, cg, bd, S, walk, b);
     return;
   }
-  const int slice = (b - g.bh) / tokens;
-  coarse_reduce_block(col_ptr, perm, part_k, part_v, gk, gv, g, cg, slice, b - g.bh - slice * tokens);
+  int r = b - g.bh;
+  if (r < g.bh * tokens_hi) {  // tokens of levels 3..Le (the longest columns, dispatched first)
+    const int slice = r / tokens_hi;
+    coarse_reduce_block(col_ptr, perm, part_k, part_v, gk, gv, g, cg, slice, g.rows[2] + r - slice * tokens_hi);
+    return;
+  }
+  r -= g.bh * tokens_hi;  // level-2 tokens
+  const int slice = r / g.rows[2];
+  coarse_reduce_block(col_ptr, perm, part_k, part_v, gk, gv, g, cg, slice, r - slice * g.rows[2]);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1147,12 +1151,12 @@ hipError_t launch_attn_bwd(const Geom& g, const CscGeom& cg, const void* q, cons
   const DkdvPlan pl = dkdv_plan<false>(g);
   if (g.Le >= 2) {
     // the pooled-token reduction, with the dK/dV work lists built beside it
-    int tokens = 0;
-    for (int l = 2; l <= g.Le; ++l) tokens += g.rows[l];
+    int tokens_hi = 0;
+    for (int l = 3; l <= g.Le; ++l) tokens_hi += g.rows[l];
     LaunchTimer timer(kBwdReduce, stream);
-    reduce_and_order<<<g.bh + tokens * g.bh, 256, 0, stream>>>(col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv,
-                                                                ws.items, ws.splits, ws.split_done, g, cg,
-                                                                dkdv_bounds(g), pl.S, pl.walk, tokens);
+    reduce_and_order<<<g.bh + (g.rows[2] + tokens_hi) * g.bh, 256, 0, stream>>>(
+        col_ptr, perm, ws.part_k, ws.part_v, ws.gk, ws.gv, ws.items, ws.splits, ws.split_done, g, cg, dkdv_bounds(g),
+        pl.S, pl.walk, tokens_hi);
   }
   {
     LaunchTimer timer(kBwdDkdv, stream);
