@@ -427,4 +427,16 @@ int llsa_attn_bwd_complement(const llsa_problem* prob, const void* q, const void
                                                    perm, dq, dk, dv, w, st));
 }
 
+int llsa_stream_wait(hipStream_t waiter, hipStream_t signaler) {
+  // an event without the system-scope fence: kernels of one device see each other's results through the
+  // device-scope release at kernel end; the host- and peer-visible fence only delays the waiting stream
+  hipEvent_t ev;
+  if (hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
+    return LLSA_ERR_LAUNCH;
+  hipError_t e = hipEventRecord(ev, signaler);
+  if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+  const hipError_t d = hipEventDestroy(ev);  // released once the recorded point completes
+  return e == hipSuccess && d == hipSuccess ? LLSA_OK : LLSA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -75,6 +75,8 @@ for _f in ("llsa_pyramid_rows", "llsa_colptr_len", "llsa_perm_len"):
     getattr(_lib, _f).restype = ctypes.c_int64
 _lib.llsa_workspace_bytes.argtypes = [_P, ctypes.c_int]
 _lib.llsa_workspace_bytes.restype = ctypes.c_size_t
+_lib.llsa_stream_wait.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+_lib.llsa_stream_wait.restype = ctypes.c_int
 _lib.llsa_timing_enable.argtypes = [ctypes.c_int]
 _lib.llsa_timing_enable.restype = ctypes.c_int
 _lib.llsa_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -116,6 +118,11 @@ def perm_len(prob: Problem) -> int:
 
 def workspace_bytes(prob: Problem, op: int) -> int:
     return int(_lib.llsa_workspace_bytes(ctypes.byref(prob), op))
+
+
+def stream_wait(waiter, signaler):
+    """`waiter` waits, on the device, for the work enqueued on `signaler` so far (device-scope event)."""
+    _check(_lib.llsa_stream_wait(_stream(waiter), _stream(signaler)), "llsa_stream_wait")
 
 
 def timing_enable(on: bool = True):
@@ -255,18 +262,14 @@ class Buffers:
 
     def forward_backward(self, q, k, v, dout, stream, side):
         """The whole chain with the index transpose on the second stream `side`, beside the forward: it needs
-        only the selection, and the backward waits for it (events; both streams at default priority)."""
-        import torch
+        only the selection, and the backward waits for it (device-scope events through stream_wait; both
+        streams at default priority)."""
         p = self.prob
-        if not hasattr(self, "_ev"):
-            self._ev = (torch.cuda.Event(), torch.cuda.Event())
         self.pyramid(q, k, v, stream)
         select(p, self.pq, self.pk, self.idx, stream)
-        self._ev[0].record(stream)
-        side.wait_event(self._ev[0])
+        stream_wait(side, stream)
         index_transpose(p, self.idx, self.col_ptr, self.perm, self.ws_t, side)
-        self._ev[1].record(side)
         attn_fwd(p, q, k, v, self.pka, self.pva, self.idx, self.o, self.lse, stream)
-        stream.wait_event(self._ev[1])
+        stream_wait(stream, side)
         attn_bwd(p, q, k, v, self.o, self.lse, dout, self.pka, self.pva, self.idx, self.col_ptr, self.perm,
                  self.dq, self.dk, self.dv, self.ws_b, stream)

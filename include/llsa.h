@@ -257,6 +257,15 @@ size_t llsa_workspace_bytes(const llsa_problem* prob, int op);
 /* Static, NUL-terminated description of a status code. */
 const char* llsa_status_string(int status);
 
+/* ---- streams ------------------------------------------------------------------------------------ */
+/* Makes `waiter` wait, on the device, for the work enqueued on `signaler` so far, through an event with
+ * no system-scope fence (HIP's hipEventDisableSystemFence): the results are visible to later kernels of
+ * this device, not to the host or other devices.  For the two-stream step, in which the index transpose
+ * runs beside the forward: one call after the selection (side waits for main) and one before the
+ * backward (main waits for side).  Both streams belong to the current device; NULL is the default
+ * stream.  The library creates and releases the event inside the call and keeps nothing.  Returns
+ * LLSA_OK, or LLSA_ERR_LAUNCH if a HIP event call fails. */
+int llsa_stream_wait(hipStream_t waiter, hipStream_t signaler);
 
 /* ---- kernel timing (for benchmarks) ------------------------------------------------------------ */
 /* Kernel families of this library, for llsa_timing_read. */
