@@ -143,12 +143,14 @@ def device_inputs(x):
 
 class Chain:
     """Buffers and the step of one workload: pool -> select -> forward, and for forward+backward workloads the
-    transpose on a second stream beside the forward, then the backward."""
+    transpose on a second stream beside the forward, then the backward.  The inputs are row-major token grids,
+    and the problem says so (grid_w: the dK/dV work-list order hint)."""
 
     def __init__(self, llsa, w, t, stream, side):
         self.llsa, self.w, self.t, self.stream, self.side = llsa, w, t, stream, side
         self.b = llsa.Buffers(llsa.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels,
-                                           dtype=llsa.BF16 if w.dtype == "bf16" else llsa.F32),
+                                           dtype=llsa.BF16 if w.dtype == "bf16" else llsa.F32,
+                                           grid_w=w.grid[1] if w.grid[1] else 0),
                               backward=w.backward)
         self.p = self.b.prob
 
@@ -371,8 +373,10 @@ def main():
         dense = dense_sdpa(w, t["q"], t["k"], t["v"], t["dout"], 3, fwd_chain, ms_step)
         print(f"dense SDPA: {dense}", file=sys.stderr, flush=True)
 
-        # the chain on 2-D-locally reordered inputs (reorder Q, K, V, dO in; O, dQ, dK, dV back out)
+        # the chain on 2-D-locally reordered inputs (reorder Q, K, V, dO in; O, dQ, dK, dV back out); the
+        # reordered tokens are no longer a row-major grid, so the problem carries no grid hint meanwhile
         H, W = w.grid
+        b.prob.grid_w = 0
         qr, kr, vr, dr = (torch.empty_like(t["q"]) for _ in range(4))
         o2, dq2, dk2, dv2 = (torch.empty_like(t["q"]) for _ in range(4))
 

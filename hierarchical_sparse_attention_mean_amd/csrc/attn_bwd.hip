@@ -496,8 +496,9 @@ namespace {
 // so the result does not depend on which chunk that is.
 // Items: an unsplit group is (group, 0, T_g, -1); chunk c of split group i is (group, c, i, first slot + c),
 // the split record (group, first slot, chunks, T_g).  Item order per slice: groups with more than twice the
-// mean length first (each expanded into its chunks), then the rest, each part in group order (stable
-// partitions by block-wide prefix sums), so the longest work starts first.  Bounds per slice (n_1 K stages in
+// mean length first (each expanded into its chunks), then the rest, each part in list order (stable
+// partitions by block-wide prefix sums), so the longest work starts first.  List order is group order, or
+// with a token grid, groups of four consecutive grid rows at the same column next to each other.  Bounds per slice (n_1 K stages in
 // all), for the smallest S: items <= groups + n_1 / 8, slots <= n_1 / 8, split groups <= n_1 / 16 (each split
 // group has T_g > S and at most 2 T_g / S chunks).
 // grid.x = slices, 1024 threads.
@@ -540,12 +541,23 @@ __device__ __forceinline__ void dkdv_order_block(const int32_t* __restrict__ col
     *thi = (int)(tot >> 32);
     __syncthreads();
   };
-  // Thread t owns the contiguous run of groups [g0, g1): it counts its items, one scan places every run, and
-  // the thread then writes its run's items in group order.
+  // List order of the groups: with a token grid (g.gpr groups per grid row), bands of four grid rows taken
+  // column by column, so that the four consecutive items a workgroup takes come from four consecutive rows --
+  // groups one row apart share query blocks, which the workgroup's waves then find in the CU's L1 -- and rows
+  // past the last whole band in group order; without a grid, group order.
+  const int band = 4 * g.gpr, banded = g.gpr > 0 ? gps / band * band : 0;
+  auto list_group = [&](int pp) {
+    if (pp >= banded) return pp;
+    const int b0 = pp / band * band, within = pp - b0;
+    return b0 + (within & 3) * g.gpr + (within >> 2);
+  };
+  // Thread t owns the contiguous run [g0, g1) of that order: it counts its items, one scan places every run,
+  // and the thread then writes its run's items in that order.
   const int m = (gps + kT - 1) / kT;
   const int g0 = min(gps, t * m), g1 = min(gps, g0 + m);
   int c_long = 0, c_short = 0, c_slot = 0, c_split = 0;
-  for (int gi = g0; gi < g1; ++gi) {
+  for (int pp = g0; pp < g1; ++pp) {
+    const int gi = list_group(pp);
     const int T = glen(gi);
     const bool lng = T > thresh, split = lng && T > S;
     const int nch = split ? chunks(T) : 1;
@@ -557,7 +569,8 @@ __device__ __forceinline__ void dkdv_order_block(const int32_t* __restrict__ col
   int p_long, p_short, p_slot, p_split, nlong, nshort, t2, t3;
   scan(c_long, c_short, &p_long, &p_short, &nlong, &nshort);  // item positions: long groups, then the others
   scan(c_slot, c_split, &p_slot, &p_split, &t2, &t3);          // partial slots, split-group index
-  for (int gi = g0; gi < g1; ++gi) {
+  for (int pp = g0; pp < g1; ++pp) {
+    const int gi = list_group(pp);
     const int T = glen(gi);
     const bool lng = T > thresh, split = lng && T > S;
     if (split) {

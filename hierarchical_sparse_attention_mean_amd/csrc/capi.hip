@@ -54,6 +54,7 @@ int resolve(const llsa_problem* in, Resolved* r) {
   if (Le < 0 || Le > L) return LLSA_ERR_SHAPE;
   float scale = p.scale == 0.0f ? 1.0f / sqrtf((float)p.d) : p.scale;
   if (!isfinite(scale)) return LLSA_ERR_PARAM;
+  if (p.grid_w < 0) return LLSA_ERR_SHAPE;
   // limits of the gfx950 kernels
   if (p.d != llsa::kD || p.block != llsa::kB) return LLSA_ERR_UNSUPPORTED;
   if (p.topk > 32 || nL > 512 || (int64_t)p.topk * Le > 128) return LLSA_ERR_UNSUPPORTED;
@@ -62,6 +63,9 @@ int resolve(const llsa_problem* in, Resolved* r) {
   p.levels = L;
   p.enrich_levels = Le;
   p.scale = scale;
+  // the grid hint applies when a grid row holds whole dK/dV key-block groups (4 blocks of B tokens)
+  const int64_t group_tokens = 4 * (int64_t)p.block;
+  if (p.grid_w > 0 && (p.grid_w % group_tokens != 0 || p.n % p.grid_w != 0)) p.grid_w = 0;
   if (r) {
     r->p = p;
     r->bh = bh;
@@ -83,6 +87,7 @@ int resolve(const llsa_problem* in, Resolved* r) {
     g.R = off;
     g.scale = scale;
     g.scale_log2 = scale * llsa::kLog2e;
+    g.gpr = (int)(p.grid_w / group_tokens);
     CscGeom& cg = r->cg;
     memset(&cg, 0, sizeof(cg));
     cg.T = Le < 1 ? 1 : Le;

@@ -40,6 +40,7 @@ struct Geom {
   int off[kMaxLevels + 2];      // off[l] = first pyramid row of level l (l >= 1)
   float scale_log2;             // sigma * log2(e)
   float scale;                  // sigma
+  int gpr;                      // dK/dV key-block groups per row of the token grid (0: no grid)
 };
 
 typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));

@@ -34,14 +34,15 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("levels", ctypes.c_int32), ("enrich_levels", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("grid_w", ctypes.c_int32)]
 
     def __repr__(self):
         return ("Problem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
 
 
-def problem(batch, heads, n, d=64, block=16, topk=8, levels=0, enrich_levels=-1, dtype=BF16, scale=0.0):
-    return Problem(batch, heads, n, d, block, topk, levels, enrich_levels, dtype, scale)
+def problem(batch, heads, n, d=64, block=16, topk=8, levels=0, enrich_levels=-1, dtype=BF16, scale=0.0, grid_w=0):
+    """grid_w: tokens per row of a row-major 2-D token grid (a scheduling hint; 0 = none)."""
+    return Problem(batch, heads, n, d, block, topk, levels, enrich_levels, dtype, scale, grid_w)
 
 
 class LlsaError(RuntimeError):

@@ -44,6 +44,16 @@ def test_resolve_defaults(L):
     assert r.levels == 3 and L.pyramid_rows(r) == 16384 + 1024 + 64
 
 
+def test_grid_hint_kept_only_where_it_applies(L):
+    """grid_w (a dK/dV scheduling hint) survives resolution only when a grid row holds whole groups of four key
+    blocks (a multiple of 4B = 64 tokens) and the rows tile n; otherwise it resolves to 0 (no grid)."""
+    assert L.resolve(L.problem(1, 2, 65536, grid_w=256)).grid_w == 256
+    assert L.resolve(L.problem(1, 2, 65536, grid_w=0)).grid_w == 0
+    assert L.resolve(L.problem(1, 2, 65536, grid_w=96)).grid_w == 0      # not a multiple of 64
+    assert L.resolve(L.problem(1, 2, 4608, grid_w=256, levels=2)).grid_w == 256   # 18 rows
+    assert L.resolve(L.problem(1, 2, 4096, grid_w=192)).grid_w == 0      # 192 does not divide 4096
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(n=4096 + 16), "ERR_SHAPE"),          # n mod B^L != 0 at the default L = 2
     (dict(n=4096, levels=3), "ERR_SHAPE"),     # L above floor(log_B n - 1)
@@ -57,6 +67,7 @@ def test_resolve_defaults(L):
     (dict(n=1 << 20, levels=1, topk=8), "ERR_UNSUPPORTED"),  # n_L = 65536 > 512
     (dict(n=4096, dtype=7), "ERR_DTYPE"),
     (dict(n=4096, scale=float("inf")), "ERR_PARAM"),
+    (dict(n=4096, grid_w=-64), "ERR_SHAPE"),
 ])
 def test_validation_codes(L, kw, code):
     base = dict(batch=1, heads=2)

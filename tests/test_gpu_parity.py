@@ -239,6 +239,30 @@ def test_split_groups_deterministic(L):
         assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+@pytest.mark.parametrize("kind,grid,levels", [("hub", (32, 128), 2), ("field", (18, 256), 2), ("field", (256, 256), 3)],
+                         ids=["hub_n4096_split_groups", "field_n4608_partial_band", "field_n65536"])
+def test_grid_hint_changes_no_output(L, kind, grid, levels):
+    """grid_w only reorders the dK/dV work list (groups of four consecutive grid rows next to each other): the
+    GPU chain gives the same bits with and without it -- on hub inputs whose long groups run as chunks, with a
+    last band of only two grid rows, and on a three-level field."""
+    H, W = grid
+    n = H * W
+    w = inputs.custom(1, 2, n, 64, "bf16", seed=37, kind=kind, grid=grid, topk=8, levels=levels, backward=True)
+    x = inputs.make_inputs(w, with_dout=True)
+    q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
+    outs = []
+    for gw in (0, W):
+        p = L.problem(1, 2, n, topk=8, levels=levels, grid_w=gw)
+        assert L.resolve(p).grid_w == gw
+        b = L.Buffers(p)
+        b.forward(q, k, v)
+        b.backward(q, k, v, do)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)])
+    for nm, a, c in zip(("idx", "o", "lse", "dq", "dk", "dv"), *outs):
+        assert torch.equal(a, c), nm
+
+
 def test_tie_rule_on_gpu(L):
     """Every pooled key equal: all scores tie exactly, every unit keeps the lowest block indices."""
     n, K = 4096, 8
