@@ -134,10 +134,20 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   const size_t esrc_slice = kComp ? (size_t)cm.slice : (size_t)g.R * g.K;
   const float sl2 = g.scale_log2;
 
+  // Fine block of sweep position ip within a slice: with a token grid (g.gpr key-block groups, 4 g.gpr fine
+  // blocks per grid row), bands of four grid rows taken column by column, so that a workgroup's four waves,
+  // which take consecutive positions, run fine blocks one grid row apart -- their selections overlap, and the
+  // shared key rows hit in the CU's L1; rows past the last whole band, and problems without a grid, in order.
+  const int brow = 4 * g.gpr, bband = 4 * brow, bbanded = g.gpr > 0 ? g.rows[1] / bband * bband : 0;
+  auto sweep_block = [&](int ip) {
+    if (ip >= bbanded) return ip;
+    const int b0 = ip / bband * bband, within = ip - b0;
+    return b0 + (within & 3) * brow + (within >> 2);
+  };
   // copy the inputs of the wave's j-th block (clamped to the last) into slot p (Q: the single Q slot)
   auto prefetch = [&](int j, int p) {
     const int gb = wb.first + wb.stride * min(j, wb.count - 1);
-    const int slice = uniform(gb / g.rows[1]), i = gb - slice * g.rows[1];
+    const int slice = uniform(gb / g.rows[1]), i = sweep_block(gb - slice * g.rows[1]);
     const bf16_t* qrows = q + slice * slice_elems + (size_t)16 * i * kD;  // 2 KB, contiguous
     lds_dma16_nt(qrows + 8 * lane, &qs[w][0]);
     lds_dma16_nt(qrows + 512 + 8 * lane, &qs[w][512]);
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
 
   auto finish_block = [&]() {
     const int gb = wb.first + wb.stride * cj;
-    const int i = gb - cslice * g.rows[1];
+    const int i = sweep_block(gb - cslice * g.rows[1]);
     const float lt = group_sum(sm.l);
     const float inv = 1.0f / lt;
     // O^T[d][query c] -> bf16 rows of the K tile (query c, dims 16t + 4g .. +3), then coalesced 16-byte stores
