@@ -326,10 +326,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16_t* __restrict__
     st16_nt(ob + 8 * kD, x1);
   };
 
-  // End of the workgroup's ju-th unit: the four waves' partials summed through LDS (the K and V tiles' space,
-  // free between stages), 16 entries at a time: every wave writes its partials to a region of its own at once,
-  // then each thread sums its elements over the four regions in wave order -- ((w0 + w1) + w2) + w3, a fixed
-  // order -- and stores them.
+  // End of the wave's ju-th unit: the pooled-token partials it accumulated in registers over the unit's 16
+  // blocks are stored to the unit's slot (K partials with the softmax scale), and the accumulators cleared.
   auto unit_end = [&](int ju) {
     if (nhigh == 0) return;
     const int U = su.first + su.stride * ju;
