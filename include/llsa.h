@@ -80,10 +80,11 @@ typedef struct {
   float scale;                /* softmax scale sigma; 0 selects 1/sqrt(d)                             */
   int32_t grid_w;             /* scheduling hint: tokens per row when each slice is a row-major 2-D    */
                               /* token grid (n = rows * grid_w), else 0.  Outputs never depend on it.   */
-                              /* With it, the dK/dV work list takes key-block groups from four          */
-                              /* consecutive grid rows together, which share query blocks; it is used   */
-                              /* when grid_w is a multiple of 4B that divides n, and ignored otherwise. */
-                              /* Negative: LLSA_ERR_SHAPE.                                              */
+                              /* With it, the forward runs fine blocks of four consecutive grid rows    */
+                              /* side by side (their selections overlap), and the dK/dV work list takes */
+                              /* key-block groups of four consecutive rows together (they share query   */
+                              /* blocks); used when grid_w is a multiple of 4B that divides n, and      */
+                              /* ignored otherwise.  Negative: LLSA_ERR_SHAPE.                          */
 } llsa_problem;
 
 /* Operation ids for llsa_workspace_bytes. */
