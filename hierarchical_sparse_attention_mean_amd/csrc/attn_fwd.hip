@@ -17,8 +17,9 @@
 //     pyramid) with a per-entry logit bias that is -inf past the end of the list.
 //   * Online softmax in the log2 domain with fp32 running max / sum; O rounded to bf16 at the end,
 //     natural-log LSE stored for the backward pass.
-//   * Persistent waves: each XCD sweeps a contiguous range of fine blocks with all its resident waves, and
-//     each wave pipelines its blocks' stages back to back (the next block's first stage is in flight while
+//   * Persistent waves: each XCD sweeps a contiguous range of fine blocks with all its resident waves (for a
+//     row-major token grid, in bands of four grid rows, so that a workgroup's waves run blocks one row apart,
+//     whose selections overlap), and each wave pipelines its blocks' stages back to back (the next block's first stage is in flight while
 //     the current block finishes; its Q rows and indices are copied to LDS a whole block ahead).
 //   * The complement reading of the enrichment (launch_attn_fwd_complement) is the same kernel with its
 //     entry table pointing into the complement lists (up to 576 entries per fine block).
