@@ -496,9 +496,9 @@ namespace {
 // the split record (group, first slot, chunks, T_g).  Item order per slice: groups with more than twice the
 // mean length first (each expanded into its chunks), then the rest, each part in list order (stable
 // partitions by block-wide prefix sums), so the longest work starts first.  List order is group order, or
-// with a token grid, groups of four consecutive grid rows at the same column next to each other.  Bounds per slice (n_1 K stages in
-// all), for the smallest S: items <= groups + n_1 / 8, slots <= n_1 / 8, split groups <= n_1 / 16 (each split
-// group has T_g > S and at most 2 T_g / S chunks).
+// with a token grid, groups of four consecutive grid rows at the same column next to each other.  Bounds per
+// slice (n_1 K stages in all), for the smallest S: items <= groups + n_1 / 8, slots <= n_1 / 8, split groups
+// <= n_1 / 16 (each split group has T_g > S and at most 2 T_g / S chunks).
 // grid.x = slices, 1024 threads.
 // ------------------------------------------------------------------------------------------------
 // kT threads (a multiple of 64, at most 1024) build slice `slice`'s list.

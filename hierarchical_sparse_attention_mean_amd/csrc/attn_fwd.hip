@@ -19,8 +19,9 @@
 //     natural-log LSE stored for the backward pass.
 //   * Persistent waves: each XCD sweeps a contiguous range of fine blocks with all its resident waves (for a
 //     row-major token grid, in bands of four grid rows, so that a workgroup's waves run blocks one row apart,
-//     whose selections overlap), and each wave pipelines its blocks' stages back to back (the next block's first stage is in flight while
-//     the current block finishes; its Q rows and indices are copied to LDS a whole block ahead).
+//     whose selections overlap), and each wave pipelines its blocks' stages back to back (the next block's
+//     first stage is in flight while the current block finishes; its Q rows and indices are copied to LDS a
+//     whole block ahead).
 //   * The complement reading of the enrichment (launch_attn_fwd_complement) is the same kernel with its
 //     entry table pointing into the complement lists (up to 576 entries per fine block).
 // fp32 design: same wavefront-per-block mapping on the VALU (lane = query x 16-dim quarter), for the
