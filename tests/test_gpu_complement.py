@@ -196,3 +196,26 @@ def test_complement_backward_fullsize_sampled(L):
         worst = check_close(nm, gs.reshape(1, -1), r_.reshape(1, -1), "bf16")
         msg.append(f"{nm} {worst:.2e}")
     print(f"{w.name} slice {s}: complement " + ", ".join(msg))
+
+
+def test_complement_grid_hint_changes_no_output(L):
+    """The complement reading with and without the grid hint (grid_w): the forward's sweep order and the dK/dV
+    work-list order change, the outputs keep their bits (field inputs on a 64 x 256 grid, two heads)."""
+    H, W = 64, 256
+    w = inputs.custom(1, 2, H * W, 64, "bf16", seed=41, kind="field", grid=(H, W), topk=8, levels=2, backward=True)
+    x = inputs.make_inputs(w, with_dout=True)
+    q, k, v, do = (dev(x[nm]) for nm in ("q", "k", "v", "dout"))
+    outs = []
+    for gw in (0, W):
+        b = L.Buffers(L.problem(1, 2, H * W, topk=8, levels=2, grid_w=gw))
+        assert b.prob.grid_w == gw
+        b.pyramid(q, k, v)
+        L.select(b.prob, b.pq, b.pk, b.idx)
+        wf = torch.empty(max(1, L.workspace_bytes(b.prob, L.OP_ATTN_FWD_COMPLEMENT)), dtype=torch.uint8, device="cuda")
+        wb = torch.empty(max(1, L.workspace_bytes(b.prob, L.OP_ATTN_BWD_COMPLEMENT)), dtype=torch.uint8, device="cuda")
+        L.attn_fwd_complement(b.prob, q, k, v, b.pka, b.pva, b.idx, b.o, b.lse, wf)
+        L.attn_bwd_complement(b.prob, q, k, v, b.o, b.lse, do, b.pka, b.pva, b.idx, b.dq, b.dk, b.dv, wb)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)])
+    for nm, a, c in zip(("idx", "o", "lse", "dq", "dk", "dv"), *outs):
+        assert torch.equal(a, c), nm
