@@ -1021,20 +1021,22 @@ __global__ __launch_bounds__(256, 3) void bwd_dkdv_bf16(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) DkdvLds sm;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Work item: the item list puts each slice's long groups first.  With bh a multiple of 8, XCD x (= block % 8,
-  // round-robin dispatch) owns slices [x bh/8, (x+1) bh/8) and walks their lists position-major, so every XCD
-  // starts on its longest groups and keeps its slices in its L2; otherwise all slices go position-major.
+  // round-robin dispatch) owns slices [x bh/8, (x+1) bh/8) and walks their lists position-major (four positions
+  // of one slice per workgroup), so every XCD starts on its longest groups and keeps its slices in its L2;
+  // otherwise all slices go position-major the same way.
+  // A workgroup's four waves take four consecutive positions of one slice's list (neighbouring groups, which
+  // share query blocks in the CU's L1); consecutive workgroups alternate between the slices.
   int slice, pos;
   if (g.bh % 8 == 0) {
-    const int nsl = g.bh / 8, it = 4 * (blockIdx.x / 8) + w;
-    if (it >= nsl * walk) return;  // no workgroup barrier below
-    slice = (blockIdx.x % 8) * nsl + it % nsl;
-    pos = it / nsl;
+    const int nsl = g.bh / 8, quad = blockIdx.x / 8;
+    slice = (blockIdx.x % 8) * nsl + quad % nsl;
+    pos = 4 * (quad / nsl) + w;
   } else {
-    const int it = 4 * blockIdx.x + w;
-    if (it >= g.bh * walk) return;
-    slice = it % g.bh;
-    pos = it / g.bh;
+    const int quad = blockIdx.x;
+    slice = quad % g.bh;
+    pos = 4 * (quad / g.bh) + w;
   }
+  if (pos >= walk) return;  // no workgroup barrier below
   int4 item = items[(size_t)slice * bd.items + pos];  // pos < walk <= capacity; group -1 past the last item
   item = make_int4(uniform(item.x), uniform(item.y), uniform(item.z), uniform(item.w));
   if (item.x < 0) return;
@@ -1076,7 +1078,8 @@ void launch_dkdv(const Geom& g, const CscGeom& cg, const void* q, const void* k,
                  void* dk, void* dv, const BwdWs& ws, const DkdvPlan& pl, bool lists_ready, hipStream_t stream) {
   const DkdvBounds bd = dkdv_bounds(g);
   const int walk = pl.walk;
-  const int grid = g.bh % 8 == 0 ? 8 * ((g.bh / 8 * walk + 3) / 4) : (g.bh * walk + 3) / 4;
+  const int quads = (walk + 3) / 4;  // workgroups per slice: four list positions each
+  const int grid = g.bh % 8 == 0 ? 8 * (g.bh / 8) * quads : g.bh * quads;
   if (!lists_ready)
     dkdv_order<<<g.bh, 1024, 0, stream>>>(col_ptr, ws.items, ws.splits, ws.split_done, g, cg, bd, pl.S, walk);
   bwd_dkdv_bf16<kComp><<<grid, 256, 0, stream>>>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
