@@ -271,7 +271,11 @@ const char* llsa_status_string(int status);
  * runs beside the forward: one call after the selection (side waits for main) and one before the
  * backward (main waits for side).  Both streams belong to the current device; NULL is the default
  * stream.  The library creates and releases the event inside the call and keeps nothing.  Returns
- * LLSA_OK, or LLSA_ERR_LAUNCH if a HIP event call fails. */
+ * LLSA_OK, or LLSA_ERR_LAUNCH if a HIP event call fails.
+ * Stream capture: the calls of the path (pyramid, select, attn_fwd, index_transpose, attn_bwd) and this
+ * one enqueue only kernels and event waits (no allocation, memset or host synchronisation), so a HIP
+ * stream capture of the two-stream step replays with the results of the eager step.  The kernel timer
+ * below records timing events and must stay disabled while a stream is captured. */
 int llsa_stream_wait(hipStream_t waiter, hipStream_t signaler);
 
 /* ---- kernel timing (for benchmarks) ------------------------------------------------------------ */

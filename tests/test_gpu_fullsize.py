@@ -135,3 +135,48 @@ def test_two_stream_chain_matches_one_stream(L):
     for s, g in got:
         for nm, a, r in zip(("idx", "O", "lse", "dq", "dk", "dv"), g, ref[s]):
             assert torch.equal(a, r), (s, nm)
+
+
+def test_two_stream_chain_replays_as_graph(L):
+    """The two-stream chain captured once as a HIP graph (its fork and join are device-scope event waits, and
+    no call in it issues a memset) replays bit for bit what the eager one-stream chain gives: four replays on
+    alternating inputs copied into the captured input buffers, with an eager step on the other inputs and a
+    synchronisation between replays."""
+    import dataclasses
+    w = inputs.WORKLOADS["fwdbwd_bf16_n65536"]
+    sets = []
+    for seed in (w.seed, w.seed + 1):
+        x = inputs.make_inputs(dataclasses.replace(w, seed=seed), with_dout=True)
+        sets.append([_dev(x[nm]) for nm in ("q", "k", "v", "dout")])
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    outs = lambda: [t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)]
+    ref = []
+    for q, k, v, do in sets:
+        b.forward(q, k, v)
+        b.backward(q, k, v, do)
+        ref.append(outs())
+    static = [t.clone() for t in sets[0]]
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(main):
+        b.forward_backward(*static, main, side)          # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=main):
+        b.forward_backward(*static, main, side)
+    torch.cuda.synchronize()
+    for s in (0, 1, 0, 1):
+        for dst, src in zip(static, sets[s]):
+            dst.copy_(src)
+        for t in (b.o, b.dq, b.dk, b.dv):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for nm, a, r in zip(("idx", "O", "lse", "dq", "dk", "dv"), outs(), ref[s]):
+            assert torch.equal(a, r), (s, nm)
+        with torch.cuda.stream(main):
+            b.forward_backward(*sets[1 - s], main, side)  # eager work between replays
+        torch.cuda.synchronize()
+        for nm, a, r in zip(("idx", "O", "lse", "dq", "dk", "dv"), outs(), ref[1 - s]):
+            assert torch.equal(a, r), (s, "eager", nm)
