@@ -37,9 +37,15 @@ WARM_STEPS = 50                # steps of the per-step (median, min, max) distri
 ATTN = ("attn_fwd", "bwd_dq", "bwd_reduce", "bwd_dkdv")
 
 
-def kernel_symbol(name, dtype):
-    return {"pool": "pool_levels12", "select": "select_level",
-            "attn_fwd": "attn_fwd_bf16" if dtype == "bf16" else "attn_fwd_f32",
+def kernel_symbol(name, w, enrich):
+    """The kernel a family runs on workload w: the bf16 forward pairs fine blocks when n_1 is even, K <= 32 and
+    K * L_e <= 64 (the limits of attn_fwd_pair_bf16), else runs one block per wave."""
+    if w.dtype == "bf16":
+        pair = (w.n // w.block) % 2 == 0 and w.topk <= 32 and w.topk * enrich <= 64
+        fwd = "attn_fwd_pair_bf16" if pair else "attn_fwd_bf16"
+    else:
+        fwd = "attn_fwd_f32"
+    return {"pool": "pool_levels12", "select": "select_level", "attn_fwd": fwd,
             "transpose": "csc_*", "bwd_dq": "bwd_dq_bf16", "bwd_reduce": "reduce_and_order",
             "bwd_dkdv": "bwd_dkdv_bf16"}[name]
 
@@ -204,7 +210,7 @@ def breakdown(w, p, fam, steps):
         kernels[nm] = k
     dom = max(kernels, key=lambda nm: kernels[nm]["ms_per_step"])
     dk = kernels[dom]
-    sym = kernel_symbol(dom, w.dtype)
+    sym = kernel_symbol(dom, w, p.enrich_levels)
     a_gbs = alg[dom]["bytes"] / (dk["avg_launch_ms"] * 1e-3) / 1e9 if dk["launches_per_step"] == 1 else dk["alg_GBps"]
     # HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (calibrated by a plain copy), from the
     # committed summary under profiles/; None when absent or when the kernel's sources changed since

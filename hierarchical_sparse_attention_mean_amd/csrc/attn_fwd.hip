@@ -24,6 +24,12 @@
 //     whole block ahead).
 //   * The complement reading of the enrichment (launch_attn_fwd_complement) is the same kernel with its
 //     entry table pointing into the complement lists (up to 576 entries per fine block).
+// bf16 pair design (attn_fwd_pair_bf16, the selected-token reading when n_1 is even, K <= 32 and K L_e <= 64):
+// one wavefront = two fine blocks, each its own 16-query tile and online softmax, walking the union of the two
+// blocks' entry lists once -- the gathered K and V rows of a stage, their LDS tiles and the transposed V reads
+// serve both tiles, and an entry a block does not attend gets bias -inf in its tile.  With a token grid the two
+// blocks are one grid row apart, where selections overlap most, and the union has about 40 % fewer rows than the
+// two lists.
 // fp32 design: same wavefront-per-block mapping on the VALU (lane = query x 16-dim quarter), for the
 // small fp32 workloads that need 1e-4 agreement.
 #include "common.hpp"
@@ -299,6 +305,404 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
   }
 }
 
+// Two fine blocks per wavefront.  With a token grid the pair is vertical -- blocks i and i + (blocks per grid row),
+// whose selections overlap most (two fine blocks one grid row apart keep about 6.6 of 8 key blocks in common on
+// 2-D fields) -- else blocks 2p and 2p + 1.  The wave walks the union of the two blocks' entry lists once: every
+// stage's 32 K and V rows go through the LDS tiles once and serve both 16-query tiles, each with its own online
+// softmax; an entry the tile's block does not attend carries logit bias -inf there (probability exactly 0), so
+// each tile computes the same sums as its block alone, in another order.
+//   * Raw stages (two key blocks each): the blocks both keep, two per stage, then one block only A keeps beside one
+//     only B keeps (there are as many of each), then the odd shared block beside a padding slot.  The first stage
+//     thus holds entries of both blocks, so both running maxima start finite.
+//   * Enrichment stages: per level l >= 2 the K tokens of A's ancestor unit, and B's that A's unit does not keep
+//     (nothing more when the two share the unit); then the level-1 tokens of the union of the picks; 32 per stage,
+//     bias 4l where the tile's block attends the entry, -inf elsewhere and past the end.
+// The union of pair j + 1 is built from its selection rows and entry indices (copied to LDS a pair ahead) just
+// before its first stage is issued, into the second of two union slots, while pair j's last stage is consumed.
+constexpr int kPairCoarse = 64;  // enrichment entries per block (K * L_e) the pair kernel takes
+// A union entry: row (key block, or pyramid row) in bits 0..23, level in bits 24..29, and in bits 30 and 31 the
+// tiles (A: 1, B: 2) whose block attends it.
+__device__ __forceinline__ int tagged(int row, int level, int tiles) {
+  return (int)((uint32_t)row | ((uint32_t)level << 24) | ((uint32_t)tiles << 30));
+}
+
+template <int kMaxPC>
+__global__ __launch_bounds__(256, 2) void attn_fwd_pair_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                          const bf16_t* __restrict__ v, const bf16_t* __restrict__ pk,
+                                                          const bf16_t* __restrict__ pv, const int32_t* __restrict__ idx,
+                                                          bf16_t* __restrict__ o, float* __restrict__ lse, Geom g) {
+  __shared__ __attribute__((aligned(16))) bf16_t vs[4][32 * kLd];      // V tile (read transposed)
+  __shared__ __attribute__((aligned(16))) bf16_t ks[4][32 * kLd];      // K tile (read as MFMA A operand)
+  __shared__ __attribute__((aligned(16))) bf16_t qs[4][32 * kD];       // Q rows of the next pair: A 0..15, B 16..31
+  __shared__ __attribute__((aligned(16))) int is1[4][64];              // next pair's selection rows: A at 0, B at 32
+  __shared__ __attribute__((aligned(16))) int es[4][2][kMaxPC];        // next pair's enrichment block indices (A, B)
+  __shared__ __attribute__((aligned(16))) int ub[4][2][64];            // union slots: key block | tiles << 30
+  __shared__ __attribute__((aligned(16))) int ue[4][2][2 * kMaxPC];    // union entries: row | level << 24 | tiles << 30
+  __shared__ __attribute__((aligned(16))) EntryTabT<kMaxPC> tab;       // per-entry constants (shared)
+  const int lane = threadIdx.x & 63, c = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  fill_entry_tab(g, tab);
+  // Sweep: XCD x (= block % 8, round-robin dispatch) owns the contiguous position range [plo, phi) of all slices'
+  // pairs, and its per_xcd waves take it round by round: in round j, wave r runs position
+  // plo + j per_xcd + (r + 148 j) mod per_xcd.  Each round covers one window of neighbouring pairs (kept in the
+  // XCD's L2), a workgroup's four waves take four consecutive positions (their pairs share key rows in L1), and
+  // the rotation by a multiple of four moves each wave to another column of the window every round: the pairs'
+  // stage counts differ with the image (the unions differ), and a wave always on the same column would collect
+  // one strip's.
+  const int npairs = g.rows[1] / 2;
+  const int per_xcd = 4 * (gridDim.x / 8), wr = 4 * (blockIdx.x / 8) + w, xcd = blockIdx.x % 8;
+  const int plo = (int)((int64_t)xcd * g.bh * npairs / 8), phi = (int)((int64_t)(xcd + 1) * g.bh * npairs / 8);
+  auto sweep_pos = [&](int j) { return plo + j * per_xcd + (wr + 148 * j) % per_xcd; };
+  const int jfull = (phi - plo) / per_xcd;
+  const int count = uniform(jfull + (sweep_pos(jfull) < phi ? 1 : 0));
+  if (count == 0) return;  // no workgroup barrier is used below
+  bf16_t* vt = vs[w];
+  bf16_t* kt = ks[w];
+  const int K = g.K, ncA = g.K * g.Le;
+  const size_t slice_elems = (size_t)g.n * kD, slice_rows = (size_t)g.R * kD;
+  const float sl2 = g.scale_log2;
+
+  // Pair of sweep position ip within a slice.  Vertical pairs need an even number of grid rows; pair rows are then
+  // taken in bands of four, column by column, so that a workgroup's four waves run pairs one pair row apart.
+  const int R = 4 * g.gpr;
+  const bool vert = g.gpr > 0 && (g.rows[1] / R) % 2 == 0;
+  const int dB = vert ? R : 1;
+  const int pband = 4 * R, pbanded = vert ? npairs / pband * pband : 0;
+  auto pair_a = [&](int ip) {
+    if (!vert) return 2 * ip;
+    int prow, col;
+    if (ip < pbanded) {
+      const int b0 = ip / pband * pband, within = ip - b0;
+      prow = b0 / R + (within & 3);
+      col = within >> 2;
+    } else {
+      prow = ip / R;
+      col = ip - prow * R;
+    }
+    return 2 * prow * R + col;
+  };
+  // slice and first block of the wave's j-th pair (clamped to the last), from a table of 64 pairs at a time held in
+  // lanes (pair pchunk + lane): the divisions run once per 64 pairs, in parallel
+  int pchunk = -64, lslice = 0, lia = 0;
+  auto pair_of = [&](int j, int* slice, int* ia) {
+    j = min(j, count - 1);
+    if (j < pchunk || j >= pchunk + 64) {
+      pchunk = j & ~63;
+      const int pos = sweep_pos(min(pchunk + lane, count - 1));
+      lslice = pos / npairs;
+      lia = pair_a(pos - lslice * npairs);
+    }
+    *slice = __builtin_amdgcn_readlane(lslice, j - pchunk);
+    *ia = __builtin_amdgcn_readlane(lia, j - pchunk);
+  };
+  // copy the inputs of the wave's j-th pair (clamped to the last) into the single set of next-pair buffers
+  auto prefetch = [&](int j) {
+    int slice, ia;
+    pair_of(j, &slice, &ia);
+    const int ib = ia + dB;
+    const bf16_t* qa = q + slice * slice_elems + (size_t)16 * ia * kD;  // 2 KB each, contiguous
+    const bf16_t* qb = q + slice * slice_elems + (size_t)16 * ib * kD;
+    lds_dma16_nt(qa + 8 * lane, &qs[w][0]);
+    lds_dma16_nt(qa + 512 + 8 * lane, &qs[w][512]);
+    lds_dma16_nt(qb + 8 * lane, &qs[w][1024]);
+    lds_dma16_nt(qb + 512 + 8 * lane, &qs[w][1536]);
+    const int32_t* I = idx + (size_t)slice * g.R * g.K;
+    if ((lane & 31) < K) lds_dma4(I + (size_t)(g.off[1] + (lane < 32 ? ia : ib)) * K + (lane & 31), &is1[w][0]);
+    if (ncA > 0) {
+      const int e = min(lane, ncA - 1);
+      lds_dma4(I + tab.pos0[e] + (ia >> tab.shift[e]) * tab.stride[e], &es[w][0][0]);
+      lds_dma4(I + tab.pos0[e] + (ib >> tab.shift[e]) * tab.stride[e], &es[w][1][0]);
+    }
+  };
+
+  // Union of the pair whose inputs sit in the next-pair buffers, into union slot u; returns its raw stages and
+  // enrichment entries.  Lane s < K holds A's value s, lane 32 + s B's value s.
+  // Membership compares all K x K pairs at once: with Kp = K rounded up to a power of two, pair (i, j) is bit
+  // i Kp + j of a wave ballot (one ballot per 64 pairs); A's value i is in B's list if row i has a bit set, B's value
+  // j in A's list if column j has.
+  const int lgK = K <= 1 ? 0 : 32 - __builtin_clz(K - 1), Kp = 1 << lgK;
+  const int rounds = max(1, (Kp * Kp) >> 6);
+  uint64_t colpat = 0;  // bit j of every row
+  for (int t = 0; t < 64; t += Kp) colpat |= 1ull << t;
+  const uint64_t rowpat = Kp >= 64 ? ~0ull : (1ull << Kp) - 1;
+  auto member = [&](int val, bool act) {  // whether the other block's list holds val
+    bool hit = false;
+    const int rowbit = (lane & 31) * Kp;  // first bit of row i = lane (A's lanes)
+    for (int r = 0; r < rounds; ++r) {
+      const int pp = 64 * r + lane, i = pp >> lgK, j = pp & (Kp - 1);
+      const int a = __shfl(val, min(i, 31), 64), b = __shfl(val, 32 + min(j, 31), 64);
+      const uint64_t m = __ballot(i < K && j < K && a == b);
+      if (lane < 32)
+        hit |= (rowbit >> 6) == r && ((m >> (rowbit & 63)) & rowpat) != 0;
+      else
+        hit |= (m & (colpat << (lane & 31))) != 0;
+    }
+    return act && hit;
+  };
+  auto below = [&](uint64_t m) {  // set bits of m below this lane
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
+  auto build_union = [&](int u, int ia, int ib, int* nraw, int* nc) {
+    const bool act = (lane & 31) < K, sideA = lane < 32;
+    // raw key blocks
+    const int val = act ? is1[w][lane] : -1;
+    const bool hit = member(val, act);
+    const uint64_t msh = __ballot(act && sideA && hit), mao = __ballot(act && sideA && !hit);
+    const uint64_t mbo = __ballot(act && !sideA && !hit);
+    const int ns = __popcll(msh), no = K - ns, hs = ns >> 1, odd = ns & 1;
+    if (act && sideA && hit) {
+      const int r = below(msh);
+      const int slot = r < 2 * hs ? r : 2 * hs + 2 * no;
+      ub[w][u][slot] = tagged(val, 0, 3);
+      if (r >= 2 * hs) ub[w][u][slot + 1] = val;  // padding slot: attended by neither tile
+    } else if (act && sideA) {
+      ub[w][u][2 * hs + 2 * below(mao)] = tagged(val, 0, 1);
+    } else if (act) {
+      ub[w][u][2 * hs + 2 * below(mbo) + 1] = tagged(val, 0, 2);
+    }
+    *nraw = hs + no + odd;
+    // enrichment entries: levels 2..L_e, then level 1 (the raw union's tokens)
+    int base = 0;
+    for (int l = 2; l <= g.Le; ++l) {
+      const int off = level_off(g, l), sh = 4 * (l - 1);
+      const int ev = act ? es[w][sideA ? 0 : 1][(l - 2) * K + (lane & 31)] : -1;
+      if ((ia >> sh) == (ib >> sh)) {  // one ancestor unit: the same K tokens
+        if (act && sideA) ue[w][u][base + lane] = tagged(off + ev, l, 3);
+        base += K;
+      } else {
+        const bool eh = member(ev, act);
+        const uint64_t meo = __ballot(act && !sideA && !eh);
+        if (act && sideA) ue[w][u][base + lane] = tagged(off + ev, l, eh ? 3 : 1);
+        else if (act && !eh) ue[w][u][base + K + below(meo)] = tagged(off + ev, l, 2);
+        base += K + __popcll(meo);
+      }
+    }
+    if (g.Le >= 1) {
+      const int off = level_off(g, 1);
+      if (act && sideA) ue[w][u][base + lane] = tagged(off + val, 1, hit ? 3 : 1);
+      else if (act && !hit) ue[w][u][base + K + below(mbo)] = tagged(off + val, 1, 2);
+      base += K + no;
+    }
+    *nc = base;
+  };
+
+  // stage s of the pair in union slot u (slice `slice`), coalesced: instruction m reads rows 8m .. 8m+7 of the
+  // stage's 32 keys (lane l: row 8m + l/8, bytes 16 (l%8)) -- K into r[m], V into r[4+m]
+  auto issue = [&](int u, int slice, int nraw, int nc, int s, Stage& st) {
+    const char* kb;
+    const char* vb;
+    uint32_t off[4];
+    const uint32_t sub = (uint32_t)lane >> 3, col = 16u * (lane & 7);
+    if (s < nraw) {
+      const int b0 = __builtin_amdgcn_readfirstlane(ub[w][u][2 * s]) & 0x3fffffff;
+      const int b1 = __builtin_amdgcn_readfirstlane(ub[w][u][2 * s + 1]) & 0x3fffffff;
+      kb = reinterpret_cast<const char*>(k + slice * slice_elems);
+      vb = reinterpret_cast<const char*>(v + slice * slice_elems);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) off[m] = (16u * (m < 2 ? b0 : b1) + 8u * (m & 1) + sub) * (2 * kD) + col;
+    } else {
+      const int e0 = 32 * (s - nraw) + (int)sub;
+      kb = reinterpret_cast<const char*>(pk + slice * slice_rows);
+      vb = reinterpret_cast<const char*>(pv + slice * slice_rows);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) off[m] = (uint32_t)(ue[w][u][min(e0 + 8 * m, nc - 1)] & 0xffffff) * (2 * kD) + col;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.r[m] = ld16(kb + off[m]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.r[4 + m] = ld16(vb + off[m]);
+  };
+
+  int par = 0;            // union slot of the pair being consumed
+  int cj = 0, cs = 0;     // pair / stage being consumed
+  int ij = 0, is = 0;     // pair / stage last issued
+  int cslice, cia, nslice, nia;
+  pair_of(0, &cslice, &cia);
+  pair_of(1, &nslice, &nia);
+  int craw, cnc, nraw_n = 0, nnc = 0;
+  uint4 q0, q1, q2, q3;
+  // Q operands of the pair whose rows sit in the Q slot; the slot is refilled right after, so the reads must have
+  // completed before the next DMA is issued
+  auto read_q = [&]() {
+    const bf16_t* qr = &qs[w][c * kD + 8 * gq];
+    q0 = *reinterpret_cast<const uint4*>(qr);
+    q1 = *reinterpret_cast<const uint4*>(qr + 32);
+    q2 = *reinterpret_cast<const uint4*>(qr + 16 * kD);
+    q3 = *reinterpret_cast<const uint4*>(qr + 16 * kD + 32);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  prefetch(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_q();
+  build_union(0, cia, cia + dB, &craw, &cnc);
+  wait_lds();  // the union is read (and the next-pair buffers refilled) next
+  prefetch(1);
+  int cnst = craw + (cnc + 31) / 32, nnst = 0;
+
+  Softmax sa, sb;
+  sa.init();
+  sb.init();
+
+  auto issue_next = [&](Stage& st) {
+    if (++is == (ij == cj ? cnst : nnst)) {
+      is = 0;
+      ++ij;
+      if (ij < count) {
+        // first stage of the next pair (the current one is in its last stage): its inputs were copied at the
+        // start of the current pair, and every stage issued since (cnst - 1 of them) is newer
+        if (cnst >= 2)
+          __builtin_amdgcn_s_waitcnt(0xf78);  // vmcnt(8), as a builtin so that the compiler's own waits see it
+        else
+          __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt(0)
+        build_union(par ^ 1, nia, nia + dB, &nraw_n, &nnc);
+        nnst = nraw_n + (nnc + 31) / 32;
+      }
+    }
+    // past the end: an in-bounds reload (the current pair's first stage) that is never consumed
+    const bool cur = ij >= count || ij == cj;
+    issue(cur ? par : par ^ 1, cur ? cslice : nslice, cur ? craw : nraw_n, cur ? cnc : nnc,
+          ij >= count ? 0 : is, st);
+  };
+
+  auto store_o = [&](const Softmax& sm, bf16_t* tile, int i) {
+    const float lt = group_sum(sm.l);
+    const float inv = 1.0f / lt;
+    // O^T[d][query c] -> bf16 rows of the tile (query c, dims 16t + 4g .. +3), then coalesced 16-byte stores of
+    // whole rows (lane l: query l/8 and 8 + l/8, bytes 16 (l%8))
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint2 x;
+      x.x = pack_bf16x2(sm.acc[t][0] * inv, sm.acc[t][1] * inv);
+      x.y = pack_bf16x2(sm.acc[t][2] * inv, sm.acc[t][3] * inv);
+      *reinterpret_cast<uint2*>(tile + c * kLd + 16 * t + 4 * gq) = x;
+    }
+    bf16_t* ob = o + cslice * slice_elems + (size_t)16 * i * kD;
+    const int ro = (lane >> 3) * kLd + 8 * (lane & 7), go = (lane >> 3) * kD + 8 * (lane & 7);
+    const uint4 o0 = *reinterpret_cast<const uint4*>(tile + ro);
+    const uint4 o1 = *reinterpret_cast<const uint4*>(tile + ro + 8 * kLd);
+    st16_nt(ob + go, o0);
+    st16_nt(ob + go + 8 * kD, o1);
+    if (gq == 0) lse[(size_t)cslice * g.n + 16 * i + c] = (sm.m + log2f(lt)) * kLn2;
+  };
+
+  // One stage: the 32 key rows go to the K and V tiles; S^T = K Q^T for both tiles; each tile's logits take its
+  // own bias; P^T of both tiles against the one transposed V read.  Returns true once the last pair is done; a
+  // stage past the end (an in-bounds reload) only goes to the tiles.
+  auto consume = [&](const Stage& st) {
+    {
+      const int o = (lane >> 3) * kLd + 8 * (lane & 7);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        *reinterpret_cast<uint4*>(kt + o + 8 * m * kLd) = st.r[m];
+        *reinterpret_cast<uint4*>(vt + o + 8 * m * kLd) = st.r[4 + m];
+      }
+    }
+    if (cj >= count) return true;
+    float ba[8], bb[8];
+    if (cs < craw) {
+      const uint32_t t0 = (uint32_t)ub[w][par][2 * cs] >> 30, t1 = (uint32_t)ub[w][par][2 * cs + 1] >> 30;
+      const float a0 = (t0 & 1) ? 0.f : -INFINITY, a1 = (t1 & 1) ? 0.f : -INFINITY;
+      const float b0 = (t0 & 2) ? 0.f : -INFINITY, b1 = (t1 & 2) ? 0.f : -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ba[r] = a0; ba[4 + r] = a1;
+        bb[r] = b0; bb[4 + r] = b1;
+      }
+    } else {
+      const int e0 = 32 * (cs - craw) + 4 * gq;
+      const int4 w0 = *reinterpret_cast<const int4*>(&ue[w][par][e0]);
+      const int4 w1 = *reinterpret_cast<const int4*>(&ue[w][par][e0 + 16]);
+      const int wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int e = e0 + (r & 3) + 16 * (r >> 2);
+        const uint32_t x = (uint32_t)wv[r];
+        const float bias = 4.0f * (float)((x >> 24) & 63);
+        ba[r] = e < cnc && (x >> 30) & 1 ? bias : -INFINITY;
+        bb[r] = e < cnc && (x >> 30) & 2 ? bias : -INFINITY;
+      }
+    }
+    // A operands: key row c and 16 + c, dims 8g..8g+7 and 32+8g..32+8g+7
+    const bf16_t* kr = kt + c * kLd + 8 * gq;
+    const bf16x8 k00 = *reinterpret_cast<const bf16x8*>(kr), k01 = *reinterpret_cast<const bf16x8*>(kr + 32);
+    const bf16x8 k10 = *reinterpret_cast<const bf16x8*>(kr + 16 * kLd);
+    const bf16x8 k11 = *reinterpret_cast<const bf16x8*>(kr + 16 * kLd + 32);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = mfma_bf16_k32(k00, as_bf16x8(q0), s0);
+    s0 = mfma_bf16_k32(k01, as_bf16x8(q1), s0);
+    s1 = mfma_bf16_k32(k10, as_bf16x8(q0), s1);
+    s1 = mfma_bf16_k32(k11, as_bf16x8(q1), s1);
+    u0 = mfma_bf16_k32(k00, as_bf16x8(q2), u0);
+    u0 = mfma_bf16_k32(k01, as_bf16x8(q3), u0);
+    u1 = mfma_bf16_k32(k10, as_bf16x8(q2), u1);
+    u1 = mfma_bf16_k32(k11, as_bf16x8(q3), u1);
+    float xa[8], xb[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      xa[r] = fmaf(s0[r], sl2, ba[r]);
+      xa[4 + r] = fmaf(s1[r], sl2, ba[4 + r]);
+      xb[r] = fmaf(u0[r], sl2, bb[r]);
+      xb[4 + r] = fmaf(u1[r], sl2, bb[4 + r]);
+    }
+    float pa[8], pb[8];
+    sa.update<8>(xa, pa);
+    sb.update<8>(xb, pb);
+    uint4 wa, wb2;
+    wa.x = pack_bf16x2(pa[0], pa[1]);
+    wa.y = pack_bf16x2(pa[2], pa[3]);
+    wa.z = pack_bf16x2(pa[4], pa[5]);
+    wa.w = pack_bf16x2(pa[6], pa[7]);
+    wb2.x = pack_bf16x2(pb[0], pb[1]);
+    wb2.y = pack_bf16x2(pb[2], pb[3]);
+    wb2.z = pack_bf16x2(pb[4], pb[5]);
+    wb2.w = pack_bf16x2(pb[6], pb[7]);
+    const bf16x8 pva = as_bf16x8(wa), pvb = as_bf16x8(wb2);
+    const bf16_t* r0 = vt + (4 * gq + (c >> 2)) * kLd + 4 * (c & 3);
+    const bf16_t* r1 = r0 + 16 * kLd;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 va = cat4(lds_read_tr16(r0 + 16 * t), lds_read_tr16(r1 + 16 * t));
+      sa.acc[t] = mfma_bf16_k32(va, pva, sa.acc[t]);
+      sb.acc[t] = mfma_bf16_k32(va, pvb, sb.acc[t]);
+    }
+    if (++cs == cnst) {
+      store_o(sa, kt, cia);
+      store_o(sb, vt, cia + dB);
+      cs = 0;
+      if (++cj >= count) return true;
+      par ^= 1;
+      cslice = nslice;
+      cia = nia;
+      craw = nraw_n;
+      cnc = nnc;
+      cnst = nnst;
+      pair_of(cj + 1, &nslice, &nia);
+      read_q();
+      prefetch(cj + 1);
+      sa = Softmax();
+      sa.init();
+      sb = Softmax();
+      sb.init();
+    }
+    return false;
+  };
+
+  // Every trip runs both halves and the loop exits only at its end, so that each path into the loop header has the
+  // same loads in flight (A's); a consume after the last pair only drains its stage (see consume).  An exit from
+  // the middle would reach the header in the compiler's control flow with B's loads in flight, and its waits would
+  // then treat B's registers as loading on every trip.
+  Stage A, B;
+  issue(par, cslice, craw, cnc, 0, A);
+  for (;;) {
+    issue_next(B);
+    const bool d1 = consume(A);
+    issue_next(A);
+    const bool d2 = consume(B);
+    if (d1 || d2) break;
+  }
+}
+
 // fp32 path: wave per fine block, lane = (query c, dims 16g .. 16g+15), entries one at a time on the VALU.
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q, const float* __restrict__ k,
                                                     const float* __restrict__ v, const float* __restrict__ pk,
@@ -381,6 +785,14 @@ hipError_t launch_attn_fwd(const Geom& g, int dtype_bf16, const void* q, const v
   const int grid = (nb + 3) / 4;
   LaunchTimer timer(kAttnFwd, stream);
   if (dtype_bf16) {
+    if (g.rows[1] % 2 == 0 && g.K <= 32 && g.K * g.Le <= kPairCoarse) {
+      // two fine blocks per wave; two workgroups per CU (their LDS), which leaves room for the index transpose
+      auto kernel = attn_fwd_pair_bf16<kPairCoarse>;
+      kernel<<<max(8, persistent_grid((const void*)kernel, 256, (nb / 2 + 3) / 4) / 8 * 8), 256, 0, stream>>>(
+          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)pk, (const bf16_t*)pv, idx,
+          (bf16_t*)o, lse, g);
+      return hipGetLastError();
+    }
     // two thirds of the resident workgroups: as fast as a full load (the gathers are bound by the CU's vector
     // memory path, not by the number of waves), and it leaves room for a kernel on another stream -- the index
     // transpose, which needs only the selection, can run beside the forward

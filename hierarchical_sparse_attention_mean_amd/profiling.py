@@ -31,6 +31,7 @@ CSRC = os.path.join(HERE, "csrc")
 _COMMON = ["common.hpp", "entries.hpp", "persist.hpp", "launch.hpp"]
 KERNEL_SOURCES = {
     "attn_fwd_bf16": ["attn_fwd.hip"] + _COMMON,
+    "attn_fwd_pair_bf16": ["attn_fwd.hip"] + _COMMON,
     "bwd_dq_bf16": ["attn_bwd.hip"] + _COMMON,
     "bwd_dkdv_bf16": ["attn_bwd.hip"] + _COMMON,
     "reduce_and_order": ["attn_bwd.hip"] + _COMMON,

@@ -79,12 +79,15 @@ typedef struct {
   int32_t dtype;              /* llsa_dtype of the raw tensors                                        */
   float scale;                /* softmax scale sigma; 0 selects 1/sqrt(d)                             */
   int32_t grid_w;             /* scheduling hint: tokens per row when each slice is a row-major 2-D    */
-                              /* token grid (n = rows * grid_w), else 0.  Outputs never depend on it.   */
-                              /* With it, the forward runs fine blocks of four consecutive grid rows    */
-                              /* side by side (their selections overlap), and the dK/dV work list takes */
-                              /* key-block groups of four consecutive rows together (they share query   */
-                              /* blocks); used when grid_w is a multiple of 4B that divides n, and      */
-                              /* ignored otherwise.  Negative: LLSA_ERR_SHAPE.                          */
+                              /* token grid (n = rows * grid_w), else 0; used when grid_w is a multiple */
+                              /* of 4B that divides n, ignored otherwise; negative: LLSA_ERR_SHAPE.     */
+                              /* With it, the bf16 forward pairs each fine block with the one a grid    */
+                              /* row below (their selections overlap) where it pairs neighbours         */
+                              /* without, and the dK/dV work list takes key-block groups of four        */
+                              /* consecutive grid rows together (they share query blocks).  The         */
+                              /* selection never depends on it, and neither does the backward given the */
+                              /* same forward outputs; the bf16 forward's O and LSE differ only by the   */
+                              /* order of its floating-point sums (within the bf16 tolerance).          */
 } llsa_problem;
 
 /* Operation ids for llsa_workspace_bytes. */

@@ -37,7 +37,8 @@ def _dev(t):
 def _run_sampled(L, w, samples):
     x = inputs.make_inputs(w, with_dout=True)
     q, k, v, do = (_dev(x[nm]) for nm in ("q", "k", "v", "dout"))
-    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    # in the launch configuration bench.py times: the token grid as the scheduling hint
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels, grid_w=w.grid[1]))
     b.forward(q, k, v)
     b.backward(q, k, v, do)
     torch.cuda.synchronize()
@@ -84,7 +85,7 @@ def test_fullsize_fwd_n16384_8_heads(L):
     w = inputs.WORKLOADS["fwd_bf16_n16384"]
     x = inputs.make_inputs(w)
     q, k, v = (_dev(x[nm]) for nm in ("q", "k", "v"))
-    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels), backward=False)
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels, grid_w=w.grid[1]), backward=False)
     b.forward(q, k, v)
     torch.cuda.synchronize()
     assert torch.isfinite(b.o.float()).all()
@@ -117,7 +118,7 @@ def test_two_stream_chain_matches_one_stream(L):
     for seed in (w.seed, w.seed + 1):
         x = inputs.make_inputs(dataclasses.replace(w, seed=seed), with_dout=True)
         sets.append([_dev(x[nm]) for nm in ("q", "k", "v", "dout")])
-    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels, grid_w=w.grid[1]))
     outs = lambda: [t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)]
     ref = []
     for q, k, v, do in sets:
@@ -148,7 +149,7 @@ def test_two_stream_chain_replays_as_graph(L):
     for seed in (w.seed, w.seed + 1):
         x = inputs.make_inputs(dataclasses.replace(w, seed=seed), with_dout=True)
         sets.append([_dev(x[nm]) for nm in ("q", "k", "v", "dout")])
-    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels))
+    b = L.Buffers(L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, w.levels, grid_w=w.grid[1]))
     outs = lambda: [t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)]
     ref = []
     for q, k, v, do in sets:

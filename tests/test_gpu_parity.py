@@ -66,8 +66,12 @@ def _prepare(name, w, levels, Le):
     return _cache[name]
 
 
-def _prob(L, w, levels, Le):
-    return L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, levels, Le, L.BF16 if w.dtype == "bf16" else L.F32)
+def _prob(L, w, levels, Le, grid_w=None):
+    """The problem of a case, with the workload's token grid as the scheduling hint when it has one (as bench.py
+    runs it: on 2-D fields the bf16 forward then pairs fine blocks one grid row apart)."""
+    gw = w.grid[1] if grid_w is None else grid_w
+    return L.problem(w.batch, w.heads, w.n, w.d, w.block, w.topk, levels, Le, L.BF16 if w.dtype == "bf16" else L.F32,
+                     grid_w=gw)
 
 
 @pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
@@ -119,6 +123,32 @@ def test_forward_with_oracle_selection(L, name, w, levels, Le):
     lse_err = np.abs(host(b.lse) - ref["lse"]).max()
     assert lse_err <= (1e-4 if w.dtype == "f32" else 2e-2), lse_err
     print(f"{name}: O worst {worst:.2e}, lse max err {lse_err:.2e}")
+
+
+# A row length for a synthetic grid hint: 64 tokens (four key blocks per grid row) when it tiles n into an even number
+# of rows, so that the bf16 forward pairs every fine block with the one four blocks later (vertical pairs).
+def _vertical_hint(n):
+    return 64 if n % 64 == 0 and (n // 64) % 2 == 0 else 0
+
+
+@pytest.mark.parametrize("name,w,levels,Le", [c for c in CASES if c[1].dtype == "bf16" and _vertical_hint(c[1].n)],
+                         ids=[c[0] for c in CASES if c[1].dtype == "bf16" and _vertical_hint(c[1].n)])
+def test_forward_vertical_pairs_with_oracle_selection(L, name, w, levels, Le):
+    """The bf16 forward with fine blocks paired four blocks apart (a grid hint of 64 tokens per row, whatever the
+    inputs' own layout): each wave walks the union of two blocks' entry lists, so every case of the table -- odd K,
+    L_e = 0 and 1, K = 16 and 32, L = 4, hub selections -- runs with shared, one-sided and padding slots."""
+    x, ex, ref = _prepare(name, w, levels, Le)
+    b = L.Buffers(_prob(L, w, levels, Le, grid_w=_vertical_hint(w.n)), backward=False)
+    assert L.resolve(b.prob).grid_w == _vertical_hint(w.n)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    b.pyramid(q, k, v)
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    L.attn_fwd(b.prob, q, k, v, b.pka, b.pva, idx, b.o, b.lse)
+    torch.cuda.synchronize()
+    worst = check_close("O", flat(host(b.o)), ref["o"], w.dtype)
+    lse_err = np.abs(host(b.lse) - ref["lse"]).max()
+    assert lse_err <= 2e-2, lse_err
+    print(f"{name} (vertical pairs): O worst {worst:.2e}, lse max err {lse_err:.2e}")
 
 
 def _backward_cases():
@@ -241,25 +271,45 @@ def test_split_groups_deterministic(L):
 
 @pytest.mark.parametrize("kind,grid,levels", [("hub", (32, 128), 2), ("field", (18, 256), 2), ("field", (256, 256), 3)],
                          ids=["hub_n4096_split_groups", "field_n4608_partial_band", "field_n65536"])
-def test_grid_hint_changes_no_output(L, kind, grid, levels):
-    """grid_w only reorders the dK/dV work list (groups of four consecutive grid rows next to each other): the
-    GPU chain gives the same bits with and without it -- on hub inputs whose long groups run as chunks, with a
-    last band of only two grid rows, and on a three-level field."""
+def test_grid_hint_keeps_selection_and_backward_bits(L, kind, grid, levels):
+    """grid_w changes no selection, and the backward from the same forward outputs gives the same bits with and
+    without it (it only reorders the dK/dV work list: groups of four consecutive grid rows next to each other) --
+    on hub inputs whose long groups run as chunks, with a last band of only two grid rows, and on a three-level
+    field.  The forward pairs fine blocks one grid row apart with the hint and side by side without it: the same
+    sums in another order, so O and LSE agree to the bf16 tolerance and each meets the oracle (n <= 4608 here)."""
     H, W = grid
     n = H * W
     w = inputs.custom(1, 2, n, 64, "bf16", seed=37, kind=kind, grid=grid, topk=8, levels=levels, backward=True)
     x = inputs.make_inputs(w, with_dout=True)
     q, k, v, do = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dout"])
-    outs = []
+    bufs = []
     for gw in (0, W):
         p = L.problem(1, 2, n, topk=8, levels=levels, grid_w=gw)
         assert L.resolve(p).grid_w == gw
         b = L.Buffers(p)
         b.forward(q, k, v)
+        torch.cuda.synchronize()
+        bufs.append(b)
+    b0, b1 = bufs
+    assert torch.equal(b0.idx, b1.idx)
+    check_close("O", host(b1.o).reshape(2, -1), host(b0.o).reshape(2, -1), "bf16")
+    assert np.abs(host(b1.lse) - host(b0.lse)).max() <= 2e-2
+    if n <= 4608:
+        ex = {nm: flat(x[nm].exact) for nm in ("q", "k", "v")}
+        ref = oracle.run(ex["q"], ex["k"], ex["v"], 16, 8, levels=levels)
+        if np.array_equal(host(b0.idx).astype(np.int64), ref["idx"].astype(np.int64)):
+            for b in bufs:
+                check_close("O", flat(host(b.o)), ref["o"], "bf16")
+                assert np.abs(host(b.lse) - ref["lse"]).max() <= 2e-2
+    # the backward from the same O and LSE
+    b1.o.copy_(b0.o)
+    b1.lse.copy_(b0.lse)
+    outs = []
+    for b in bufs:
         b.backward(q, k, v, do)
         torch.cuda.synchronize()
-        outs.append([t.clone() for t in (b.idx, b.o, b.lse, b.dq, b.dk, b.dv)])
-    for nm, a, c in zip(("idx", "o", "lse", "dq", "dk", "dv"), *outs):
+        outs.append([t.clone() for t in (b.dq, b.dk, b.dv)])
+    for nm, a, c in zip(("dq", "dk", "dv"), *outs):
         assert torch.equal(a, c), nm
 
 
