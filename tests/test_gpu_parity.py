@@ -45,6 +45,10 @@ CASES = [
     ("bf16_n8192_L1_nL512", inputs.custom(1, 1, 8192, 64, "bf16", seed=23, topk=8, levels=1, backward=True), 1, -1),
     ("bf16_n65536_L2_K32", inputs.custom(1, 1, 65536, 64, "bf16", seed=24, topk=32, levels=2, backward=True), 2, -1),
     ("bf16_n1048576_L4", inputs.custom(1, 1, 1 << 20, 64, "bf16", seed=25, topk=8, levels=4, backward=True), 4, -1),
+    # the bf16 forward's pair kernel at its edges: K = 2 with no enrichment gives pairs whose union is a single stage;
+    # K * L_e = 66 > 64 runs the one-block-per-wave forward (forward only: K (L_e - 1) > 32 is past the backward)
+    ("bf16_n4096_K2_Le0", inputs.custom(1, 2, 4096, 64, "bf16", seed=26, topk=2, levels=2, backward=True), 2, 0),
+    ("bf16_n98304_K22_L3_fwd", inputs.custom(1, 1, 98304, 64, "bf16", seed=27, topk=22, levels=3), 3, -1),
     # hub inputs: a few key blocks kept by every query block, so the dK/dV kernel splits their groups
     ("bf16_hub_n4096_split", inputs.custom(1, 2, 4096, 64, "bf16", seed=21, kind="hub", topk=8, levels=2,
                                            backward=True), 2, -1),
