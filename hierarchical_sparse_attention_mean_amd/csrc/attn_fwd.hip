@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_bf16(const bf16_t* __restrict
 }
 
 // Two fine blocks per wavefront.  With a token grid the pair is vertical -- blocks i and i + (blocks per grid row),
-// whose selections overlap most (two fine blocks one grid row apart keep about 6.6 of 8 key blocks in common on
+// whose selections overlap most (two fine blocks one grid row apart keep about 6.8 of 8 key blocks in common on
 // 2-D fields) -- else blocks 2p and 2p + 1.  The wave walks the union of the two blocks' entry lists once: every
 // stage's 32 K and V rows go through the LDS tiles once and serve both 16-query tiles, each with its own online
 // softmax; an entry the tile's block does not attend carries logit bias -inf there (probability exactly 0), so
