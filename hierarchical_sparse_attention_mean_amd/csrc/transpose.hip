@@ -6,23 +6,28 @@
 // lists the CSR positions p = u*K + k with idx[u][k] = j, in ascending p.
 //
 // Design (integer work only; all levels of all slices in each launch unless stated):
-//   1-3 together when n_1 + 1 <= 16384 (csc_count_scan: counters in LDS, one workgroup per slice and level),
-//   else:
-//   1. zero the per-column counters;
-//   2. count: one thread per CSR entry, integer atomic add on its column's counter;
-//   3. scan: one 1024-thread workgroup per (slice, level) turns counts into col_ptr with wavefront prefix
-//      sums and seeds the per-column cursors;
-//   4. fill, when every level is transposed (T = L), level by level from the coarsest: the selection is
-//      hierarchical -- a unit's picks at level l < L are children of its parent's picks at level l+1 -- so
-//      the units that can have picked key block j of level l are the children of the level-(l+1) units in
-//      column j/B of level l+1.  One wavefront per (slice, group of B = 16 columns) walks those candidate
-//      units in ascending order (at the coarsest level: all units) and writes each found entry at its
-//      column's start plus its rank, from ballot prefix counts: ascending order directly, no atomics.  A
-//      column with fewer entries found than counted (an input that is not hierarchical) is redone by a scan of
-//      all its level's rows;
-//   5. otherwise (T < L): scatter, one thread per entry claiming a slot in its column with an atomic on the
-//      cursor, then order, one thread per entry writing itself at its rank among the column's entries, which
-//      makes every column ascending and the result independent of the order in which the atomics landed.
+//   Column counts and col_ptr (with the per-column cursors), in one of three ways:
+//   a. n_1 + 1 <= 16384: csc_count_scan -- counters in LDS, one workgroup per slice and level, counted and scanned
+//      in one kernel;
+//   b. else, when K >= 4 and every level is transposed: csc_count_part -- partial histograms in LDS over 4, 8 or
+//      16 (<= K) parts of each level's entries and ranges of 4096 columns, small enough to run beside the forward
+//      -- then csc_sum_parts (the parts of each column summed in part order) and csc_scan; no global atomics;
+//   c. else: zero the counters; csc_count, one thread per CSR entry, an integer atomic add on its column's
+//      counter; csc_scan, one 1024-thread workgroup per (slice, level), wavefront prefix sums.
+//   Then the entries:
+//   - fill, when every level is transposed (T = L), level by level from the coarsest: the selection is
+//     hierarchical -- a unit's picks at level l < L are children of its parent's picks at level l+1 -- so
+//     the units that can have picked key block j of level l are the children of the level-(l+1) units in
+//     column j/B of level l+1.  One wavefront per (slice, group of B = 16 columns) walks those candidate
+//     units in ascending order (at the coarsest level: all units) and writes each found entry at its
+//     column's start plus its rank, from ballot prefix counts: ascending order directly, no atomics.  A
+//     column with fewer entries found than counted (an input that is not hierarchical) is redone by a scan of
+//     all its level's rows;
+//   - otherwise (T < L): scatter, one thread per entry claiming a slot in its column with an atomic on the
+//     cursor, then order, one thread per entry writing itself at its rank among the column's entries, which
+//     makes every column ascending and the result independent of the order in which the atomics landed.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -177,6 +182,67 @@ __global__ __launch_bounds__(kScanThreads) void csc_count_scan(const int32_t* __
   }
 }
 
+// Steps 1-3 without global atomics when a level's entries are too many for one workgroup (csc_count_scan):
+// grid.x = P parts x ranges of kPartCols columns, grid.y = T levels, grid.z = slice; 1024 threads, LDS of
+// kPartCols ints (16 KB: these workgroups fit on a CU beside the forward's, which the transpose runs beside).
+// Part p counts the entries [p ne / P, (p+1) ne / P) of its level whose column lies in its range, with LDS
+// atomics, and writes its range of the histogram to part[p][j] at tmp[slice][pm_off[l] + p n_l + j] (the
+// level's staging area holds n_l K >= n_l P ints); csc_sum_parts then sums the P histograms of each column in
+// part order, and csc_scan scans the counts.  Integer counts: the result does not depend on the order of the atomics.  (Global
+// atomics for the counts slowed the forward running beside them by about 8 %.)
+constexpr int kPartCols = 4096;
+template <int P>
+__global__ __launch_bounds__(kScanThreads) void csc_count_part(const int32_t* __restrict__ idx,
+                                                               int32_t* __restrict__ tmp, Geom g, CscGeom cg) {
+  __shared__ int cnt_s[kPartCols];
+  const int part = blockIdx.x % P, c0 = kPartCols * (blockIdx.x / P), l = blockIdx.y + 1, slice = blockIdx.z;
+  const int nl = g.rows[l], t = threadIdx.x;
+  if (c0 >= nl) return;  // a column range past this level's columns (no barrier is used before this point)
+  const int nc = min(kPartCols, nl - c0);
+  for (int x = t; x < nc; x += kScanThreads) cnt_s[x] = 0;
+  __syncthreads();
+  const int32_t* I = idx + (size_t)slice * g.R * g.K + (size_t)g.off[l] * g.K;
+  const int ne = nl * g.K;
+  const int e0 = (int)((int64_t)part * ne / P), e1 = (int)((int64_t)(part + 1) * ne / P);
+  for (int x0 = e0; x0 < e1; x0 += 8 * kScanThreads) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int x = x0 + i * kScanThreads + t;
+      v[i] = x < e1 ? I[x] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(v[i], nl - 1) - c0;  // below 0 (skipped) for a negative index
+      if (v[i] >= 0 && j >= 0 && j < nc) atomicAdd(&cnt_s[j], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = tmp + (size_t)slice * cg.pm_len + cg.pm_off[l] + (size_t)part * nl + c0;
+  for (int x = t; x < nc; x += kScanThreads) out[x] = cnt_s[x];
+}
+
+// grid.x = column groups of 256, grid.y = T levels, grid.z = slice; 256 threads, one column each.  Column j's
+// count is the sum of the P part histograms (in part order), written as csc_count leaves it
+// (cnt[cp_off + j + 1], entry 0 zero) for csc_scan.  Few registers and no LDS, so that it runs beside the forward.
+template <int P>
+__global__ __launch_bounds__(256) void csc_sum_parts(const int32_t* __restrict__ tmp, int32_t* __restrict__ cnt,
+                                                     Geom g, CscGeom cg) {
+  const int l = blockIdx.y + 1, slice = blockIdx.z, nl = g.rows[l];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= nl) return;
+  const int32_t* parts = tmp + (size_t)slice * cg.pm_len + cg.pm_off[l] + j;
+  int pc[P];
+#pragma unroll
+  for (int q = 0; q < P; ++q) pc[q] = parts[(size_t)q * nl];
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < P; ++q) c += pc[q];
+  int32_t* a = cnt + (size_t)slice * cg.cp_len + cg.cp_off[l];
+  a[j + 1] = c;
+  if (j == 0) a[0] = 0;
+}
+
 constexpr int kMaxTopK = 32;  // K limit of the GPU path
 
 // Level-l fill (see step 4).  grid.x = ceil(n_l / 16) column groups, grid.y = slice; one wavefront each, so
@@ -329,6 +395,30 @@ hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_
     LaunchTimer timer(kTranspose, stream);
     csc_count_scan<<<dim3(cg.T, g.bh), kScanThreads, (g.rows[1] + 1) * sizeof(int32_t), stream>>>(idx, ws_cnt,
                                                                                               col_ptr, g, cg);
+  } else if (cg.T == g.L && g.K >= 4) {
+    // partial histograms in the staging area, which the fills below do not use (P <= K parts fit it)
+    auto run = [&](auto kp) {
+      constexpr int P = decltype(kp)::value;
+      {
+        LaunchTimer timer(kTranspose, stream);
+        const int ranges = (g.rows[1] + kPartCols - 1) / kPartCols;
+        csc_count_part<P><<<dim3(P * ranges, cg.T, g.bh), kScanThreads, 0, stream>>>(idx, ws_tmp, g, cg);
+      }
+      {
+        LaunchTimer timer(kTranspose, stream);
+        csc_sum_parts<P><<<dim3((g.rows[1] + 255) / 256, cg.T, g.bh), 256, 0, stream>>>(ws_tmp, ws_cnt, g, cg);
+      }
+      {
+        LaunchTimer timer(kTranspose, stream);
+        csc_scan<<<dim3(cg.T, g.bh), kScanThreads, 0, stream>>>(ws_cnt, col_ptr, g, cg);
+      }
+    };
+    if (g.K >= 16)
+      run(std::integral_constant<int, 16>{});
+    else if (g.K >= 8)
+      run(std::integral_constant<int, 8>{});
+    else
+      run(std::integral_constant<int, 4>{});
   } else {
     const int64_t ncnt = (int64_t)g.bh * cg.cp_len;
     {

@@ -170,7 +170,24 @@ def test_transpose_bit_exact(L, name, w, levels, Le):
     assert np.array_equal(b.perm.cpu().numpy(), ref["perm"])
 
 
-@pytest.mark.parametrize("n,K,levels,Le", [(4096, 8, 2, 2), (65536, 8, 3, 3), (4096, 5, 2, 1)])
+def test_transpose_partitioned_counts(L):
+    """n_1 = 16384 (N = 262144, K = 16, L = 3): the column counts come from per-part LDS histograms summed per
+    column (one counter too many for the one-workgroup LDS count); the oracle's own selection of two slices, CSC
+    bit for bit."""
+    w = inputs.custom(1, 2, 262144, 64, "bf16", seed=29, topk=16, levels=3)
+    x = inputs.make_inputs(w)
+    ex = {nm: flat(t.exact) for nm, t in x.items()}
+    pq, pk = oracle.pool(ex["q"], 16, 3), oracle.pool(ex["k"], 16, 3)
+    idx, _ = oracle.select(pq, pk, w.n, 16, 3, 16)
+    cp_ref, pm_ref = oracle.index_transpose(idx, w.n, 16, 3, 16, 3)
+    b = L.Buffers(L.problem(1, 2, w.n, topk=16, levels=3))
+    L.index_transpose(b.prob, torch.from_numpy(idx.astype(np.int32)).cuda(), b.col_ptr, b.perm, b.ws_t)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.col_ptr.cpu().numpy(), cp_ref)
+    assert np.array_equal(b.perm.cpu().numpy(), pm_ref)
+
+
+@pytest.mark.parametrize("n,K,levels,Le", [(4096, 8, 2, 2), (65536, 8, 3, 3), (4096, 5, 2, 1), (262144, 16, 3, 3)])
 def test_transpose_non_hierarchical(L, n, K, levels, Le):
     """Rows that are not children of their parent's picks (random ascending rows at every level): the
     hierarchical fill misses entries, raises its flag and the general path must give the oracle's CSC."""
