@@ -245,16 +245,19 @@ __global__ __launch_bounds__(256) void csc_sum_parts(const int32_t* __restrict__
 
 constexpr int kMaxTopK = 32;  // K limit of the GPU path
 
-// Level-l fill (see step 4).  grid.x = ceil(n_l / 16) column groups, grid.y = slice; one wavefront each, so
-// that all of them are resident at once.  Candidates go in rounds of 512 (32 parents): the parents' positions
-// are read by 32 lanes, then every lane issues the row loads of its 8 candidates of the round at once (a long
-// column would otherwise pay one memory round trip per 64 candidates); the 8 sub-chunks of 64 candidates are
-// then ranked in candidate order with one ballot per column, the running per-column counts wave-uniform.
-// KM: the smallest of 8, 16, 32 that holds K (registers per candidate row).
-constexpr int kFillPer = 8, kFillRound = 64 * kFillPer;
-template <int KM>
+// Level-l fill (see the design notes).  grid.x = ceil(n_l / 16) column groups, grid.y = slice; one wavefront
+// each, so that all of them are resident at once.  Candidates go in rounds of 64 kFillPer (4 kFillPer parents):
+// the parents' positions are read by the first lanes, then every lane issues the row loads of its kFillPer
+// candidates of the round at once (a long column would otherwise pay one memory round trip per 64 candidates);
+// the kFillPer sub-chunks of 64 candidates are then ranked in candidate order with one ballot per column, the
+// running per-column counts wave-uniform.
+// KM: the smallest of 8, 16, 32 that holds K (registers per candidate row).  kFillPer: candidates per lane and
+// round; 2 for KM = 16 (62 VGPRs), so that two of these waves fit on a SIMD beside the forward's two, which the
+// transpose runs beside (with 8: 168 VGPRs, one wave, and the N = 262144 transpose outlasted the forward).
+template <int KM, int kFillPer>
 __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ idx, const int32_t* __restrict__ col_ptr,
                                                int32_t* __restrict__ perm, Geom g, CscGeom cg, int l) {
+  constexpr int kFillRound = 64 * kFillPer;
   const int J = blockIdx.x, slice = blockIdx.y, lane = threadIdx.x;
   const int nl = g.rows[l], K = g.K;
   const int32_t* I = idx + (size_t)slice * g.R * K + (size_t)g.off[l] * K;  // level-l rows
@@ -437,7 +440,7 @@ hipError_t launch_index_transpose(const Geom& g, const CscGeom& cg, const int32_
   if (cg.T == g.L) {
     for (int l = g.L; l >= 1; --l) {
       LaunchTimer timer(kTranspose, stream);
-      auto kernel = g.K <= 8 ? csc_fill<8> : g.K <= 16 ? csc_fill<16> : csc_fill<kMaxTopK>;
+      auto kernel = g.K <= 8 ? csc_fill<8, 8> : g.K <= 16 ? csc_fill<16, 2> : csc_fill<kMaxTopK, 8>;
       kernel<<<dim3((g.rows[l] + 15) / 16, g.bh), 64, 0, stream>>>(idx, col_ptr, perm, g, cg, l);
     }
   } else {
