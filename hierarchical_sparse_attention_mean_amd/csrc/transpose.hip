@@ -182,14 +182,14 @@ __global__ __launch_bounds__(kScanThreads) void csc_count_scan(const int32_t* __
   }
 }
 
-// Steps 1-3 without global atomics when a level's entries are too many for one workgroup (csc_count_scan):
+// Counts without global atomics when a level's entries are too many for one workgroup (csc_count_scan):
 // grid.x = P parts x ranges of kPartCols columns, grid.y = T levels, grid.z = slice; 1024 threads, LDS of
 // kPartCols ints (16 KB: these workgroups fit on a CU beside the forward's, which the transpose runs beside).
 // Part p counts the entries [p ne / P, (p+1) ne / P) of its level whose column lies in its range, with LDS
 // atomics, and writes its range of the histogram to part[p][j] at tmp[slice][pm_off[l] + p n_l + j] (the
 // level's staging area holds n_l K >= n_l P ints); csc_sum_parts then sums the P histograms of each column in
-// part order, and csc_scan scans the counts.  Integer counts: the result does not depend on the order of the atomics.  (Global
-// atomics for the counts slowed the forward running beside them by about 8 %.)
+// part order, and csc_scan scans the counts.  Integer counts: the result does not depend on the order of the
+// atomics.  (Global atomics for the counts slowed the forward running beside them by about 8 %.)
 constexpr int kPartCols = 4096;
 template <int P>
 __global__ __launch_bounds__(kScanThreads) void csc_count_part(const int32_t* __restrict__ idx,
