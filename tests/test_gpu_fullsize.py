@@ -48,6 +48,12 @@ def _run_sampled(L, w, samples):
     for s in samples:
         ex = {nm: x[nm].exact.reshape(w.bh, w.n, w.d)[s:s + 1] for nm in ("q", "k", "v", "dout")}
         ref = oracle.run(ex["q"], ex["k"], ex["v"], w.block, w.topk, levels=w.levels, dout=ex["dout"])
+        # the pyramid at this size's launch shape (levels 1 and 2 in one launch, then level 3, at N = 262144):
+        # fp32 means of bf16 inputs, so within fp32 rounding of the oracle's
+        for nm, got in (("pq", b.pq), ("pk", b.pk), ("pv", b.pv)):
+            g = host(got).reshape(w.bh, -1)[s]
+            err = np.abs(g - ref[nm].reshape(-1)).max()
+            assert err <= 1e-5 * max(1.0, np.abs(ref[nm]).max()), (nm, s, err)
         compared, total = selection_parity(idx[s:s + 1].cpu().numpy(), ref["idx"], ref["pq"], ref["pk"], w.n,
                                            w.block, w.levels, w.topk)
         print(f"{w.name} slice {s}: selection rows compared {compared}/{total}")

@@ -96,6 +96,26 @@ def test_pyramid(L, name, w, levels, Le):
             assert err.max() <= 0, (nm, err.max())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pyramid_many_slices(L, dtype):
+    """384 slices of N = 4096 (L = 2): 384 x 16 chunks x 3 tensors = 18432 pooling workgroups, several rounds of
+    them on the device; every slice's whole pyramid against the oracle's."""
+    w = inputs.custom(2, 192, 4096, 64, dtype, seed=31, topk=8, levels=2)
+    x = inputs.make_inputs(w)
+    b = L.Buffers(_prob(L, w, 2, -1), backward=False)
+    b.pyramid(dev(x["q"]), dev(x["k"]), dev(x["v"]))
+    torch.cuda.synchronize()
+    for nm, got in (("pq", b.pq), ("pk", b.pk), ("pv", b.pv)):
+        ref = oracle.pool(flat(x["q" if nm == "pq" else "k" if nm == "pk" else "v"].exact), w.block, 2)
+        err = np.abs(host(got) - ref).max()
+        assert err <= 1e-5 * max(1.0, np.abs(ref).max()), (nm, err)
+    if dtype == "bf16":
+        for nm, got, src in (("pk", b.pkb, "k"), ("pv", b.pvb, "v")):
+            r = oracle.pool(flat(x[src].exact), w.block, 2).reshape(got.shape)
+            err = np.abs(got.float().cpu().numpy() - r) - (2.0 ** -8 * np.abs(r) + 1e-6 * max(1.0, np.abs(r).max()))
+            assert err.max() <= 0, (nm, err.max())
+
+
 @pytest.mark.parametrize("name,w,levels,Le", CASES, ids=[c[0] for c in CASES])
 def test_select(L, name, w, levels, Le):
     x, ex, ref = _prepare(name, w, levels, Le)
